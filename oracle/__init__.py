@@ -1,0 +1,147 @@
+"""Python access to the C oracle (``oracle/liboracle.so``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark use it; the product package never imports it.  Arguments are
+numpy arrays on the host; the wrappers only marshal pointers.  ctypes releases
+the GIL during each call, so independent calls may run on several threads.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+# ORACLE_LIB lets the mutation test load a deliberately broken copy.
+LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
+K = 16
+PAD = (1 << 21) - 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I32 = ctypes.c_int32
+        L.oracle_splitmix64.restype = ctypes.c_uint64
+        L.oracle_splitmix64.argtypes = [ctypes.c_uint64]
+        L.oracle_default_seeds.argtypes = [P]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_bf16_rne.argtypes = [ctypes.c_float]
+        L.oracle_bf16_rne_array.argtypes = [P, I64, P]
+        L.oracle_context.argtypes = [P, I64, P, I32, P, P]
+        L.oracle_hash.argtypes = [P, I64, P, I32, P, P, I64, P]
+        L.oracle_embed_bag_bf16.argtypes = [P, I64, I32, P, I64, P]
+        L.oracle_embed_bag_int8.argtypes = [P, P, I64, I32, P, I64, P]
+        L.oracle_gate_add.argtypes = [P, P, I64, I32, P, P, P, P]
+        L.oracle_forward.argtypes = [P, I64, P, I32, P, P, I32, P, P, I64, I32,
+                                     P, P, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def splitmix64(x: int) -> int:
+    return int(lib().oracle_splitmix64(x & 0xFFFFFFFFFFFFFFFF))
+
+
+def default_seeds() -> np.ndarray:
+    s = np.zeros(K, dtype=np.uint64)
+    lib().oracle_default_seeds(_p(s))
+    return s
+
+
+def bf16_rne(x) -> np.ndarray:
+    x = _c(x, np.float32).reshape(-1)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_bf16_rne_array(_p(x), x.size, _p(out))
+    return out
+
+
+def context(tokens, seq_offsets, history=None) -> np.ndarray:
+    t = _c(tokens, np.int32)
+    so = _c(seq_offsets, np.int32)
+    h = _c(history, np.int32)
+    ctx = np.zeros((t.size, 3), dtype=np.int32)
+    lib().oracle_context(_p(t), t.size, _p(so), so.size - 1, _p(h), _p(ctx))
+    return ctx
+
+
+def hash_rows(tokens, seq_offsets, R, history=None, seeds=None) -> np.ndarray:
+    t = _c(tokens, np.int32)
+    so = _c(seq_offsets, np.int32)
+    h = _c(history, np.int32)
+    sd = default_seeds() if seeds is None else _c(seeds, np.uint64)
+    rows = np.zeros((t.size, K), dtype=np.int32)
+    lib().oracle_hash(_p(t), t.size, _p(so), so.size - 1, _p(h), _p(sd), int(R), _p(rows))
+    return rows
+
+
+def embed_bag_bf16(T, rows) -> np.ndarray:
+    T = _c(T, np.uint16)
+    rows = _c(rows, np.int32)
+    n = rows.shape[0]
+    d = T.shape[1]
+    eN = np.zeros((n, d), dtype=np.float32)
+    lib().oracle_embed_bag_bf16(_p(T), T.shape[0], d, _p(rows), n, _p(eN))
+    return eN
+
+
+def embed_bag_int8(Q, scale, rows) -> np.ndarray:
+    Q = _c(Q, np.int8)
+    scale = _c(scale, np.float32)
+    rows = _c(rows, np.int32)
+    n = rows.shape[0]
+    d = Q.shape[1]
+    eN = np.zeros((n, d), dtype=np.float32)
+    lib().oracle_embed_bag_int8(_p(Q), _p(scale), Q.shape[0], d, _p(rows), n, _p(eN))
+    return eN
+
+
+def gate_add(eN, e1_rows, W_g, e1=None, residual=None) -> np.ndarray:
+    eN = _c(eN, np.float32)
+    n, d = eN.shape
+    idx = _c(e1_rows, np.int32)
+    e1 = _c(e1, np.uint16)
+    W_g = _c(W_g, np.float32)
+    res = _c(residual, np.uint16)
+    out = np.zeros((n, d), dtype=np.uint16)
+    lib().oracle_gate_add(_p(eN), _p(idx), n, d, _p(e1), _p(W_g), _p(res), _p(out))
+    return out
+
+
+def forward(tokens, seq_offsets, table, W_g, e1=None, residual=None, history=None,
+            seeds=None, scale=None):
+    """Whole path.  ``table`` is uint16 bf16 bits [R][d], or int8 [R][d] with
+    ``scale`` fp32 [R].  Returns (out bf16 bits [n][d], rows [n][16], eN fp32)."""
+    t = _c(tokens, np.int32)
+    so = _c(seq_offsets, np.int32)
+    h = _c(history, np.int32)
+    sd = default_seeds() if seeds is None else _c(seeds, np.uint64)
+    is_int8 = np.asarray(table).dtype == np.int8
+    tab = _c(table, np.int8 if is_int8 else np.uint16)
+    sc = _c(scale, np.float32)
+    R, d = tab.shape
+    n = t.size
+    out = np.zeros((n, d), dtype=np.uint16)
+    rows = np.zeros((n, K), dtype=np.int32)
+    eN = np.zeros((n, d), dtype=np.float32)
+    lib().oracle_forward(_p(t), n, _p(so), so.size - 1, _p(h), _p(sd), 1 if is_int8 else 0,
+                         _p(tab), _p(sc), R, d, _p(_c(e1, np.uint16)), _p(_c(W_g, np.float32)),
+                         _p(_c(residual, np.uint16)), _p(out), _p(rows), _p(eN))
+    return out, rows, eN

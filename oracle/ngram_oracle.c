@@ -1,0 +1,209 @@
+/*
+ * CPU oracle for the hashed n-gram embedding gather-sum.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may load, link or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or helper with the HIP
+ * library; it is written from the definitions below and nothing else.
+ *
+ * What is computed, and where it is stated:
+ *   - "Qwen Brought Back N-Grams. All 51 Billion Parameters of Them.",
+ *     section "N-grams, of all things": per token, the bigram and trigram
+ *     context is hashed into one 20M-row table, 16 rows are gathered and
+ *     summed into one 2560-wide vector, which is added to the residual stream.
+ *   - "Qwen3.8-Flash-Next: A 51B N-gram Embedding Table with Heterogeneous
+ *     Memory Prefetch", Key point 1, the fusion equation
+ *     h0 = e_1gram(w_t) + W_g (elementwise) e_Ngram, and "a deterministic hash".
+ *   - Key point 3 of the same page: the INT8 table size.
+ *
+ * The pages leave the hash, the packing, the seeds, the padding, the order of
+ * the sum and the rounding open.  The readings taken (each one a plain
+ * choice, not a claim about the pages):
+ *   - hash: splitmix64 (Steele, Lea and Flood, "Fast Splittable Pseudorandom
+ *     Number Generators", OOPSLA 2014; finaliser constants of Vigna's public
+ *     domain splitmix64): splitmix64(x) is the generator's first output from
+ *     state x, i.e. mix(x + gamma);
+ *   - keys: 21-bit fields; bigram K2 = c1<<21 | c0, trigram
+ *     K3 = c2<<42 | c1<<21 | c0, with c0 = w_t, c1 = w_{t-1}, c2 = w_{t-2};
+ *   - rows: row_k = splitmix64(key_k XOR seed_k) mod R, key_k = K2 for
+ *     k = 0..7 and K3 for k = 8..15; default seed_k = splitmix64(k * gamma);
+ *   - context before a sequence's first token: the caller's 2-token history
+ *     when given, else the pad id 2^21 - 1;
+ *   - sum: fp32, starting from +0, k = 0..15 in order; int8 rows are
+ *     dequantised inside the sum as acc = fmaf(q, scale_row, acc);
+ *   - gate: h = fmaf(W_g[j], acc, e1[w_t][j]) (or + 0 without e1);
+ *     y = residual + h (or h without residual); out = bf16 round-to-nearest-
+ *     even of y, NaN to the canonical quiet NaN 0x7FC0.
+ * Build with -ffp-contract=off: every fp32 operation above is one IEEE
+ * operation, and fmaf is the C library's correctly rounded fused multiply-add.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_K 16
+#define ORACLE_PAD 0x1FFFFF
+#define ORACLE_GAMMA 0x9E3779B97F4A7C15ull
+
+/* splitmix64: one output of the generator from state x (mod 2^64). */
+uint64_t oracle_splitmix64(uint64_t x)
+{
+    uint64_t z = x + ORACLE_GAMMA;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* Outputs 0..15 of the splitmix64 generator started from state 0. */
+void oracle_default_seeds(uint64_t seeds[ORACLE_K])
+{
+    for (int k = 0; k < ORACLE_K; ++k)
+        seeds[k] = oracle_splitmix64((uint64_t)k * ORACLE_GAMMA);
+}
+
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round an fp32 value to the nearest bf16, ties to even. */
+uint16_t oracle_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (isnan(f))
+        return 0x7FC0;
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+void oracle_bf16_rne_array(const float* x, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_rne(x[i]);
+}
+
+/*
+ * The n-gram context of every token: ctx[i] = (c0, c1, c2) = (w_t, w_{t-1},
+ * w_{t-2}).  Sequence s holds tokens seq_offsets[s] .. seq_offsets[s+1]-1.
+ * Its extended stream is [h0, h1, tokens of s...] with (h0, h1) = history[s]
+ * or (PAD, PAD); position p of s reads c1 = ext[p+1], c2 = ext[p].
+ */
+void oracle_context(const int32_t* tokens, int64_t n, const int32_t* seq_offsets,
+                    int32_t S, const int32_t* history, int32_t* ctx)
+{
+    (void)n;
+    for (int32_t s = 0; s < S; ++s) {
+        int64_t start = seq_offsets[s], end = seq_offsets[s + 1];
+        int64_t len = end - start;
+        int32_t* ext = (int32_t*)malloc(sizeof(int32_t) * (size_t)(len + 2));
+        ext[0] = history ? history[2 * s] : ORACLE_PAD;
+        ext[1] = history ? history[2 * s + 1] : ORACLE_PAD;
+        for (int64_t p = 0; p < len; ++p)
+            ext[p + 2] = tokens[start + p];
+        for (int64_t p = 0; p < len; ++p) {
+            int64_t i = start + p;
+            ctx[3 * i + 0] = ext[p + 2];
+            ctx[3 * i + 1] = ext[p + 1];
+            ctx[3 * i + 2] = ext[p];
+        }
+        free(ext);
+    }
+}
+
+/* rows[i][k] = splitmix64(key_k XOR seeds[k]) mod R. */
+void oracle_hash(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                 const int32_t* history, const uint64_t* seeds, int64_t R, int32_t* rows)
+{
+    int32_t* ctx = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)(n > 0 ? n : 1));
+    oracle_context(tokens, n, seq_offsets, S, history, ctx);
+    for (int64_t i = 0; i < n; ++i) {
+        uint64_t c0 = (uint64_t)(uint32_t)ctx[3 * i + 0];
+        uint64_t c1 = (uint64_t)(uint32_t)ctx[3 * i + 1];
+        uint64_t c2 = (uint64_t)(uint32_t)ctx[3 * i + 2];
+        uint64_t bigram = (c1 << 21) | c0;
+        uint64_t trigram = (c2 << 42) | (c1 << 21) | c0;
+        for (int k = 0; k < ORACLE_K; ++k) {
+            uint64_t key = k < 8 ? bigram : trigram;
+            uint64_t h = oracle_splitmix64(key ^ seeds[k]);
+            rows[i * ORACLE_K + k] = (int32_t)(h % (uint64_t)R);
+        }
+    }
+    free(ctx);
+}
+
+/* eN[i][j] = sum over k = 0..15, in order, of T[rows[i][k]][j] (fp32). */
+void oracle_embed_bag_bf16(const uint16_t* T, int64_t R, int32_t d, const int32_t* rows,
+                           int64_t n, float* eN)
+{
+    (void)R;
+    for (int64_t i = 0; i < n; ++i)
+        for (int32_t j = 0; j < d; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < ORACLE_K; ++k) {
+                int64_t r = rows[i * ORACLE_K + k];
+                acc = acc + oracle_bf16_to_f32(T[r * d + j]);
+            }
+            eN[i * d + j] = acc;
+        }
+}
+
+/* INT8 rows with one fp32 scale per row, dequantised inside the sum. */
+void oracle_embed_bag_int8(const int8_t* Q, const float* scale, int64_t R, int32_t d,
+                           const int32_t* rows, int64_t n, float* eN)
+{
+    (void)R;
+    for (int64_t i = 0; i < n; ++i)
+        for (int32_t j = 0; j < d; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < ORACLE_K; ++k) {
+                int64_t r = rows[i * ORACLE_K + k];
+                acc = fmaf((float)Q[r * d + j], scale[r], acc);
+            }
+            eN[i * d + j] = acc;
+        }
+}
+
+/*
+ * out[i][j] = bf16(residual[i][j] + fmaf(W_g[j], eN[i][j], e1[e1_rows[i]][j])).
+ * e1_rows[i] is the token w_t (the 1-gram id).  e1 and residual may be NULL.
+ */
+void oracle_gate_add(const float* eN, const int32_t* e1_rows, int64_t n, int32_t d,
+                     const uint16_t* e1, const float* W_g, const uint16_t* residual,
+                     uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        for (int32_t j = 0; j < d; ++j) {
+            float base = e1 ? oracle_bf16_to_f32(e1[(int64_t)e1_rows[i] * d + j]) : 0.0f;
+            float h = fmaf(W_g[j], eN[i * d + j], base);
+            float y = residual ? oracle_bf16_to_f32(residual[i * d + j]) + h : h;
+            out[i * d + j] = oracle_bf16_rne(y);
+        }
+}
+
+/* The whole path for a bf16 (dtype 0) or int8 (dtype 1) table, one step
+ * after another: context and hash, then the sum, then gate and residual. */
+void oracle_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                    const int32_t* history, const uint64_t* seeds, int32_t dtype,
+                    const void* table, const float* scale, int64_t R, int32_t d,
+                    const uint16_t* e1, const float* W_g, const uint16_t* residual,
+                    uint16_t* out, int32_t* rows_out, float* eN_out)
+{
+    size_t nn = (size_t)(n > 0 ? n : 1);
+    int32_t* rows = rows_out ? rows_out : (int32_t*)malloc(sizeof(int32_t) * ORACLE_K * nn);
+    float* eN = eN_out ? eN_out : (float*)malloc(sizeof(float) * (size_t)d * nn);
+    oracle_hash(tokens, n, seq_offsets, S, history, seeds, R, rows);
+    if (dtype == 0)
+        oracle_embed_bag_bf16((const uint16_t*)table, R, d, rows, n, eN);
+    else
+        oracle_embed_bag_int8((const int8_t*)table, scale, R, d, rows, n, eN);
+    oracle_gate_add(eN, tokens, n, d, e1, W_g, residual, out);
+    if (!rows_out)
+        free(rows);
+    if (!eN_out)
+        free(eN);
+}

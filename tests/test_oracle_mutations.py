@@ -1,0 +1,64 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of the oracle's C source, builds it
+with gcc into a temporary library, and runs the oracle pin tests against it
+in a subprocess; the pins must fail.  The committed oracle is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ngram_oracle.c")
+
+MUTATIONS = {
+    "no_gamma": ("uint64_t z = x + ORACLE_GAMMA;", "uint64_t z = x;"),
+    "wrong_shift": ("(z ^ (z >> 27))", "(z ^ (z >> 28))"),
+    "wrong_multiplier": ("0x94D049BB133111EBull", "0x94D049BB133111EDull"),
+    "bigram_trigram_swapped": ("k < 8 ? bigram : trigram", "k < 8 ? trigram : bigram"),
+    "field_width_20": ("uint64_t bigram = (c1 << 21) | c0;", "uint64_t bigram = (c1 << 20) | c0;"),
+    "trigram_drops_c2": ("uint64_t trigram = (c2 << 42) | (c1 << 21) | c0;",
+                         "uint64_t trigram = (c1 << 21) | c0;"),
+    "context_off_by_one": ("ctx[3 * i + 2] = ext[p];", "ctx[3 * i + 2] = ext[p + 1];"),
+    "history_swapped": ("ext[0] = history ? history[2 * s] : ORACLE_PAD;",
+                        "ext[0] = history ? history[2 * s + 1] : ORACLE_PAD;"),
+    "seed_index": ("uint64_t h = oracle_splitmix64(key ^ seeds[k]);",
+                   "uint64_t h = oracle_splitmix64(key ^ seeds[k & 7]);"),
+    "mod_low_word": ("(int32_t)(h % (uint64_t)R)", "(int32_t)((uint32_t)h % (uint64_t)R)"),
+    "sum_reversed": ("acc = acc + oracle_bf16_to_f32(T[r * d + j]);",
+                     "acc = oracle_bf16_to_f32(T[(int64_t)rows[i * ORACLE_K + 15 - k] * d + j]) + acc;"),
+    "sum_skips_last_row": ("acc = acc + oracle_bf16_to_f32(T[r * d + j]);",
+                           "if (k < 15) acc = acc + oracle_bf16_to_f32(T[r * d + j]);"),
+    "int8_unfused": ("acc = fmaf((float)Q[r * d + j], scale[r], acc);",
+                     "acc = (float)Q[r * d + j] * scale[r] + acc;"),
+    "int8_wrong_scale_row": ("acc = fmaf((float)Q[r * d + j], scale[r], acc);",
+                             "acc = fmaf((float)Q[r * d + j], scale[k], acc);"),
+    "gate_unfused": ("float h = fmaf(W_g[j], eN[i * d + j], base);",
+                     "float h = W_g[j] * eN[i * d + j] + base;"),
+    "gate_drops_residual": ("float y = residual ? oracle_bf16_to_f32(residual[i * d + j]) + h : h;",
+                            "float y = h;"),
+    "gate_wrong_e1_row": ("e1[(int64_t)e1_rows[i] * d + j]", "e1[(int64_t)i * d + j]"),
+    "round_half_up": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
+                      "return (uint16_t)((u + 0x8000u) >> 16);"),
+    "round_truncate": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
+                       "return (uint16_t)(u >> 16);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, tmp_path):
+    before, after = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(before) == 1, f"mutation site for {name} not found exactly once"
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(src.replace(before, after))
+    mlib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-o", str(mlib), str(msrc), "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(mlib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
