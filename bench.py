@@ -1,0 +1,304 @@
+"""Benchmark of the hashed n-gram embedding gather-sum on one MI355X.
+
+A step is one pass of the whole path over one batch: ngram_forward (context,
+hash, gather of 16 rows per token, fp32 sum, gate with e1 and W_g, residual
+add, bf16 rounding) on the workload's batch, inputs resident in HBM.  The
+default workload is prefill: 8 sequences x 4096 tokens (Zipf(1.1) over a
+151936-token vocabulary), a 20,000,000 x 2560 bf16 table (95.4 GiB), e1
+151936 x 2560 bf16, W_g[2560] fp32, residual [32768][2560] bf16 updated in
+place.  Consecutive steps rotate over 4 distinct batches (tokens + residual,
+672 MB of residual) so that no step finds the previous step's residual in
+the 256 MB Infinity Cache.
+
+Prints one JSON line: tokens/s over the timed steps, the roofline of the
+fused kernel (algorithmic HBM bytes per launch / mean launch time from HIP
+events on the launch stream, against 8 TB/s), and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "n-gram gather-sum tokens/s; achieved GB/s as % of HBM (or PCIe) peak"
+HBM_PEAK_GBPS = 8000.0
+PCIE_PEAK_GBPS = 64.0          # PCIe Gen5 x16, one direction
+K_ROWS = 16
+
+
+def nominal_bytes_per_token(d: int, table: str = "bf16", e1: bool = True, residual: bool = True) -> int:
+    """Algorithmic HBM bytes one token moves through the fused kernel: its 16
+    table rows (bf16: 2 B per element; int8: 1 B per element plus a 4-byte row
+    scale), its e1 row, its residual row read and its output row written (2 B
+    per element each), and its token id (4 B).  W_g (d x 4 B) is read once per
+    launch and counted per launch, not per token."""
+    row = d * 2 if table == "bf16" else d + 4
+    b = K_ROWS * row + 4
+    if e1:
+        b += 2 * d
+    if residual:
+        b += 2 * d
+    b += 2 * d                 # output row
+    return b
+
+
+def dma_time_estimate_us(K: int, d: int, elem_bytes: int, bandwidth_gbps: float) -> float:
+    """Closed-form PCIe time of one token's rows: K * d * S / bandwidth
+    ("Qwen3.8-Flash-Next: A 51B N-gram Embedding Table with Heterogeneous
+    Memory Prefetch", Key point 3, the T_DMA equation)."""
+    return K * d * elem_bytes / (bandwidth_gbps * 1e9) * 1e6
+
+
+def table_bytes(R: int, d: int, table: str = "bf16") -> int:
+    return R * d * (2 if table == "bf16" else 1) + (0 if table == "bf16" else 4 * R)
+
+
+def source_sha256() -> str:
+    p = os.path.join(ROOT, "hashed_gram_embedding_ngram_amd", "csrc", "ngram.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_sha256():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "int8", "decode1", "decode2", "decode4"])
+    ap.add_argument("--dist", default="zipf", choices=["zipf", "uniform"],
+                    help="token distribution (uniform: the no-reuse control)")
+    ap.add_argument("--batches", type=int, default=4, help="distinct batches rotated over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1_000_000,
+                    help="table rows of the host copy the CPU oracle reads")
+    return ap.parse_args()
+
+
+def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, max_seconds=20.0):
+    """The oracle timed on the host cores on a bounded sample of the
+    workload: the whole batch, sequence by sequence, hashed into a host copy
+    of the first ``R_cpu`` table rows (the full table does not fit in host
+    memory; a random-row gather far beyond the last-level cache is
+    DRAM-bound either way), one oracle_forward call per sequence on a pool of
+    threads; repeated until about ``max_seconds`` / 4 of wall time."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+
+    toks, offs, hist = host_inputs.tokens, host_inputs.offsets, host_inputs.history
+    nseq = len(offs) - 1
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16, nseq))
+
+    def one(s):
+        a, b = int(offs[s]), int(offs[s + 1])
+        oracle.forward(toks[a:b], np.array([0, b - a], np.int32), table_np, host_inputs.W_g,
+                       e1=e1_np, residual=None if res_np is None else res_np[a:b],
+                       history=None if hist is None else hist[s:s + 1], scale=scale_np)
+        return b - a
+
+    passes = tokens_done = 0
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while True:
+            tokens_done += sum(ex.map(one, range(nseq)))
+            passes += 1
+            if time.time() - t0 >= max_seconds / 4 or passes >= 8:
+                break
+    wall = time.time() - t0
+    return {
+        "value": tokens_done / wall,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{passes} pass(es) over the {len(toks)}-token batch ({nseq} sequences, one "
+                   f"oracle_forward call per sequence on {threads} threads); rows hashed mod "
+                   f"{R_cpu} into a {table_np.nbytes / 2**30:.2f} GiB host copy of the first "
+                   f"{R_cpu} table rows (the full table does not fit in host memory); "
+                   f"host copy prep {prep_s:.1f} s, not timed"),
+        "cpu_model": _cpu_model(),
+        "wall_s": wall,
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path is built and measured on a single MI355X; it has no multi-GPU mode)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import hashed_gram_embedding_ngram_amd as ng
+    import synth
+    from synth.workloads import CONFIGS, HostInputs
+
+    dev = torch.device("cuda:0")
+    spec = CONFIGS[args.workload].replace(dist=args.dist)
+    n, d = spec.n, spec.d
+    t_setup = time.time()
+
+    # Shared tensors: table, e1, W_g (batch 0's seed).
+    h0 = HostInputs(spec)
+    s0 = spec.seed
+    if spec.table == "int8":
+        table = synth.fill_gpu(spec.table_kind, s0, synth.TAG_TABLE,
+                               torch.empty(spec.R * d, dtype=torch.int8, device=dev))
+        scale = synth.fill_gpu(synth.KIND_F32_SCALE, s0, synth.TAG_SCALE,
+                               torch.empty(spec.R, dtype=torch.float32, device=dev))
+        T = ng.Table(table, spec.R, d, ng.TABLE_INT8_ROWSCALE, row_scale=scale)
+    else:
+        table = synth.fill_gpu(spec.table_kind, s0, synth.TAG_TABLE,
+                               torch.empty(spec.R * d, dtype=torch.int16, device=dev))
+        scale = None
+        T = ng.Table(table, spec.R, d)
+    e1 = synth.fill_gpu(synth.KIND_BF16_NORMAL12, s0, synth.TAG_E1,
+                        torch.empty(spec.V * d, dtype=torch.int16, device=dev)) if spec.e1 else None
+    W_g = torch.from_numpy(h0.W_g).to(dev)
+
+    # Rotating batches: tokens, offsets, history, residual (in place), out.
+    nb = max(1, args.batches)
+    batches = []
+    for b in range(nb):
+        hb = h0 if b == 0 else HostInputs(spec.replace(batch=b))
+        tok = torch.from_numpy(hb.tokens).to(dev)
+        off = torch.from_numpy(hb.offsets).to(dev)
+        hist = None if hb.history is None else torch.from_numpy(np.ascontiguousarray(hb.history)).to(dev)
+        if spec.residual:
+            res = synth.fill_gpu(synth.KIND_BF16_NORMAL6, spec.replace(batch=b).seed, synth.TAG_RESIDUAL,
+                                 torch.empty(n * d, dtype=torch.int16, device=dev))
+            out = res
+        else:
+            res = None
+            out = torch.empty(n * d, dtype=torch.int16, device=dev)
+        batches.append((tok, off, hist, res, out))
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        tok, off, hist, res, out = batches[i % nb]
+        ng.ngram_forward(tok, off, T, W_g, out, e1=e1, residual=res, history=hist, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    bpt = nominal_bytes_per_token(d, spec.table, spec.e1, spec.residual)
+    bytes_per_launch = bpt * n + 4 * d
+    achieved = bytes_per_launch / mean_launch_s / 1e9
+    traffic = measured_traffic(args.workload if args.dist == "zipf" else f"{args.workload}_{args.dist}")
+
+    result = {
+        "metric": METRIC,
+        "value": n * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "tokens": n,
+            "sequences": len(spec.lengths),
+            "seq_len": spec.lengths[0],
+            "R": spec.R,
+            "d": d,
+            "K": K_ROWS,
+            "table_dtype": spec.table,
+            "vocab": spec.V,
+            "token_dist": f"zipf({spec.zipf_s})" if args.dist == "zipf" else "uniform",
+            "residual_in_place": spec.residual,
+            "rotating_batches": nb,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "kernel": "ngram_fwd_kernel",
+            "algorithmic_bytes_per_token": bpt,
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+            "mean_launch_us": mean_launch_s * 1e6,
+        },
+        "setup_s": setup_s,
+    }
+
+    if not args.no_cpu_baseline:
+        R_cpu = min(args.cpu_rows, spec.R)
+        tp = time.time()
+        if spec.table == "int8":
+            table_np = table[: R_cpu * d].cpu().numpy().reshape(R_cpu, d)
+            scale_np = scale[:R_cpu].cpu().numpy()
+        else:
+            table_np = table[: R_cpu * d].cpu().numpy().view(np.uint16).reshape(R_cpu, d)
+            scale_np = None
+        e1_np = None if e1 is None else e1.cpu().numpy().view(np.uint16).reshape(spec.V, d)
+        res_np = None if batches[0][3] is None else batches[0][3].cpu().numpy().view(np.uint16).reshape(n, d)
+        result["cpu_baseline"] = cpu_baseline(HostInputs(spec.replace(R=R_cpu)), table_np, scale_np,
+                                              e1_np, res_np, R_cpu, time.time() - tp)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,732 @@
+// libngram.so: the hashed n-gram embedding gather-sum for MI355X (gfx950).
+//
+// Method: "Qwen Brought Back N-Grams. All 51 Billion Parameters of Them.",
+// section "N-grams, of all things" (hash the bigram and trigram context of a
+// token into one 20M x 2560 table, gather 16 rows, sum them, add the sum to
+// the residual stream), and "Qwen3.8-Flash-Next: A 51B N-gram Embedding Table
+// with Heterogeneous Memory Prefetch", Key point 1 (gate with the 1-gram
+// embedding: h = e_1gram(w_t) + W_g (.) e_N).  The hash, seeds, padding,
+// summation order and rounding are fixed in include/ngram.h.
+//
+// Layout of the work on CDNA4.  The path is a gather-reduce that moves about
+// 97 KB of HBM per token for 0.5 flop per byte, so it is bound by HBM
+// bandwidth; there is no contraction and no MFMA.  One workgroup owns a tile
+// of tokens.  Its threads first hash the tile's (token, k) pairs, one pair per
+// thread, into a row list in LDS.  Then each wavefront owns 512-column slices
+// of the rows: every lane loads 16 bytes (8 bf16, or 8 int8) of each of the
+// 16 rows, so one load instruction reads 1 KiB contiguous of one row and the
+// 16 loads of a slice are all in flight before the first add.  The row ids
+// are wave-uniform (read from LDS, moved to scalar registers), so each row
+// address is a scalar base plus a per-lane offset.  The sum runs in fp32 in
+// k order, the gate is one fused multiply-add, the residual one add, and the
+// result is rounded to bf16 in registers and stored with one 16-byte store per
+// lane: the residual is read once and written once.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "ngram.h"
+
+namespace {
+
+constexpr int kK = NGRAM_K;
+constexpr uint32_t kPad = NGRAM_PAD_ID;
+constexpr int kVec = 8;                 // table elements per lane per slice
+constexpr int kSlice = 64 * kVec;       // columns per wavefront slice
+constexpr uint32_t kNaNbf16 = 0x7FC0u;
+constexpr uint32_t kNaNf32 = 0x7FC00000u;
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Seeds {
+    uint64_t s[kK];
+};
+
+// splitmix64 (Steele, Lea and Flood, OOPSLA 2014; Vigna's finaliser
+// constants): the generator's first output from state x.
+__host__ __device__ inline uint64_t splitmix64(uint64_t x) {
+    uint64_t z = x + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// ---------------------------------------------------------------------------
+// Context: (w_t, w_{t-1}, w_{t-2}) of token i, from its own sequence, else the
+// sequence's history, else the pad id.  Memory-safe for any seq_offsets.
+struct Ctx {
+    uint32_t c0, c1, c2;
+    bool ok;
+};
+
+__device__ inline Ctx token_context(const int32_t* __restrict__ tok, int64_t i,
+                                    const int32_t* __restrict__ so, int S,
+                                    const int32_t* __restrict__ hist, uint32_t c0_limit) {
+    int lo = 0, hi = S - 1;     // the last sequence s with so[s] <= i
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(so[mid]) <= i) lo = mid; else hi = mid - 1;
+    }
+    const int64_t p = i - static_cast<int64_t>(so[lo]);
+    const uint32_t h0 = hist ? static_cast<uint32_t>(hist[2 * lo]) : kPad;
+    const uint32_t h1 = hist ? static_cast<uint32_t>(hist[2 * lo + 1]) : kPad;
+    Ctx c;
+    c.c0 = static_cast<uint32_t>(tok[i]);
+    c.c1 = (p >= 1 && i >= 1) ? static_cast<uint32_t>(tok[i - 1]) : h1;
+    c.c2 = (p >= 2 && i >= 2) ? static_cast<uint32_t>(tok[i - 2]) : (p == 1 ? h1 : h0);
+    c.ok = c.c0 < c0_limit && c.c1 <= kPad && c.c2 <= kPad;
+    return c;
+}
+
+__device__ inline int32_t hashed_row(const Ctx& c, int k, const Seeds& sd, uint64_t R) {
+    const uint64_t c0 = c.c0, c1 = c.c1, c2 = c.c2;
+    const uint64_t bigram = (c1 << 21) | c0;
+    const uint64_t trigram = (c2 << 42) | (c1 << 21) | c0;
+    const uint64_t key = k < 8 ? bigram : trigram;
+    return static_cast<int32_t>(splitmix64(key ^ sd.s[k]) % R);
+}
+
+// ---------------------------------------------------------------------------
+// Element helpers.
+__device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ inline uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return kNaNbf16;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eight table elements of one row slice, as fp32.
+template <int DT> struct Row8;
+
+template <> struct Row8<NGRAM_TABLE_BF16> {
+    using Raw = uint4;
+    __device__ static Raw load(const void* base, int64_t off) {
+        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    }
+};
+template <> struct Row8<NGRAM_TABLE_INT8_ROWSCALE> {
+    using Raw = uint2;
+    __device__ static Raw load(const void* base, int64_t off) {
+        return *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(base) + off);
+    }
+};
+
+__device__ inline void add_row(float acc[8], const uint4& v) {
+    acc[0] = acc[0] + bf16lo(v.x); acc[1] = acc[1] + bf16hi(v.x);
+    acc[2] = acc[2] + bf16lo(v.y); acc[3] = acc[3] + bf16hi(v.y);
+    acc[4] = acc[4] + bf16lo(v.z); acc[5] = acc[5] + bf16hi(v.z);
+    acc[6] = acc[6] + bf16lo(v.w); acc[7] = acc[7] + bf16hi(v.w);
+}
+
+__device__ inline float i8f(uint32_t w, int b) {
+    return static_cast<float>(static_cast<int8_t>((w >> (8 * b)) & 0xFFu));
+}
+
+__device__ inline void fma_row(float acc[8], const uint2& v, float s) {
+    acc[0] = __builtin_fmaf(i8f(v.x, 0), s, acc[0]);
+    acc[1] = __builtin_fmaf(i8f(v.x, 1), s, acc[1]);
+    acc[2] = __builtin_fmaf(i8f(v.x, 2), s, acc[2]);
+    acc[3] = __builtin_fmaf(i8f(v.x, 3), s, acc[3]);
+    acc[4] = __builtin_fmaf(i8f(v.y, 0), s, acc[4]);
+    acc[5] = __builtin_fmaf(i8f(v.y, 1), s, acc[5]);
+    acc[6] = __builtin_fmaf(i8f(v.y, 2), s, acc[6]);
+    acc[7] = __builtin_fmaf(i8f(v.y, 3), s, acc[7]);
+}
+
+// The fp32 sum over k = 0..15 of the lane's 8 columns of rows r[0..15].
+// All 16 loads are issued before the first add.
+template <int DT>
+__device__ inline void gather_sum(float acc[8], const void* __restrict__ tab,
+                                  const float* __restrict__ scale, const int32_t r[kK],
+                                  int64_t d, int64_t j0) {
+    using Raw = typename Row8<DT>::Raw;
+    Raw v[kK];
+#pragma unroll
+    for (int k = 0; k < kK; ++k) v[k] = Row8<DT>::load(tab, static_cast<int64_t>(r[k]) * d + j0);
+    // Keep the scheduler from sinking loads below the adds: all 16 row
+    // loads of the slice are in flight before the first one is consumed.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    if constexpr (DT == NGRAM_TABLE_BF16) {
+#pragma unroll
+        for (int k = 0; k < kK; ++k) add_row(acc, v[k]);
+    } else {
+        float s[kK];
+#pragma unroll
+        for (int k = 0; k < kK; ++k) s[k] = scale[r[k]];
+#pragma unroll
+        for (int k = 0; k < kK; ++k) fma_row(acc, v[k], s[k]);
+    }
+}
+
+// out = bf16(res + fmaf(w, acc, e1)) for the lane's 8 columns.
+template <bool E1, bool RES>
+__device__ inline uint4 gate8(const float acc[8], const float w[8], const uint16_t* __restrict__ e1row,
+                              const uint16_t* __restrict__ resrow) {
+    float base[8];
+    if constexpr (E1) {
+        const uint4 e = *reinterpret_cast<const uint4*>(e1row);
+        base[0] = bf16lo(e.x); base[1] = bf16hi(e.x); base[2] = bf16lo(e.y); base[3] = bf16hi(e.y);
+        base[4] = bf16lo(e.z); base[5] = bf16hi(e.z); base[6] = bf16lo(e.w); base[7] = bf16hi(e.w);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) base[q] = 0.0f;
+    }
+    float y[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) y[q] = __builtin_fmaf(w[q], acc[q], base[q]);
+    if constexpr (RES) {
+        const uint4 rv = *reinterpret_cast<const uint4*>(resrow);
+        y[0] = bf16lo(rv.x) + y[0]; y[1] = bf16hi(rv.x) + y[1];
+        y[2] = bf16lo(rv.y) + y[2]; y[3] = bf16hi(rv.y) + y[3];
+        y[4] = bf16lo(rv.z) + y[4]; y[5] = bf16hi(rv.z) + y[5];
+        y[6] = bf16lo(rv.w) + y[6]; y[7] = bf16hi(rv.w) + y[7];
+    }
+    uint4 o;
+    o.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
+    o.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
+    o.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
+    o.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
+    return o;
+}
+
+__device__ inline void load_w8(float w[8], const float* __restrict__ wg, int64_t j0) {
+    const float4 a = *reinterpret_cast<const float4*>(wg + j0);
+    const float4 b = *reinterpret_cast<const float4*>(wg + j0 + 4);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// Fused kernel: context, hash, gather, sum, gate, residual, rounding.
+struct FwdArgs {
+    const int32_t* tok;
+    const int32_t* so;
+    const int32_t* hist;
+    const void* tab;
+    const float* scale;
+    const uint16_t* e1;
+    const float* wg;
+    const uint16_t* res;
+    uint16_t* out;
+    int32_t* rows_out;
+    int64_t n;
+    uint64_t R;
+    int32_t S;
+    int32_t d;
+    int32_t tpw;        // tokens per workgroup
+    uint32_t c0_limit;  // token ids must be below this (V, capped at the pad id)
+    Seeds sd;
+};
+
+template <int DT, bool E1, bool RES>
+__global__ void __launch_bounds__(1024) ngram_fwd_kernel(const FwdArgs a) {
+    extern __shared__ int32_t lds[];
+    int32_t* lrows = lds;                 // [tpw][16] row ids (-1: invalid token)
+    int32_t* ltok = lds + a.tpw * kK;     // [tpw] w_t (-1: invalid token)
+    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * a.tpw;
+
+    for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
+        const int tl = t >> 4, k = t & (kK - 1);
+        const int64_t i = tile0 + tl;
+        int32_t row = -1, c0 = -1;
+        if (i < a.n) {
+            const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
+            if (c.ok) {
+                row = hashed_row(c, k, a.sd, a.R);
+                c0 = static_cast<int32_t>(c.c0);
+            }
+            if (a.rows_out) a.rows_out[i * kK + k] = row;
+        }
+        lrows[t] = row;
+        if (k == 0) ltok[tl] = c0;
+    }
+    __syncthreads();
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t d = a.d;
+    const int nslices = (a.d + kSlice - 1) / kSlice;
+    const int64_t rem = a.n - tile0;
+    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+    for (int sl = wave; sl < nslices; sl += nwaves) {
+        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+        if (j0 >= d) continue;
+        float w[8];
+        load_w8(w, a.wg, j0);
+        for (int tl = 0; tl < tile_n; ++tl) {
+            const int64_t i = tile0 + tl;
+            uint16_t* o = a.out + i * d + j0;
+            const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
+            if (c0 < 0) {
+                const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
+                *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
+                continue;
+            }
+            int32_t r[kK];
+#pragma unroll
+            for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
+            float acc[8];
+            gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+            const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
+            const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
+            *reinterpret_cast<uint4*>(o) = gate8<E1, RES>(acc, w, e1row, resrow);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Unfused pieces: hash, gather-sum (fp32 out), gate-add.
+struct HashArgs {
+    const int32_t* tok;
+    const int32_t* so;
+    const int32_t* hist;
+    int32_t* rows_out;
+    int64_t n;
+    uint64_t R;
+    int32_t S;
+    uint32_t c0_limit;
+    Seeds sd;
+};
+
+__global__ void __launch_bounds__(256) ngram_hash_kernel(const HashArgs a) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= a.n * kK) return;
+    const int64_t i = t >> 4;
+    const int k = static_cast<int>(t & (kK - 1));
+    const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
+    a.rows_out[t] = c.ok ? hashed_row(c, k, a.sd, a.R) : -1;
+}
+
+struct BagArgs {
+    const void* tab;
+    const float* scale;
+    const int32_t* rows;
+    float* eN;
+    int64_t n;
+    int64_t R;
+    int32_t d;
+    int32_t tpw;
+};
+
+template <int DT>
+__global__ void __launch_bounds__(1024) ngram_bag_kernel(const BagArgs a) {
+    extern __shared__ int32_t lds[];
+    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * a.tpw;
+    for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
+        const int64_t i = tile0 + (t >> 4);
+        int32_t r = -1;
+        if (i < a.n) {
+            r = a.rows[i * kK + (t & (kK - 1))];
+            if (r < 0 || r >= a.R) r = -1;
+        }
+        lds[t] = r;
+    }
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t d = a.d;
+    const int nslices = (a.d + kSlice - 1) / kSlice;
+    const int64_t rem = a.n - tile0;
+    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+    for (int sl = wave; sl < nslices; sl += nwaves) {
+        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+        if (j0 >= d) continue;
+        for (int tl = 0; tl < tile_n; ++tl) {
+            float* o = a.eN + (tile0 + tl) * d + j0;
+            int32_t r[kK];
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < kK; ++k) {
+                r[k] = __builtin_amdgcn_readfirstlane(lds[tl * kK + k]);
+                ok = ok && r[k] >= 0;
+            }
+            float acc[8];
+            if (ok) {
+                gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
+            }
+            reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+    }
+}
+
+struct GateArgs {
+    const float* eN;
+    const int32_t* tok;
+    const uint16_t* e1;
+    const float* wg;
+    const uint16_t* res;
+    uint16_t* out;
+    int64_t n;
+    int32_t d;
+    uint32_t c0_limit;
+};
+
+template <bool E1, bool RES>
+__global__ void __launch_bounds__(256) ngram_gate_kernel(const GateArgs a) {
+    const int64_t dv = a.d / kVec;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (g >= a.n * dv) return;
+    const int64_t i = g / dv;
+    const int64_t j0 = (g - i * dv) * kVec;
+    const int64_t d = a.d;
+    uint16_t* o = a.out + i * d + j0;
+    const uint32_t c0 = static_cast<uint32_t>(a.tok[i]);
+    if (c0 >= a.c0_limit) {
+        const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
+        *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
+        return;
+    }
+    const float4 x0 = reinterpret_cast<const float4*>(a.eN + i * d + j0)[0];
+    const float4 x1 = reinterpret_cast<const float4*>(a.eN + i * d + j0)[1];
+    const float acc[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float w[8];
+    load_w8(w, a.wg, j0);
+    const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
+    const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
+    *reinterpret_cast<uint4*>(o) = gate8<E1, RES>(acc, w, e1row, resrow);
+}
+
+// Zero-copy staging of host-table rows: one wavefront per (token, k) row
+// and 16-byte (bf16) or 8-byte (int8) lanes; stage row t = i*16 + k.
+struct StageArgs {
+    const void* tab;
+    const float* scale;
+    const int32_t* rows;
+    void* stage;
+    float* stage_scale;
+    int32_t* remap;
+    int64_t nrows;      // n * 16
+    int64_t R;
+    int64_t row_bytes;
+};
+
+template <typename U>
+__global__ void __launch_bounds__(256) ngram_stage_kernel(const StageArgs a) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (t >= a.nrows) return;
+    const int lane = threadIdx.x & 63;
+    const int32_t r = a.rows[t];
+    const bool ok = r >= 0 && r < a.R;
+    if (lane == 0) {
+        a.remap[t] = ok ? static_cast<int32_t>(t) : -1;
+        if (ok && a.stage_scale) a.stage_scale[t] = a.scale[r];
+    }
+    if (!ok) return;
+    const U* src = reinterpret_cast<const U*>(static_cast<const char*>(a.tab) + static_cast<int64_t>(r) * a.row_bytes);
+    U* dst = reinterpret_cast<U*>(static_cast<char*>(a.stage) + t * a.row_bytes);
+    const int64_t nu = a.row_bytes / static_cast<int64_t>(sizeof(U));
+    for (int64_t q = lane; q < nu; q += 64) dst[q] = src[q];
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+int hip_status(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(NGRAM_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return NGRAM_OK;
+}
+
+int check_table(const ngram_table* T) {
+    if (!T) return fail(NGRAM_EINVAL, "table is NULL");
+    if (!T->data) return fail(NGRAM_EINVAL, "table data is NULL");
+    if (T->R < 1 || T->R > NGRAM_MAX_ROWS) return fail(NGRAM_ERANGE, "R=%lld outside [1, 2^31-1]", (long long)T->R);
+    if (T->d <= 0 || T->d % kVec != 0) return fail(NGRAM_EINVAL, "d=%d must be a positive multiple of 8", T->d);
+    if (T->d > NGRAM_MAX_D) return fail(NGRAM_ERANGE, "d=%d above %d", T->d, NGRAM_MAX_D);
+    if (T->dtype == NGRAM_TABLE_BF16) {
+        if (!aligned(T->data, 16)) return fail(NGRAM_EALIGN, "bf16 table data not 16-byte aligned");
+    } else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) {
+        if (!aligned(T->data, 8)) return fail(NGRAM_EALIGN, "int8 table data not 8-byte aligned");
+        if (!T->row_scale) return fail(NGRAM_EINVAL, "int8 table needs row_scale");
+        if (!aligned(T->row_scale, 4)) return fail(NGRAM_EALIGN, "row_scale not 4-byte aligned");
+    } else {
+        return fail(NGRAM_EINVAL, "unknown table dtype %d", T->dtype);
+    }
+    if (T->location != NGRAM_IN_DEVICE && T->location != NGRAM_IN_HOST)
+        return fail(NGRAM_EINVAL, "unknown table location %d", T->location);
+    return NGRAM_OK;
+}
+
+// The device-side address of the table data (host tables: the mapping).
+int table_device_ptr(const ngram_table* T, const void** out) {
+    if (T->location == NGRAM_IN_DEVICE) {
+        *out = T->data;
+        return NGRAM_OK;
+    }
+    void* dp = nullptr;
+    const hipError_t e = hipHostGetDevicePointer(&dp, const_cast<void*>(T->data), 0);
+    if (e != hipSuccess || !dp) {
+        (void)hipGetLastError();
+        return fail(NGRAM_EHIP, "host table is not pinned, device-mapped memory: %s", hipGetErrorString(e));
+    }
+    *out = dp;
+    return NGRAM_OK;
+}
+
+int check_tokens(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S) {
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > INT32_MAX) return fail(NGRAM_ERANGE, "n=%lld above 2^31-1", (long long)n);
+    if (n > 0 && !tokens) return fail(NGRAM_EINVAL, "tokens is NULL");
+    if (n > 0 && !seq_offsets) return fail(NGRAM_EINVAL, "seq_offsets is NULL");
+    if (n > 0 && S < 1) return fail(NGRAM_EINVAL, "S=%d must be >= 1 when n > 0", S);
+    return NGRAM_OK;
+}
+
+Seeds make_seeds(const uint64_t* seeds) {
+    Seeds s;
+    for (int k = 0; k < kK; ++k) s.s[k] = seeds ? seeds[k] : splitmix64(static_cast<uint64_t>(k) * 0x9E3779B97F4A7C15ull);
+    return s;
+}
+
+uint32_t c0_limit_for(const uint16_t* e1, int64_t V) {
+    if (!e1) return kPad;
+    return V < static_cast<int64_t>(kPad) ? static_cast<uint32_t>(V) : kPad;
+}
+
+// Launch shape of the slice kernels: one wavefront per 512-column slice (at
+// most 16 per workgroup) and `tpw` tokens per workgroup.
+struct Shape {
+    int waves;
+    int tpw;
+};
+
+Shape slice_shape(int64_t n, int32_t d) {
+    const int nslices = (d + kSlice - 1) / kSlice;
+    Shape s;
+    s.waves = nslices < 16 ? nslices : 16;
+    int tpw = env_int("NGRAM_TOKENS_PER_WG", 0);
+    if (tpw <= 0) tpw = n >= 4096 ? 4 : 1;
+    if (tpw > 64) tpw = 64;
+    s.tpw = tpw;
+    return s;
+}
+
+template <int DT, bool E1, bool RES>
+void launch_fwd(const FwdArgs& a, const Shape& sh, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>((a.n + sh.tpw - 1) / sh.tpw));
+    const dim3 block(64 * sh.waves);
+    const size_t lds = static_cast<size_t>(sh.tpw) * (kK + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES>), grid, block, lds, st, a);
+}
+
+template <int DT>
+void launch_fwd_dt(const FwdArgs& a, const Shape& sh, hipStream_t st) {
+    const bool e1 = a.e1 != nullptr, res = a.res != nullptr;
+    if (e1 && res) launch_fwd<DT, true, true>(a, sh, st);
+    else if (e1) launch_fwd<DT, true, false>(a, sh, st);
+    else if (res) launch_fwd<DT, false, true>(a, sh, st);
+    else launch_fwd<DT, false, false>(a, sh, st);
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* ngram_status_string(int status) {
+    switch (status) {
+        case NGRAM_OK: return "NGRAM_OK";
+        case NGRAM_EINVAL: return "NGRAM_EINVAL: invalid argument";
+        case NGRAM_EALIGN: return "NGRAM_EALIGN: misaligned pointer";
+        case NGRAM_ERANGE: return "NGRAM_ERANGE: size out of range";
+        case NGRAM_EHIP: return "NGRAM_EHIP: HIP runtime error";
+        case NGRAM_ENOTSUP: return "NGRAM_ENOTSUP: not supported";
+        default: return "unknown ngram status";
+    }
+}
+
+const char* ngram_last_error(void) { return g_err; }
+
+int ngram_version(void) { return 1; }
+
+void ngram_default_seeds(uint64_t seeds[NGRAM_K]) {
+    const Seeds s = make_seeds(nullptr);
+    for (int k = 0; k < kK; ++k) seeds[k] = s.s[k];
+}
+
+int ngram_hash(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+               const int32_t* history, const uint64_t* seeds, int64_t R, int32_t* rows_out,
+               ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_tokens(tokens, n, seq_offsets, S);
+    if (rc) return rc;
+    if (R < 1 || R > NGRAM_MAX_ROWS) return fail(NGRAM_ERANGE, "R=%lld outside [1, 2^31-1]", (long long)R);
+    if (n > 0 && !rows_out) return fail(NGRAM_EINVAL, "rows_out is NULL");
+    if (n == 0) return NGRAM_OK;
+    HashArgs a;
+    a.tok = tokens; a.so = seq_offsets; a.hist = history; a.rows_out = rows_out;
+    a.n = n; a.R = static_cast<uint64_t>(R); a.S = S; a.c0_limit = kPad;
+    a.sd = make_seeds(seeds);
+    const int64_t total = n * kK;
+    hipLaunchKernelGGL(ngram_hash_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                       stream, a);
+    return hip_status("ngram_hash launch");
+}
+
+int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
+                    ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_table(T);
+    if (rc) return rc;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > INT32_MAX) return fail(NGRAM_ERANGE, "n=%lld above 2^31-1", (long long)n);
+    if (n > 0 && (!rows || !eN_out)) return fail(NGRAM_EINVAL, "rows or eN_out is NULL");
+    if (n > 0 && !aligned(eN_out, 16)) return fail(NGRAM_EALIGN, "eN_out not 16-byte aligned");
+    if (n == 0) return NGRAM_OK;
+    const void* tab = nullptr;
+    rc = table_device_ptr(T, &tab);
+    if (rc) return rc;
+    BagArgs a;
+    a.tab = tab; a.scale = T->row_scale; a.rows = rows; a.eN = eN_out;
+    a.n = n; a.R = T->R; a.d = T->d;
+    const Shape sh = slice_shape(n, T->d);
+    a.tpw = sh.tpw;
+    const dim3 grid(static_cast<unsigned>((n + sh.tpw - 1) / sh.tpw)), block(64 * sh.waves);
+    const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
+    if (T->dtype == NGRAM_TABLE_BF16)
+        hipLaunchKernelGGL(ngram_bag_kernel<NGRAM_TABLE_BF16>, grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL(ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE>, grid, block, lds, stream, a);
+    return hip_status("ngram_embed_bag launch");
+}
+
+int ngram_gate_add(const float* eN, const int32_t* tokens, int64_t n, int32_t d,
+                   const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
+                   uint16_t* out, ngram_stream_t stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > INT32_MAX) return fail(NGRAM_ERANGE, "n=%lld above 2^31-1", (long long)n);
+    if (d <= 0 || d % kVec != 0) return fail(NGRAM_EINVAL, "d=%d must be a positive multiple of 8", d);
+    if (d > NGRAM_MAX_D) return fail(NGRAM_ERANGE, "d=%d above %d", d, NGRAM_MAX_D);
+    if (!W_g) return fail(NGRAM_EINVAL, "W_g is NULL");
+    if (e1 && V < 1) return fail(NGRAM_ERANGE, "V=%lld must be >= 1 with e1", (long long)V);
+    if (n > 0 && (!eN || !tokens || !out)) return fail(NGRAM_EINVAL, "eN, tokens or out is NULL");
+    if (!aligned(W_g, 16) || (e1 && !aligned(e1, 16)) || (residual && !aligned(residual, 16)) ||
+        (n > 0 && (!aligned(eN, 16) || !aligned(out, 16))))
+        return fail(NGRAM_EALIGN, "eN, e1, W_g, residual and out must be 16-byte aligned");
+    if (n == 0) return NGRAM_OK;
+    GateArgs a;
+    a.eN = eN; a.tok = tokens; a.e1 = e1; a.wg = W_g; a.res = residual; a.out = out;
+    a.n = n; a.d = d; a.c0_limit = c0_limit_for(e1, V);
+    const int64_t total = n * (d / kVec);
+    const dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
+    if (e1 && residual) hipLaunchKernelGGL((ngram_gate_kernel<true, true>), grid, block, 0, stream, a);
+    else if (e1) hipLaunchKernelGGL((ngram_gate_kernel<true, false>), grid, block, 0, stream, a);
+    else if (residual) hipLaunchKernelGGL((ngram_gate_kernel<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((ngram_gate_kernel<false, false>), grid, block, 0, stream, a);
+    return hip_status("ngram_gate_add launch");
+}
+
+int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                  const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                  const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
+                  uint16_t* out, int32_t* rows_out, ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_tokens(tokens, n, seq_offsets, S);
+    if (rc) return rc;
+    rc = check_table(T);
+    if (rc) return rc;
+    if (!W_g) return fail(NGRAM_EINVAL, "W_g is NULL");
+    if (e1 && V < 1) return fail(NGRAM_ERANGE, "V=%lld must be >= 1 with e1", (long long)V);
+    if (n > 0 && !out) return fail(NGRAM_EINVAL, "out is NULL");
+    if (!aligned(W_g, 16) || (e1 && !aligned(e1, 16)) || (residual && !aligned(residual, 16)) ||
+        (n > 0 && !aligned(out, 16)))
+        return fail(NGRAM_EALIGN, "e1, W_g, residual and out must be 16-byte aligned");
+    if (n == 0) return NGRAM_OK;
+    const void* tab = nullptr;
+    rc = table_device_ptr(T, &tab);
+    if (rc) return rc;
+    FwdArgs a;
+    a.tok = tokens; a.so = seq_offsets; a.hist = history; a.tab = tab; a.scale = T->row_scale;
+    a.e1 = e1; a.wg = W_g; a.res = residual; a.out = out; a.rows_out = rows_out;
+    a.n = n; a.R = static_cast<uint64_t>(T->R); a.S = S; a.d = T->d;
+    a.c0_limit = c0_limit_for(e1, V);
+    a.sd = make_seeds(seeds);
+    const Shape sh = slice_shape(n, T->d);
+    a.tpw = sh.tpw;
+    if (T->dtype == NGRAM_TABLE_BF16) launch_fwd_dt<NGRAM_TABLE_BF16>(a, sh, stream);
+    else launch_fwd_dt<NGRAM_TABLE_INT8_ROWSCALE>(a, sh, stream);
+    return hip_status("ngram_forward launch");
+}
+
+int ngram_host_alloc(int64_t bytes, void** host_ptr) {
+    g_err[0] = 0;
+    if (!host_ptr) return fail(NGRAM_EINVAL, "host_ptr is NULL");
+    *host_ptr = nullptr;
+    if (bytes <= 0) return fail(NGRAM_EINVAL, "bytes=%lld must be positive", (long long)bytes);
+    void* p = nullptr;
+    const hipError_t e = hipHostMalloc(&p, static_cast<size_t>(bytes), hipHostMallocMapped | hipHostMallocNonCoherent);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NGRAM_EHIP, "hipHostMalloc(%lld): %s", (long long)bytes, hipGetErrorString(e));
+    }
+    *host_ptr = p;
+    return NGRAM_OK;
+}
+
+int ngram_host_free(void* host_ptr) {
+    g_err[0] = 0;
+    if (!host_ptr) return NGRAM_OK;
+    const hipError_t e = hipHostFree(host_ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NGRAM_EHIP, "hipHostFree: %s", hipGetErrorString(e));
+    }
+    return NGRAM_OK;
+}
+
+int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
+                      void* stage_out, float* stage_scale_out, int32_t* remap_out,
+                      ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_table(T_host);
+    if (rc) return rc;
+    if (T_host->location != NGRAM_IN_HOST) return fail(NGRAM_ENOTSUP, "ngram_gather_host needs a host table");
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > INT32_MAX / kK) return fail(NGRAM_ERANGE, "n=%lld above (2^31-1)/16", (long long)n);
+    if (n > 0 && (!rows || !stage_out || !remap_out)) return fail(NGRAM_EINVAL, "rows, stage_out or remap_out is NULL");
+    if (n > 0 && T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE && !stage_scale_out)
+        return fail(NGRAM_EINVAL, "int8 table needs stage_scale_out");
+    if (n > 0 && !aligned(stage_out, 16)) return fail(NGRAM_EALIGN, "stage_out not 16-byte aligned");
+    if (n == 0) return NGRAM_OK;
+    const void* tab = nullptr;
+    rc = table_device_ptr(T_host, &tab);
+    if (rc) return rc;
+    StageArgs a;
+    a.tab = tab; a.scale = T_host->row_scale; a.rows = rows; a.stage = stage_out;
+    a.stage_scale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? stage_scale_out : nullptr;
+    a.remap = remap_out; a.nrows = n * kK; a.R = T_host->R;
+    a.row_bytes = static_cast<int64_t>(T_host->d) * (T_host->dtype == NGRAM_TABLE_BF16 ? 2 : 1);
+    const dim3 grid(static_cast<unsigned>((a.nrows + 3) / 4)), block(256);
+    if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(ngram_stage_kernel<uint4>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(ngram_stage_kernel<uint2>, grid, block, 0, stream, a);
+    return hip_status("ngram_gather_host launch");
+}
+
+}  // extern "C"

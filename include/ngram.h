@@ -1,0 +1,160 @@
+/*
+ * ngram.h — C ABI of libngram.so: the hashed n-gram embedding gather-sum on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  "Qwen Brought Back N-Grams. All 51 Billion Parameters of
+ * Them.", section "N-grams, of all things": for each token the bigram and
+ * trigram context is hashed into one learned table (20,000,000 rows x 2560),
+ * 16 rows are gathered and summed into one 2560-wide vector, which is added to
+ * the residual stream.  "Qwen3.8-Flash-Next: A 51B N-gram Embedding Table
+ * with Heterogeneous Memory Prefetch", Key point 1: the sum is fused with the
+ * 1-gram embedding through an elementwise gate, h = e_1gram(w_t) + W_g (.) e_N.
+ *
+ * The pages leave the hash open.  This library fixes it:
+ *   c0 = w_t, c1 = w_{t-1}, c2 = w_{t-2}, each a 21-bit field; context before
+ *   a sequence's first token is the caller's 2-token history, else NGRAM_PAD_ID;
+ *   bigram key  K2 = c1 << 21 | c0, trigram key K3 = c2 << 42 | c1 << 21 | c0;
+ *   row_k = splitmix64(K ^ seed_k) mod R, K = K2 for k = 0..7, K3 for 8..15,
+ *   where splitmix64(x) is the first output of Steele, Lea and Flood's
+ *   splitmix64 generator from state x, and the default seed_k is output k of
+ *   that generator from state 0.
+ * Arithmetic: acc = +0.0f; for k = 0..15: acc += (float)T[row_k][j] (bf16
+ * table) or acc = fmaf((float)q[row_k][j], scale[row_k], acc) (int8 table);
+ * h = fmaf(W_g[j], acc, e1[w_t][j]) (or + 0 without e1); y = residual + h (or h);
+ * out = bf16 round-to-nearest-even of y (NaN -> 0x7FC0).  The order is fixed,
+ * so results are reproducible bit for bit.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned (hipMalloc / torch).  The library
+ *     allocates nothing in a compute call, keeps no state between calls, and
+ *     only enqueues work on `stream` (NULL = the default stream): no sync.
+ *   - Row-major layouts; bf16 values are passed as their uint16_t bit pattern.
+ *   - Return value: NGRAM_OK or a negative ngram_status.  Arguments are
+ *     checked on the host before anything is enqueued; on error nothing is
+ *     launched.  ngram_last_error() gives a message (thread-local).
+ *   - Token ids in [0, V) (and < NGRAM_PAD_ID), history ids in [0, NGRAM_PAD_ID]
+ *     and row ids in [0, R) are preconditions checked on the device: a token
+ *     that breaks one gets NaN outputs (bf16 0x7FC0 / fp32 0x7FC00000) and row
+ *     ids -1, and no memory outside the arguments is ever read.
+ *   - seq_offsets[S+1] (int32, device) must rise from 0 to n; sequence s
+ *     holds tokens seq_offsets[s] .. seq_offsets[s+1]-1; empty sequences are
+ *     allowed.
+ */
+#ifndef NGRAM_H
+#define NGRAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NGRAM_K 16                 /* rows per token: 8 bigram + 8 trigram seeds */
+#define NGRAM_PAD_ID 0x1FFFFF      /* 2^21 - 1, context before a sequence start */
+#define NGRAM_MAX_ROWS 2147483647  /* R <= 2^31 - 1 (row ids are int32) */
+#define NGRAM_MAX_D 65536          /* row width limit */
+
+typedef struct ihipStream_t* ngram_stream_t;   /* the same type as hipStream_t */
+
+typedef enum {
+    NGRAM_OK = 0,
+    NGRAM_EINVAL = -1,   /* null pointer, negative size, bad enum, d % 8 != 0 */
+    NGRAM_EALIGN = -2,   /* a pointer is not aligned as documented */
+    NGRAM_ERANGE = -3,   /* R, d or V outside the supported range */
+    NGRAM_EHIP = -4,     /* the HIP runtime reported an error */
+    NGRAM_ENOTSUP = -5   /* a combination this build does not support */
+} ngram_status;
+
+typedef enum { NGRAM_TABLE_BF16 = 0, NGRAM_TABLE_INT8_ROWSCALE = 1 } ngram_dtype;
+typedef enum { NGRAM_IN_DEVICE = 0, NGRAM_IN_HOST = 1 } ngram_location;
+
+/* The hashed table: [R][d] row-major.  bf16: data 16-byte aligned.  int8:
+ * data 8-byte aligned and row_scale[R] fp32 (4-byte aligned), value of
+ * element j of row r = q[r][j] * row_scale[r].  location NGRAM_IN_DEVICE: data
+ * and row_scale in device memory.  NGRAM_IN_HOST: data is pinned host memory
+ * mapped for the device (ngram_host_alloc, or hipHostMalloc); rows are read
+ * over PCIe by the GPU (zero copy); row_scale stays in device memory. */
+typedef struct {
+    const void* data;
+    const float* row_scale;
+    int64_t R;
+    int32_t d;
+    int32_t dtype;      /* ngram_dtype */
+    int32_t location;   /* ngram_location */
+    int32_t reserved;
+} ngram_table;
+
+const char* ngram_status_string(int status);
+const char* ngram_last_error(void);
+int ngram_version(void);
+
+/* seeds[k], k = 0..15: outputs 0..15 of the splitmix64 generator from state 0. */
+void ngram_default_seeds(uint64_t seeds[NGRAM_K]);
+
+/* Context and hash: "N-grams, of all things" + the fixed hash
+ * above.  tokens[n] int32, seq_offsets[S+1] int32, history[S][2] int32 (w_{t-2},
+ * w_{t-1} before the sequence) or NULL for pad, seeds: HOST array of 16 or
+ * NULL for the defaults.  Writes rows_out[n][16] int32 (device).
+ * Errors: EINVAL (null / n < 0 / S < 1 with n > 0), ERANGE (R outside
+ * [1, 2^31-1]). */
+int ngram_hash(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+               const int32_t* history, const uint64_t* seeds, int64_t R, int32_t* rows_out,
+               ngram_stream_t stream);
+
+/* Gather and sum: "N-grams, of all things": eN_out[i][j] =
+ * the fp32 sum over k = 0..15 in order of row rows[i][k] of T (dequantised
+ * inside the sum for int8).  rows[n][16] int32 (device), eN_out[n][d] fp32
+ * (device, 16-byte aligned).  T may live in device or pinned host memory.
+ * Errors: EINVAL, EALIGN, ERANGE (see ngram_table). */
+int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
+                    ngram_stream_t stream);
+
+/* Gate and residual: "Qwen3.8-Flash-Next: …", Key point 1, and the
+ * residual add of "N-grams, of all things": out[i][j] = bf16(residual[i][j] +
+ * fmaf(W_g[j], eN[i][j], e1[tokens[i]][j])).  eN[n][d] fp32, tokens[n] int32,
+ * e1[V][d] bf16 or NULL, W_g[d] fp32, residual[n][d] bf16 or NULL, out[n][d]
+ * bf16; out may equal residual (in-place update).  All device, eN / e1 / W_g /
+ * residual / out 16-byte aligned.  Errors: EINVAL, EALIGN, ERANGE (V < 1). */
+int ngram_gate_add(const float* eN, const int32_t* tokens, int64_t n, int32_t d,
+                   const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
+                   uint16_t* out, ngram_stream_t stream);
+
+/* The whole path in one kernel: context, hash, gather, fp32 sum,
+ * gate, residual add and bf16 rounding.  Same arguments and rules as the
+ * three calls above; the row lists live in LDS; rows_out[n][16] (device) is
+ * written when non-NULL.  Results are bit-identical to ngram_hash +
+ * ngram_embed_bag + ngram_gate_add. */
+int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                  const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                  const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
+                  uint16_t* out, int32_t* rows_out, ngram_stream_t stream);
+
+/* Pinned-host-table path, "N-grams, of all things" / "Which is why the
+ * offload matters more than the parameter count": the table shard sits in
+ * pinned host memory and the selected rows are gathered by the GPU over PCIe
+ * on a side stream, overlapped with compute on the main stream.
+ *
+ * ngram_host_alloc: pinned, device-mapped, 4 KiB-aligned host memory of
+ * `bytes` bytes (hipHostMalloc); *host_ptr receives it; free with
+ * ngram_host_free.  These two are the only calls that allocate. */
+int ngram_host_alloc(int64_t bytes, void** host_ptr);
+int ngram_host_free(void* host_ptr);
+
+/* Copy the 16 selected rows of each token from a table in pinned host memory
+ * into a device staging table: stage_out row i*16+k = T_host row rows[i][k]
+ * (raw element bytes, d elements of the table's dtype; stage_out [n*16][d],
+ * 16-byte aligned), stage_scale_out[i*16+k] = its row scale (int8 tables
+ * only, else may be NULL), remap_out[i][k] = i*16+k, or -1 where rows[i][k]
+ * is outside [0, R) (that stage row is left unwritten).  ngram_embed_bag on
+ * the staging table (R' = n*16, in device memory) with remap_out then gives
+ * exactly what ngram_embed_bag gives on T_host with rows.  Run it on a side
+ * stream and join with an event.  Errors: EINVAL, EALIGN, ERANGE, and
+ * ENOTSUP when T_host is not in host memory. */
+int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
+                      void* stage_out, float* stage_scale_out, int32_t* remap_out,
+                      ngram_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NGRAM_H */

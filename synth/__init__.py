@@ -177,3 +177,37 @@ def seq_offsets(n_seqs: int, seq_len: int) -> np.ndarray:
 
 def ragged_offsets(lengths) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+# ------------------------------ GPU fill ------------------------------------
+_gpu_lib = None
+
+
+def _gpu():
+    global _gpu_lib
+    if _gpu_lib is None:
+        import ctypes
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth.so")
+        if not os.path.exists(path):
+            raise RuntimeError("synth/libsynth.so is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(path)
+        L.synth_fill.restype = ctypes.c_int
+        L.synth_fill.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        _gpu_lib = L
+    return _gpu_lib
+
+
+def fill_gpu(kind: int, seed: int, tag: int, t, offset: int = 0, stream=None):
+    """Fill the CUDA tensor ``t`` (flat view) with elements ``offset ..`` of the
+    generated tensor, on ``stream`` (default: the current stream)."""
+    import torch
+    assert t.is_cuda and t.is_contiguous()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = _gpu().synth_fill(int(kind), seed & 0xFFFFFFFFFFFFFFFF, int(tag), t.data_ptr(),
+                           t.numel(), int(offset), stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_fill failed: {rc}")
+    return t

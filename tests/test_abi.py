@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/ngram.h declares, and rejects bad arguments on the host (before any
+HIP call) with the documented status codes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import hashed_gram_embedding_ngram_amd as ng
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ngram.h")
+OK, EINVAL, EALIGN, ERANGE, EHIP, ENOTSUP = 0, -1, -2, -3, -4, -5
+A = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ngram_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = ctypes.CDLL(ng.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in ngram.h but not exported"
+    assert set(names) == set(ng._SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    L = ng.lib()
+    for s in (OK, EINVAL, EALIGN, ERANGE, EHIP, ENOTSUP):
+        assert L.ngram_status_string(s)
+    assert L.ngram_version() >= 1
+
+
+def test_default_seeds_equal_the_oracle_seeds():
+    # host code only: no GPU needed
+    assert ng.default_seeds() == [int(s) for s in oracle.default_seeds()]
+
+
+def _table(data=A, scale=None, R=1000, d=64, dtype=0, loc=0):
+    return ng._Table(data, scale, R, d, dtype, loc, 0)
+
+
+def _err():
+    return ng.lib().ngram_last_error().decode()
+
+
+def test_hash_argument_checks():
+    L = ng.lib()
+    seeds = None
+    assert L.ngram_hash(A, -1, A, 1, None, seeds, 10, A, None) == EINVAL
+    assert L.ngram_hash(None, 5, A, 1, None, seeds, 10, A, None) == EINVAL
+    assert L.ngram_hash(A, 5, None, 1, None, seeds, 10, A, None) == EINVAL
+    assert L.ngram_hash(A, 5, A, 0, None, seeds, 10, A, None) == EINVAL
+    assert L.ngram_hash(A, 5, A, 1, None, seeds, 0, A, None) == ERANGE
+    assert L.ngram_hash(A, 5, A, 1, None, seeds, 2**31, A, None) == ERANGE
+    assert "R=" in _err()
+    assert L.ngram_hash(A, 5, A, 1, None, seeds, 10, None, None) == EINVAL
+    assert L.ngram_hash(A, 2**31, A, 1, None, seeds, 10, A, None) == ERANGE
+    assert L.ngram_hash(None, 0, None, 0, None, seeds, 10, None, None) == OK   # empty: no launch
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(data=None), EINVAL), (dict(R=0), ERANGE), (dict(R=2**31), ERANGE),
+    (dict(d=12), EINVAL), (dict(d=0), EINVAL), (dict(d=-8), EINVAL), (dict(d=65544), ERANGE),
+    (dict(data=A + 2), EALIGN), (dict(dtype=7), EINVAL), (dict(dtype=1), EINVAL),
+    (dict(dtype=1, scale=A + 1), EALIGN), (dict(dtype=1, data=A + 4, scale=A), EALIGN),
+    (dict(loc=5), EINVAL),
+])
+def test_table_checks(kw, code):
+    L = ng.lib()
+    t = _table(**kw)
+    assert L.ngram_embed_bag(ctypes.byref(t), A, 4, A, None) == code, _err()
+    assert L.ngram_forward(A, 4, A, 1, None, None, ctypes.byref(t), None, 0, A, None, A, None, None) == code
+
+
+def test_embed_bag_checks():
+    L = ng.lib()
+    t = _table()
+    assert L.ngram_embed_bag(None, A, 4, A, None) == EINVAL
+    assert L.ngram_embed_bag(ctypes.byref(t), A, -1, A, None) == EINVAL
+    assert L.ngram_embed_bag(ctypes.byref(t), None, 4, A, None) == EINVAL
+    assert L.ngram_embed_bag(ctypes.byref(t), A, 4, None, None) == EINVAL
+    assert L.ngram_embed_bag(ctypes.byref(t), A, 4, A + 4, None) == EALIGN
+    assert L.ngram_embed_bag(ctypes.byref(t), None, 0, None, None) == OK
+    t8 = _table(dtype=1, data=A + 8, scale=A + 4)            # int8: 8-byte data alignment
+    assert L.ngram_embed_bag(ctypes.byref(t8), None, 0, None, None) == OK
+
+
+def test_gate_add_checks():
+    L = ng.lib()
+    assert L.ngram_gate_add(A, A, 4, 12, None, 0, A, None, A, None) == EINVAL
+    assert L.ngram_gate_add(A, A, 4, 65544, None, 0, A, None, A, None) == ERANGE
+    assert L.ngram_gate_add(A, A, 4, 64, None, 0, None, None, A, None) == EINVAL
+    assert L.ngram_gate_add(A, A, 4, 64, A, 0, A, None, A, None) == ERANGE
+    assert L.ngram_gate_add(A, A, 4, 64, None, 0, A, None, None, None) == EINVAL
+    assert L.ngram_gate_add(A, A, 4, 64, None, 0, A, None, A + 2, None) == EALIGN
+    assert L.ngram_gate_add(A, A, 4, 64, None, 0, A + 4, None, A, None) == EALIGN
+    assert L.ngram_gate_add(A, A, 4, 64, A, 10, A, A + 8, A, None) == EALIGN
+    assert L.ngram_gate_add(A, A, -4, 64, None, 0, A, None, A, None) == EINVAL
+    assert L.ngram_gate_add(None, None, 0, 64, None, 0, A, None, None, None) == OK
+
+
+def test_forward_checks():
+    L = ng.lib()
+    t = ctypes.byref(_table())
+    assert L.ngram_forward(A, 4, A, 1, None, None, t, None, 0, None, None, A, None, None) == EINVAL
+    assert L.ngram_forward(A, 4, A, 1, None, None, t, A, 0, A, None, A, None, None) == ERANGE
+    assert L.ngram_forward(A, 4, A, 1, None, None, t, None, 0, A, None, None, None, None) == EINVAL
+    assert L.ngram_forward(A, 4, A, 1, None, None, t, None, 0, A, None, A + 2, None, None) == EALIGN
+    assert L.ngram_forward(A, 4, A, 1, None, None, t, A + 2, 10, A, None, A, None, None) == EALIGN
+    assert L.ngram_forward(A, 4, A, 0, None, None, t, None, 0, A, None, A, None, None) == EINVAL
+    assert L.ngram_forward(A, 4, None, 1, None, None, t, None, 0, A, None, A, None, None) == EINVAL
+    assert L.ngram_forward(None, 0, None, 0, None, None, t, None, 0, A, None, None, None, None) == OK
+
+
+def test_gather_host_and_host_alloc_checks():
+    L = ng.lib()
+    dev_t = ctypes.byref(_table())
+    assert L.ngram_gather_host(dev_t, A, 4, A, None, A, None) == ENOTSUP
+    host_t = ctypes.byref(_table(loc=1))
+    assert L.ngram_gather_host(host_t, None, 4, A, None, A, None) == EINVAL
+    assert L.ngram_gather_host(host_t, A, 4, A + 8, None, A, None) == EALIGN
+    assert L.ngram_gather_host(host_t, A, 2**28, A, None, A, None) == ERANGE
+    h8 = ctypes.byref(_table(loc=1, dtype=1, scale=A))
+    assert L.ngram_gather_host(h8, A, 4, A, None, A, None) == EINVAL
+    assert L.ngram_gather_host(host_t, None, 0, None, None, None, None) == OK
+    p = ctypes.c_void_p()
+    assert L.ngram_host_alloc(0, ctypes.byref(p)) == EINVAL
+    assert L.ngram_host_alloc(16, None) == EINVAL
+    assert L.ngram_host_free(None) == OK
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(ng, "_lib", None)
+    monkeypatch.setattr(ng, "LIB_PATH", "/nonexistent/libngram.so")
+    with pytest.raises(ng.NgramError):
+        ng.lib()
+
+
+def test_product_package_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "hashed_gram_embedding_ngram_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.replace("oracle/", ""), f"{f} mentions the oracle"

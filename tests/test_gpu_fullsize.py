@@ -1,0 +1,109 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: every row id of the batch bit-exact against the oracle's
+hash, and the bf16 outputs of sampled tokens (sequence starts and ends plus
+random positions) bit-exact against the oracle run on those tokens' rows.
+
+Memory: the 20M x 2560 bf16 table is 95.4 GiB of HBM; each test frees its
+tensors before the next one allocates.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import hashed_gram_embedding_ngram_amd as ng  # noqa: E402
+import oracle  # noqa: E402
+from synth.workloads import CONFIGS, DeviceInputs, HostInputs, fill_host_table  # noqa: E402
+from tests.oracle_ref import expected, sample_tokens  # noqa: E402
+from tests.test_gpu_parity import assert_bf16_equal, bits16, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _free():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _check_forward(name):
+    sp = CONFIGS[name]
+    say(f"full size {name}: n={sp.n} R={sp.R} d={sp.d} table={sp.table}")
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    out = di.residual if di.residual is not None else torch.empty(sp.n * sp.d, dtype=torch.int16, device="cuda:0")
+    rows = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+    ng.ngram_forward(di.tokens, di.offsets, di.table_obj(), di.W_g, out, e1=di.e1,
+                     residual=di.residual, history=di.history, rows_out=rows)
+    torch.cuda.synchronize()
+    got_rows = rows.cpu().numpy()
+    want_rows = oracle.hash_rows(h.tokens, h.offsets, sp.R, h.history)
+    assert np.array_equal(got_rows, want_rows), "row ids differ"
+    idx = sample_tokens(sp, m=96) if sp.n > 64 else np.arange(sp.n)
+    _, _, want = expected(h, idx, rows_all=want_rows)
+    got = bits16(out.view(sp.n, sp.d)[torch.from_numpy(idx).to("cuda:0")])
+    assert_bf16_equal(got, want, name)
+    del di, out, rows
+    _free()
+
+
+def test_prefill_full_size():
+    _check_forward("prefill")
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode2", "decode4"])
+def test_decode_full_size(name):
+    _check_forward(name)
+
+
+def test_int8_full_size():
+    _check_forward("int8")
+
+
+def test_host_table_full_size():
+    """R = 5M x 2560 bf16 (23.8 GiB) in pinned host memory: the zero-copy sum
+    and the staged path both equal the oracle on sampled tokens, and the host
+    table gives bit-identical results to the same table resident in HBM."""
+    sp = CONFIGS["host"]
+    say(f"full size host: n={sp.n} R={sp.R} d={sp.d}")
+    h = HostInputs(sp)
+    hb = ng.HostBuffer(sp.R * sp.d * 2)
+    try:
+        fill_host_table(sp, hb.numpy(np.int16, (sp.R, sp.d)))
+        di = DeviceInputs(sp, h, table=False)
+        th = ng.Table(hb, sp.R, sp.d)
+        rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+        eN_host = ng.ngram_embed_bag(th, rows)
+        out = torch.empty(sp.n * sp.d, dtype=torch.int16, device="cuda:0")
+        ng.ngram_gate_add(eN_host, di.tokens, di.W_g, out, e1=di.e1, residual=di.residual)
+        torch.cuda.synchronize()
+        want_rows = oracle.hash_rows(h.tokens, h.offsets, sp.R)
+        assert np.array_equal(rows.cpu().numpy(), want_rows)
+        idx = sample_tokens(sp, m=64)
+        _, want_eN, want = expected(h, idx, rows_all=want_rows)
+        tidx = torch.from_numpy(idx).to("cuda:0")
+        assert np.array_equal(eN_host[tidx].cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+        assert_bf16_equal(bits16(out.view(sp.n, sp.d)[tidx]), want, "host")
+
+        say("host: staged gather")
+        stage = torch.empty((sp.n * 16, sp.d), dtype=torch.int16, device="cuda:0")
+        remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+        ng.ngram_gather_host(th, rows, stage, remap)
+        eN_stage = ng.ngram_embed_bag(ng.Table(stage, sp.n * 16, sp.d), remap)
+        torch.cuda.synchronize()
+        assert np.array_equal(remap.cpu().numpy(), np.arange(sp.n * 16, dtype=np.int32).reshape(sp.n, 16))
+        assert torch.equal(eN_stage.view(torch.int32), eN_host.view(torch.int32))
+        del stage, remap, eN_stage
+        _free()
+
+        say("host: same table in HBM")
+        dev_table = torch.from_numpy(hb.numpy(np.int16, (sp.R * sp.d,))).to("cuda:0")
+        eN_dev = ng.ngram_embed_bag(ng.Table(dev_table, sp.R, sp.d), rows)
+        torch.cuda.synchronize()
+        assert torch.equal(eN_dev.view(torch.int32), eN_host.view(torch.int32))
+        del dev_table, eN_dev, eN_host, out, rows, di
+        _free()
+    finally:
+        hb.free()

@@ -1,0 +1,256 @@
+"""GPU parity against the oracle at sizes the oracle finishes in seconds,
+through the C ABI (the Python binding only marshals pointers).
+
+Bar: row ids bit-exact, fp32 sums bit-exact, bf16 outputs bit-exact (the
+relative-error bound of 1e-3 is below one bf16 ulp, so only identical bits
+meet it; the observed maximum relative error is asserted too).
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import hashed_gram_embedding_ngram_amd as ng  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from synth.workloads import CONFIGS, DeviceInputs, HostInputs, Spec  # noqa: E402
+from tests.oracle_ref import expected  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+REL_TOL = 1e-3
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def bits16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def assert_bf16_equal(got, want, what):
+    got = np.asarray(got, dtype=np.uint16)
+    want = np.asarray(want, dtype=np.uint16)
+    g = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w = (want.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    finite = np.isfinite(w)
+    rel = np.abs(g[finite] - w[finite]) / np.maximum(np.abs(w[finite]), 2.0 ** -14)
+    ndiff = int((got != want).sum())
+    assert ndiff == 0, f"{what}: {ndiff} bf16 values differ, max rel err {rel.max():.3g}"
+    assert rel.size == 0 or rel.max() <= REL_TOL
+
+
+def run_forward(di: DeviceInputs, out_of_place=False, seeds=None):
+    sp = di.spec
+    if di.residual is not None and not out_of_place:
+        out = di.residual
+    else:
+        out = torch.empty(sp.n * sp.d, dtype=torch.int16, device=di.tokens.device)
+    rows = torch.empty((sp.n, 16), dtype=torch.int32, device=di.tokens.device)
+    ng.ngram_forward(di.tokens, di.offsets, di.table_obj(), di.W_g, out, e1=di.e1,
+                     residual=di.residual, history=di.history, rows_out=rows, seeds=seeds)
+    torch.cuda.synchronize()
+    return bits16(out).reshape(sp.n, sp.d), rows.cpu().numpy()
+
+
+def check_spec(sp: Spec, **kw):
+    say(f"{sp.name} n={sp.n} R={sp.R} d={sp.d} table={sp.table} e1={sp.e1} res={sp.residual} "
+        f"hist={sp.history} {kw}")
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    out, rows = run_forward(di, **kw)
+    want_rows, _, want_out = expected(h)
+    assert np.array_equal(rows, want_rows), "row ids differ"
+    assert_bf16_equal(out, want_out, sp.name)
+    return h, di
+
+
+RAGGED = Spec("ragged_wide", (1, 2, 3, 5, 0, 250, 33), 151936, 1_000_003, 2560,
+              table_kind=synth.KIND_BF16_WIDE, residual=True, config_id=11)
+
+
+def test_tiny_config_fused():
+    check_spec(CONFIGS["tiny"])
+
+
+def test_ragged_wide_in_place():
+    check_spec(RAGGED)
+
+
+def test_ragged_wide_out_of_place_keeps_residual():
+    h, di = check_spec(RAGGED.replace(batch=1), out_of_place=True)
+    assert np.array_equal(bits16(di.residual).reshape(h.spec.n, -1), h.full_residual())
+
+
+@pytest.mark.parametrize("d", [8, 64, 520, 1032, 2568, 4104])
+def test_row_widths(d):
+    check_spec(Spec(f"d{d}", (1, 40, 0, 2, 57), 5000, 5003, d,
+                    table_kind=synth.KIND_BF16_WIDE, residual=True, config_id=12))
+
+
+@pytest.mark.parametrize("e1,res", [(False, False), (True, False), (False, True), (True, True)])
+def test_optional_e1_and_residual(e1, res):
+    check_spec(Spec(f"opt{int(e1)}{int(res)}", (130,), 2048, 4096, 256,
+                    table_kind=synth.KIND_BF16_WIDE, e1=e1, residual=res, config_id=13))
+
+
+@pytest.mark.parametrize("tpw", ["1", "3", "64"])
+def test_tokens_per_workgroup(tpw, monkeypatch):
+    monkeypatch.setenv("NGRAM_TOKENS_PER_WG", tpw)
+    check_spec(Spec(f"tpw{tpw}", (300, 7), 151936, 100_003, 2560,
+                    table_kind=synth.KIND_BF16_WIDE, residual=True, config_id=14))
+
+
+def test_decode_with_history():
+    check_spec(Spec("decode_hist", (1, 1, 1, 1), 151936, 100_003, 2560, history=True,
+                    table_kind=synth.KIND_BF16_WIDE, config_id=15))
+
+
+def test_history_of_pads_equals_no_history():
+    sp = Spec("pads", (5, 9), 1024, 4096, 64, config_id=16)
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    out0, rows0 = run_forward(di)
+    di.history = torch.full((2, 2), ng.PAD_ID, dtype=torch.int32, device="cuda:0")
+    out1, rows1 = run_forward(di)
+    assert np.array_equal(rows0, rows1) and np.array_equal(out0, out1)
+
+
+def test_int8_ragged():
+    check_spec(Spec("int8_ragged", (3, 0, 200, 1), 151936, 1_000_003, 2560, zipf_s=1.2,
+                    table="int8", table_kind=synth.KIND_I8_NORMAL, residual=True, config_id=17))
+
+
+def test_int8_small_widths():
+    check_spec(Spec("int8_d72", (33, 1), 1000, 777, 72, table="int8",
+                    table_kind=synth.KIND_I8_NORMAL, residual=True, config_id=18))
+
+
+def test_custom_seeds():
+    sp = Spec("seeds", (77,), 1024, 4096, 64, table_kind=synth.KIND_BF16_WIDE, config_id=19)
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    seeds = [(k * 0x9E3779B97F4A7C15 + 12345) & 0xFFFFFFFFFFFFFFFF for k in range(16)]
+    say("custom seeds")
+    out, rows = run_forward(di, seeds=seeds)
+    want_out, want_rows, _ = oracle.forward(h.tokens, h.offsets, h.full_table(), h.W_g,
+                                            e1=h.full_e1(), seeds=np.array(seeds, dtype=np.uint64))
+    assert np.array_equal(rows, want_rows)
+    assert_bf16_equal(out, want_out, "custom seeds")
+
+
+def test_unfused_pipeline_equals_fused_and_oracle():
+    sp = RAGGED.replace(batch=2)
+    say("unfused pipeline")
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+    eN = ng.ngram_embed_bag(di.table_obj(), rows)
+    out = torch.empty(sp.n * sp.d, dtype=torch.int16, device="cuda:0")
+    ng.ngram_gate_add(eN, di.tokens, di.W_g, out, e1=di.e1, residual=di.residual)
+    torch.cuda.synchronize()
+    want_rows, want_eN, want_out = expected(h)
+    assert np.array_equal(rows.cpu().numpy(), want_rows)
+    assert np.array_equal(eN.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+    assert_bf16_equal(bits16(out).reshape(sp.n, -1), want_out, "unfused")
+    fused, _ = run_forward(di, out_of_place=True)
+    assert np.array_equal(fused, bits16(out).reshape(sp.n, -1))
+
+
+def test_unfused_int8_sum_bits():
+    sp = Spec("int8_bag", (64, 64), 151936, 1_000_003, 2560, zipf_s=1.2, table="int8",
+              table_kind=synth.KIND_I8_NORMAL, config_id=20)
+    say("int8 embed_bag")
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+    eN = ng.ngram_embed_bag(di.table_obj(), rows)
+    torch.cuda.synchronize()
+    _, want_eN, _ = expected(h)
+    assert np.array_equal(eN.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+
+
+def test_hash_extreme_R():
+    sp = Spec("hashR", (1, 2, 300), 151936, 4096, 64, config_id=21)
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h, table=False, e1=False)
+    for R in (1, 2, 3, 1 << 20, 2**31 - 1):
+        say(f"ngram_hash R={R}")
+        rows = ng.ngram_hash(di.tokens, di.offsets, R)
+        torch.cuda.synchronize()
+        assert np.array_equal(rows.cpu().numpy(), oracle.hash_rows(h.tokens, h.offsets, R))
+
+
+def test_table_with_one_row():
+    check_spec(Spec("R1", (20,), 64, 1, 64, table_kind=synth.KIND_BF16_WIDE, config_id=22))
+
+
+def test_vocab_boundary_tokens():
+    sp = Spec("vb", (6,), 1000, 4096, 64, config_id=23)
+    h = HostInputs(sp)
+    h.tokens = np.array([0, 999, 999, 0, 998, 1], dtype=np.int32)
+    di = DeviceInputs(sp, h)
+    say("vocab boundary tokens")
+    out, rows = run_forward(di)
+    want_out, want_rows, _ = oracle.forward(h.tokens, h.offsets, h.full_table(), h.W_g, e1=h.full_e1())
+    assert np.array_equal(rows, want_rows)
+    assert_bf16_equal(out, want_out, "vocab boundary")
+
+
+def test_invalid_ids_give_nan_and_leave_others_exact():
+    sp = Spec("bad", (8,), 1000, 4096, 64, residual=True, config_id=24)
+    h = HostInputs(sp)
+    good = h.tokens.copy()
+    bad = good.copy()
+    bad[3] = 1000            # == V: out of range
+    bad[6] = -5
+    di = DeviceInputs(sp, h)
+    di.tokens = torch.from_numpy(bad).to("cuda:0")
+    say("invalid token ids")
+    out, rows = run_forward(di, out_of_place=True)
+    assert np.all(out[3] == 0x7FC0) and np.all(out[6] == 0x7FC0)
+    assert np.all(rows[3] == -1) and np.all(rows[6] == -1)
+    # tokens whose context holds no invalid id are exact
+    want_out, want_rows, _ = oracle.forward(good, h.offsets, h.full_table(), h.W_g,
+                                            e1=h.full_e1(), residual=h.full_residual())
+    for i in (0, 1, 2):
+        assert np.array_equal(rows[i], want_rows[i]) and np.array_equal(out[i], want_out[i])
+    # embed_bag with out-of-range row ids: NaN sums for those tokens only
+    rr = torch.from_numpy(want_rows.copy()).to("cuda:0")
+    rr[2, 5] = sp.R
+    rr[4, 0] = -1
+    eN = ng.ngram_embed_bag(di.table_obj(), rr)
+    torch.cuda.synchronize()
+    e = eN.cpu().numpy()
+    assert np.all(np.isnan(e[2])) and np.all(np.isnan(e[4]))
+    assert np.array_equal(e[0].view(np.uint32), oracle.embed_bag_bf16(h.full_table(), want_rows[:1])[0].view(np.uint32))
+
+
+def test_empty_batch_launches_nothing():
+    sp = Spec("empty", (4,), 1000, 4096, 64, config_id=25)
+    di = DeviceInputs(sp)
+    z = torch.zeros(0, dtype=torch.int32, device="cuda:0")
+    out = torch.zeros(0, dtype=torch.int16, device="cuda:0")
+    say("n = 0")
+    ng.ngram_forward(z, torch.zeros(1, dtype=torch.int32, device="cuda:0"), di.table_obj(),
+                     di.W_g, out, e1=di.e1)
+    r = ng.ngram_hash(z, torch.zeros(1, dtype=torch.int32, device="cuda:0"), 4096)
+    assert r.shape == (0, 16)
+    e = ng.ngram_embed_bag(di.table_obj(), torch.zeros((0, 16), dtype=torch.int32, device="cuda:0"))
+    assert e.shape == (0, 64)
+    torch.cuda.synchronize()
+
+
+def test_default_seeds_match_oracle():
+    assert ng.default_seeds() == [int(s) for s in oracle.default_seeds()]
+
+
+def test_repeated_calls_are_deterministic():
+    sp = Spec("det", (512, 100), 151936, 100_003, 2560, table_kind=synth.KIND_BF16_WIDE, config_id=26)
+    di = DeviceInputs(sp)
+    say("determinism")
+    a, ra = run_forward(di)
+    b, rb = run_forward(di)
+    assert np.array_equal(a, b) and np.array_equal(ra, rb)
