@@ -101,6 +101,12 @@ def _dev(t, dtypes, name, allow_none=False):
         raise NgramError(f"{name} must be contiguous")
 
 
+def _need(t, count, name):
+    """Refuse a buffer smaller than the call reads or writes."""
+    if t is not None and t.numel() < count:
+        raise NgramError(f"{name} holds {t.numel()} elements, the call needs {count}")
+
+
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 _I32T = (torch.int32,)
 _F32 = (torch.float32,)
@@ -133,10 +139,14 @@ class Table:
             ptr = data.ptr
         else:
             _dev(data, _BF16 if dtype == TABLE_BF16 else (torch.int8,), "table")
+            _need(data, self.R * self.d, "table")
             self.location = IN_DEVICE
             ptr = data.data_ptr()
+        if isinstance(data, HostBuffer) and data.nbytes < self.R * self.d * (2 if dtype == TABLE_BF16 else 1):
+            raise NgramError("host table buffer is smaller than R * d elements")
         if dtype == TABLE_INT8_ROWSCALE:
             _dev(row_scale, _F32, "row_scale")
+            _need(row_scale, self.R, "row_scale")
         self._c = _Table(ptr, None if row_scale is None else row_scale.data_ptr(), self.R, self.d,
                          self.dtype, self.location, 0)
 
@@ -171,6 +181,15 @@ class HostBuffer:
             pass
 
 
+def _vocab(e1, d):
+    """Rows of the [V][d] e1 table (any shape with V*d elements)."""
+    if e1 is None:
+        return 0
+    if e1.numel() % d:
+        raise NgramError(f"e1 has {e1.numel()} elements, not a multiple of d={d}")
+    return e1.numel() // d
+
+
 def ngram_hash(tokens, seq_offsets, R, rows_out=None, history=None, seeds=None, stream=None):
     _dev(tokens, _I32T, "tokens")
     _dev(seq_offsets, _I32T, "seq_offsets")
@@ -179,6 +198,8 @@ def ngram_hash(tokens, seq_offsets, R, rows_out=None, history=None, seeds=None, 
     if rows_out is None:
         rows_out = torch.empty((n, K), dtype=torch.int32, device=tokens.device)
     _dev(rows_out, _I32T, "rows_out")
+    _need(rows_out, n * K, "rows_out")
+    _need(history, 2 * (seq_offsets.numel() - 1), "history")
     _check(lib().ngram_hash(_ptr(tokens), n, _ptr(seq_offsets), seq_offsets.numel() - 1,
                             _ptr(history), _seeds_arg(seeds), int(R), _ptr(rows_out), _stream(stream)),
            "ngram_hash")
@@ -191,6 +212,8 @@ def ngram_embed_bag(table: Table, rows, eN_out=None, stream=None):
     if eN_out is None:
         eN_out = torch.empty((n, table.d), dtype=torch.float32, device=rows.device)
     _dev(eN_out, _F32, "eN_out")
+    _need(rows, n * K, "rows")
+    _need(eN_out, n * table.d, "eN_out")
     _check(lib().ngram_embed_bag(table.c, _ptr(rows), n, _ptr(eN_out), _stream(stream)),
            "ngram_embed_bag")
     return eN_out
@@ -204,7 +227,11 @@ def ngram_gate_add(eN, tokens, W_g, out, e1=None, residual=None, stream=None):
     _dev(e1, _BF16, "e1", allow_none=True)
     _dev(residual, _BF16, "residual", allow_none=True)
     n, d = eN.shape
-    V = e1.shape[0] if e1 is not None else 0
+    V = _vocab(e1, d)
+    _need(tokens, n, "tokens")
+    _need(W_g, d, "W_g")
+    _need(out, n * d, "out")
+    _need(residual, n * d, "residual")
     _check(lib().ngram_gate_add(_ptr(eN), _ptr(tokens), n, d, _ptr(e1), V, _ptr(W_g),
                                 _ptr(residual), _ptr(out), _stream(stream)), "ngram_gate_add")
     return out
@@ -220,7 +247,13 @@ def ngram_forward(tokens, seq_offsets, table: Table, W_g, out, e1=None, residual
     _dev(e1, _BF16, "e1", allow_none=True)
     _dev(residual, _BF16, "residual", allow_none=True)
     _dev(rows_out, _I32T, "rows_out", allow_none=True)
-    V = e1.shape[0] if e1 is not None else 0
+    V = _vocab(e1, table.d)
+    n, d = tokens.numel(), table.d
+    _need(W_g, d, "W_g")
+    _need(out, n * d, "out")
+    _need(residual, n * d, "residual")
+    _need(rows_out, n * K, "rows_out")
+    _need(history, 2 * (seq_offsets.numel() - 1), "history")
     _check(lib().ngram_forward(_ptr(tokens), tokens.numel(), _ptr(seq_offsets), seq_offsets.numel() - 1,
                                _ptr(history), _seeds_arg(seeds), table.c, _ptr(e1), V, _ptr(W_g),
                                _ptr(residual), _ptr(out), _ptr(rows_out), _stream(stream)),
@@ -235,6 +268,13 @@ def ngram_gather_host(table: Table, rows, stage_out, remap_out, stage_scale_out=
     if not stage_out.is_cuda or not stage_out.is_contiguous():
         raise NgramError("stage_out must be a contiguous device tensor")
     n = rows.shape[0] if rows.dim() == 2 else rows.numel() // K
+    _need(rows, n * K, "rows")
+    _need(remap_out, n * K, "remap_out")
+    row_bytes = table.d * (2 if table.dtype == TABLE_BF16 else 1)
+    if stage_out.numel() * stage_out.element_size() < n * K * row_bytes:
+        raise NgramError("stage_out is smaller than n * 16 rows")
+    if table.dtype == TABLE_INT8_ROWSCALE:
+        _need(stage_scale_out, n * K, "stage_scale_out")
     _check(lib().ngram_gather_host(table.c, _ptr(rows), n, _ptr(stage_out), _ptr(stage_scale_out),
                                    _ptr(remap_out), _stream(stream)), "ngram_gather_host")
     return stage_out, remap_out
