@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1_000_000,
                     help="table rows of the host copy the CPU oracle reads")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy kernel (for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -165,6 +167,18 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        # A plain elementwise copy of known size: reads 1 GiB, writes 1 GiB per
+        # launch.  HBM counters of this kernel give the scale of the counters.
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            torch.mul(src, 3, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4,
+                          "calibrate_copy_bytes_written": dst.numel() * 4, "launches": args.steps}))
+        return
 
     import hashed_gram_embedding_ngram_amd as ng
     import synth
