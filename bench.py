@@ -86,10 +86,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "int8", "decode1", "decode2", "decode4"])
+                    choices=["prefill", "int8", "decode1", "decode2", "decode4", "host"])
+    ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged"],
+                    help="host workload: sum straight from pinned memory, or stage rows in HBM first")
     ap.add_argument("--dist", default="zipf", choices=["zipf", "uniform"],
                     help="token distribution (uniform: the no-reuse control)")
     ap.add_argument("--batches", type=int, default=4, help="distinct batches rotated over")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one launch per batch in a HIP graph and time graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1_000_000,
                     help="table rows of the host copy the CPU oracle reads")
@@ -184,6 +188,10 @@ def main():
     import synth
     from synth.workloads import CONFIGS, HostInputs
 
+    if args.workload == "host":
+        run_host(args)
+        return
+
     dev = torch.device("cuda:0")
     spec = CONFIGS[args.workload].replace(dist=args.dist)
     n, d = spec.n, spec.d
@@ -236,18 +244,40 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(args.warmup + i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    if args.graph:
+        # One graph holds one launch per batch; each replay runs nb steps.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nb):
+                tok, off, hist, res, out = batches[i]
+                ng.ngram_forward(tok, off, T, W_g, out, e1=e1, residual=res, history=hist)
+        reps = max(1, args.steps // nb)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s_ev.record()
+        for _ in range(reps):
+            g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        args.steps = reps * nb
+        mean_launch_s = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
+    else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step(args.warmup + i)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
 
     bpt = nominal_bytes_per_token(d, spec.table, spec.e1, spec.residual)
     bytes_per_launch = bpt * n + 4 * d
@@ -280,6 +310,7 @@ def main():
             "token_dist": f"zipf({spec.zipf_s})" if args.dist == "zipf" else "uniform",
             "residual_in_place": spec.residual,
             "rotating_batches": nb,
+            "hip_graph": bool(args.graph),
         },
         "roofline": {
             "bound": "hbm",
@@ -312,6 +343,135 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def run_host(args):
+    """The pinned-host-table workload: 8192 tokens, a 5,000,000 x 2560 bf16
+    table in pinned host memory.  Side stream: hash, then the 16 rows of each
+    token read by the GPU over PCIe and summed into an fp32 [n][2560] HBM
+    buffer (zero copy), or first staged into HBM and summed there.  Main
+    stream: a [32768 x 2560] @ [2560 x 2560] bf16 GEMM stand-in for the first
+    decoder block, repeated; it then waits on the side stream's event and
+    runs the gate and residual add.  Reports the gather's PCIe rate alone, the
+    GEMMs alone, both overlapped, and the exposed time (overlapped - GEMMs)."""
+    import numpy as np
+    import torch
+
+    import hashed_gram_embedding_ngram_amd as ng
+    import synth
+    from synth.workloads import CONFIGS, DeviceInputs, HostInputs, fill_host_table
+
+    dev = torch.device("cuda:0")
+    spec = CONFIGS["host"].replace(dist=args.dist)
+    n, d, R = spec.n, spec.d, spec.R
+    t0 = time.time()
+    hb = ng.HostBuffer(R * d * 2)
+    fill_host_table(spec, hb.numpy(np.int16, (R, d)))
+    T_host = ng.Table(hb, R, d)
+    h = HostInputs(spec)
+    di = DeviceInputs(spec, h, table=False)
+    eN = torch.empty((n, d), dtype=torch.float32, device=dev)
+    rows = torch.empty((n, 16), dtype=torch.int32, device=dev)
+    out = torch.empty(n * d, dtype=torch.int16, device=dev)
+    stage = remap = None
+    if args.host_mode == "staged":
+        stage = torch.empty((n * 16, d), dtype=torch.int16, device=dev)
+        remap = torch.empty((n, 16), dtype=torch.int32, device=dev)
+    A = torch.randn((32768, d), dtype=torch.bfloat16, device=dev)
+    B = torch.randn((d, d), dtype=torch.bfloat16, device=dev).contiguous()
+    C = torch.empty((32768, d), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream(device=dev)            # default priority
+    main = torch.cuda.current_stream()
+    setup_s = time.time() - t0
+
+    def gather(stream):
+        ng.ngram_hash(di.tokens, di.offsets, R, rows_out=rows, stream=stream)
+        if args.host_mode == "staged":
+            ng.ngram_gather_host(T_host, rows, stage, remap, stream=stream)
+            ng.ngram_embed_bag(ng.Table(stage, n * 16, d), remap, eN_out=eN, stream=stream)
+        else:
+            ng.ngram_embed_bag(T_host, rows, eN_out=eN, stream=stream)
+
+    def gemms(k):
+        for _ in range(k):
+            torch.matmul(A, B, out=C)
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps
+
+    # the gather alone (side stream), with events on that stream
+    gather(side)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s_, e_ in ev:
+        s_.record(side)
+        gather(side)
+        e_.record(side)
+    torch.cuda.synchronize()
+    gather_s = sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
+    # PCIe reference: one pinned H2D copy of 1 GiB
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    h2d_s = timed(lambda: dst.copy_(src, non_blocking=True), 3)
+    del src, dst
+    # GEMMs alone; enough of them to outlast the gather (after a warm-up call
+    # that absorbs the GEMM library's first-call setup)
+    gemms(3)
+    torch.cuda.synchronize()
+    gemm1 = timed(lambda: gemms(1), 5)
+    k = max(1, int(np.ceil(1.25 * gather_s / gemm1)))
+    gemm_s = timed(lambda: gemms(k), 3)
+
+    def overlapped():
+        side.wait_stream(main)
+        gather(side)
+        ev_done = torch.cuda.Event()
+        ev_done.record(side)
+        gemms(k)
+        main.wait_event(ev_done)
+        ng.ngram_gate_add(eN, di.tokens, di.W_g, out, e1=di.e1, residual=di.residual, stream=main)
+    both_s = timed(overlapped, 3)
+    gate_s = timed(lambda: ng.ngram_gate_add(eN, di.tokens, di.W_g, out, e1=di.e1,
+                                             residual=di.residual, stream=main), 5)
+
+    pcie_bytes = n * 16 * d * 2
+    achieved = pcie_bytes / gather_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": n / gather_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 1,
+        "ms_per_step": gather_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "host", "tokens": n, "R": R, "d": d, "K": K_ROWS, "table_dtype": "bf16",
+                   "table_location": "pinned host memory", "mode": args.host_mode,
+                   "token_dist": f"zipf({spec.zipf_s})" if args.dist == "zipf" else "uniform"},
+        "roofline": {"bound": "pcie", "achieved": achieved, "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / PCIE_PEAK_GBPS, "traffic": None,
+                     "kernel": "ngram_bag_kernel (host table)",
+                     "algorithmic_bytes_per_launch": pcie_bytes,
+                     "h2d_copy_GBps": (1 << 30) / h2d_s / 1e9},
+        "overlap": {"gemm_stand_in": "[32768 x 2560] @ [2560 x 2560] bf16", "gemm_count": k,
+                    "gemm_alone_ms": gemm_s * 1e3, "gather_alone_ms": gather_s * 1e3,
+                    "overlapped_ms": both_s * 1e3, "exposed_ms": (both_s - gemm_s) * 1e3,
+                    "gate_add_ms": gate_s * 1e3,
+                    "dma_estimate_ms": dma_time_estimate_us(K_ROWS, d, 2, PCIE_PEAK_GBPS) * n / 1e3},
+        "setup_s": setup_s,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    hb.free()
 
 
 if __name__ == "__main__":

@@ -14,8 +14,10 @@
 // of tokens.  Its threads first hash the tile's (token, k) pairs, one pair per
 // thread, into a row list in LDS.  Then each wavefront owns 512-column slices
 // of the rows: every lane loads 16 bytes (8 bf16, or 8 int8) of each of the
-// 16 rows, so one load instruction reads 1 KiB contiguous of one row and the
-// 16 loads of a slice are all in flight before the first add.  The row ids
+// 16 rows, so one load instruction reads 1 KiB contiguous of one row.  The
+// compiler keeps about ten of the 16 loads of a slice in flight before the
+// first add at 76 VGPRs (six wavefronts per SIMD); forcing all 16 ahead
+// (NGRAM_SCHED_BARRIER=1) costs 122 VGPRs and measured 2% slower.  The row ids
 // are wave-uniform (read from LDS, moved to scalar registers), so each row
 // address is a scalar base plus a per-lane offset.  The sum runs in fp32 in
 // k order, the gate is one fused multiply-add, the residual one add, and the
@@ -31,7 +33,21 @@
 
 #include "ngram.h"
 
+// Compile-time cache-policy and scheduling choices of the slice loads.
+#ifndef NGRAM_SCHED_BARRIER
+#define NGRAM_SCHED_BARRIER 0      // 1: force all 16 row loads before the first add
+#endif
+#ifndef NGRAM_NT_TABLE
+#define NGRAM_NT_TABLE 0           // nontemporal table-row loads
+#endif
+#ifndef NGRAM_NT_OUT
+#define NGRAM_NT_OUT 0             // nontemporal output stores
+#endif
+
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kK = NGRAM_K;
 constexpr uint32_t kPad = NGRAM_PAD_ID;
@@ -117,15 +133,37 @@ template <int DT> struct Row8;
 template <> struct Row8<NGRAM_TABLE_BF16> {
     using Raw = uint4;
     __device__ static Raw load(const void* base, int64_t off) {
-        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off);
+#if NGRAM_NT_TABLE
+        const u32x4 v = __builtin_nontemporal_load(p);
+#else
+        const u32x4 v = *p;
+#endif
+        return make_uint4(v.x, v.y, v.z, v.w);
     }
 };
 template <> struct Row8<NGRAM_TABLE_INT8_ROWSCALE> {
     using Raw = uint2;
     __device__ static Raw load(const void* base, int64_t off) {
-        return *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(base) + off);
+        const u32x2* p = reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(base) + off);
+#if NGRAM_NT_TABLE
+        const u32x2 v = __builtin_nontemporal_load(p);
+#else
+        const u32x2 v = *p;
+#endif
+        return make_uint2(v.x, v.y);
     }
 };
+
+__device__ inline void store_out(uint16_t* o, const uint4& v) {
+    u32x4 w;
+    w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+#if NGRAM_NT_OUT
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o));
+#else
+    *reinterpret_cast<u32x4*>(o) = w;
+#endif
+}
 
 __device__ inline void add_row(float acc[8], const uint4& v) {
     acc[0] = acc[0] + bf16lo(v.x); acc[1] = acc[1] + bf16hi(v.x);
@@ -159,9 +197,11 @@ __device__ inline void gather_sum(float acc[8], const void* __restrict__ tab,
     Raw v[kK];
 #pragma unroll
     for (int k = 0; k < kK; ++k) v[k] = Row8<DT>::load(tab, static_cast<int64_t>(r[k]) * d + j0);
+#if NGRAM_SCHED_BARRIER
     // Keep the scheduler from sinking loads below the adds: all 16 row
     // loads of the slice are in flight before the first one is consumed.
     __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     if constexpr (DT == NGRAM_TABLE_BF16) {
@@ -287,7 +327,7 @@ __global__ void __launch_bounds__(1024) ngram_fwd_kernel(const FwdArgs a) {
             gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
             const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
             const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
-            *reinterpret_cast<uint4*>(o) = gate8<E1, RES>(acc, w, e1row, resrow);
+            store_out(o, gate8<E1, RES>(acc, w, e1row, resrow));
         }
     }
 }
@@ -516,12 +556,17 @@ struct Shape {
     int tpw;
 };
 
-Shape slice_shape(int64_t n, int32_t d) {
+// Tokens per workgroup: 1 for bf16 rows; 4 for int8 rows, whose half-size
+// slices leave the per-workgroup hash phase and barrier a larger share of the
+// time (measured on MI355X at 2560 columns: int8 5.3 TB/s at 1 token per
+// workgroup, 6.6 TB/s at 4; bf16 best at 1).
+Shape slice_shape(int64_t n, int32_t d, int32_t dtype) {
+    (void)n;
     const int nslices = (d + kSlice - 1) / kSlice;
     Shape s;
     s.waves = nslices < 16 ? nslices : 16;
     int tpw = env_int("NGRAM_TOKENS_PER_WG", 0);
-    if (tpw <= 0) tpw = n >= 4096 ? 4 : 1;
+    if (tpw <= 0) tpw = dtype == NGRAM_TABLE_INT8_ROWSCALE ? 4 : 1;
     if (tpw > 64) tpw = 64;
     s.tpw = tpw;
     return s;
@@ -605,7 +650,7 @@ int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float*
     BagArgs a;
     a.tab = tab; a.scale = T->row_scale; a.rows = rows; a.eN = eN_out;
     a.n = n; a.R = T->R; a.d = T->d;
-    const Shape sh = slice_shape(n, T->d);
+    const Shape sh = slice_shape(n, T->d, T->dtype);
     a.tpw = sh.tpw;
     const dim3 grid(static_cast<unsigned>((n + sh.tpw - 1) / sh.tpw)), block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
@@ -668,7 +713,7 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
     a.n = n; a.R = static_cast<uint64_t>(T->R); a.S = S; a.d = T->d;
     a.c0_limit = c0_limit_for(e1, V);
     a.sd = make_seeds(seeds);
-    const Shape sh = slice_shape(n, T->d);
+    const Shape sh = slice_shape(n, T->d, T->dtype);
     a.tpw = sh.tpw;
     if (T->dtype == NGRAM_TABLE_BF16) launch_fwd_dt<NGRAM_TABLE_BF16>(a, sh, stream);
     else launch_fwd_dt<NGRAM_TABLE_INT8_ROWSCALE>(a, sh, stream);
