@@ -281,54 +281,59 @@ __global__ void __launch_bounds__(1024) ngram_fwd_kernel(const FwdArgs a) {
     extern __shared__ int32_t lds[];
     int32_t* lrows = lds;                 // [tpw][16] row ids (-1: invalid token)
     int32_t* ltok = lds + a.tpw * kK;     // [tpw] w_t (-1: invalid token)
-    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * a.tpw;
-
-    for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
-        const int tl = t >> 4, k = t & (kK - 1);
-        const int64_t i = tile0 + tl;
-        int32_t row = -1, c0 = -1;
-        if (i < a.n) {
-            const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
-            if (c.ok) {
-                row = hashed_row(c, k, a.sd, a.R);
-                c0 = static_cast<int32_t>(c.c0);
-            }
-            if (a.rows_out) a.rows_out[i * kK + k] = row;
-        }
-        lrows[t] = row;
-        if (k == 0) ltok[tl] = c0;
-    }
-    __syncthreads();
-
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const int nslices = (a.d + kSlice - 1) / kSlice;
-    const int64_t rem = a.n - tile0;
-    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
-    for (int sl = wave; sl < nslices; sl += nwaves) {
-        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
-        if (j0 >= d) continue;
-        float w[8];
-        load_w8(w, a.wg, j0);
-        for (int tl = 0; tl < tile_n; ++tl) {
+    const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
+
+    // One tile per workgroup, or several when the grid is capped (host tables).
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t tile0 = tile * a.tpw;
+        for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
+            const int tl = t >> 4, k = t & (kK - 1);
             const int64_t i = tile0 + tl;
-            uint16_t* o = a.out + i * d + j0;
-            const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
-            if (c0 < 0) {
-                const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
-                *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
-                continue;
+            int32_t row = -1, c0 = -1;
+            if (i < a.n) {
+                const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
+                if (c.ok) {
+                    row = hashed_row(c, k, a.sd, a.R);
+                    c0 = static_cast<int32_t>(c.c0);
+                }
+                if (a.rows_out) a.rows_out[i * kK + k] = row;
             }
-            int32_t r[kK];
-#pragma unroll
-            for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
-            float acc[8];
-            gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
-            const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
-            const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
-            store_out(o, gate8<E1, RES>(acc, w, e1row, resrow));
+            lrows[t] = row;
+            if (k == 0) ltok[tl] = c0;
         }
+        __syncthreads();
+
+        const int64_t rem = a.n - tile0;
+        const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+        for (int sl = wave; sl < nslices; sl += nwaves) {
+            const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+            if (j0 >= d) continue;
+            float w[8];
+            load_w8(w, a.wg, j0);
+            for (int tl = 0; tl < tile_n; ++tl) {
+                const int64_t i = tile0 + tl;
+                uint16_t* o = a.out + i * d + j0;
+                const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
+                if (c0 < 0) {
+                    const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
+                    *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
+                    continue;
+                }
+                int32_t r[kK];
+#pragma unroll
+                for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
+                float acc[8];
+                gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+                const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
+                const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
+                store_out(o, gate8<E1, RES>(acc, w, e1row, resrow));
+            }
+        }
+        __syncthreads();                  // the next tile rewrites the LDS lists
     }
 }
 
@@ -369,45 +374,49 @@ struct BagArgs {
 template <int DT>
 __global__ void __launch_bounds__(1024) ngram_bag_kernel(const BagArgs a) {
     extern __shared__ int32_t lds[];
-    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * a.tpw;
-    for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
-        const int64_t i = tile0 + (t >> 4);
-        int32_t r = -1;
-        if (i < a.n) {
-            r = a.rows[i * kK + (t & (kK - 1))];
-            if (r < 0 || r >= a.R) r = -1;
-        }
-        lds[t] = r;
-    }
-    __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const int nslices = (a.d + kSlice - 1) / kSlice;
-    const int64_t rem = a.n - tile0;
-    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
-    for (int sl = wave; sl < nslices; sl += nwaves) {
-        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
-        if (j0 >= d) continue;
-        for (int tl = 0; tl < tile_n; ++tl) {
-            float* o = a.eN + (tile0 + tl) * d + j0;
-            int32_t r[kK];
-            bool ok = true;
-#pragma unroll
-            for (int k = 0; k < kK; ++k) {
-                r[k] = __builtin_amdgcn_readfirstlane(lds[tl * kK + k]);
-                ok = ok && r[k] >= 0;
+    const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t tile0 = tile * a.tpw;
+        for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
+            const int64_t i = tile0 + (t >> 4);
+            int32_t r = -1;
+            if (i < a.n) {
+                r = a.rows[i * kK + (t & (kK - 1))];
+                if (r < 0 || r >= a.R) r = -1;
             }
-            float acc[8];
-            if (ok) {
-                gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
-            }
-            reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+            lds[t] = r;
         }
+        __syncthreads();
+        const int64_t rem = a.n - tile0;
+        const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+        for (int sl = wave; sl < nslices; sl += nwaves) {
+            const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+            if (j0 >= d) continue;
+            for (int tl = 0; tl < tile_n; ++tl) {
+                float* o = a.eN + (tile0 + tl) * d + j0;
+                int32_t r[kK];
+                bool ok = true;
+#pragma unroll
+                for (int k = 0; k < kK; ++k) {
+                    r[k] = __builtin_amdgcn_readfirstlane(lds[tl * kK + k]);
+                    ok = ok && r[k] >= 0;
+                }
+                float acc[8];
+                if (ok) {
+                    gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
+                }
+                reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -448,8 +457,9 @@ __global__ void __launch_bounds__(256) ngram_gate_kernel(const GateArgs a) {
     *reinterpret_cast<uint4*>(o) = gate8<E1, RES>(acc, w, e1row, resrow);
 }
 
-// Zero-copy staging of host-table rows: one wavefront per (token, k) row
-// and 16-byte (bf16) or 8-byte (int8) lanes; stage row t = i*16 + k.
+// Zero-copy staging of host-table rows: one wavefront per (token, k) row,
+// 16-byte lanes (8-byte when the row is not a multiple of 16 bytes), a whole
+// row's loads issued before its stores; stage row t = i*16 + k.
 struct StageArgs {
     const void* tab;
     const float* scale;
@@ -463,21 +473,36 @@ struct StageArgs {
 };
 
 template <typename U>
-__global__ void __launch_bounds__(256) ngram_stage_kernel(const StageArgs a) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (t >= a.nrows) return;
+__global__ void __launch_bounds__(1024) ngram_stage_kernel(const StageArgs a) {
+    constexpr int kUnroll = 8;            // up to 8 x 64 lanes x 16 B of a row in flight
     const int lane = threadIdx.x & 63;
-    const int32_t r = a.rows[t];
-    const bool ok = r >= 0 && r < a.R;
-    if (lane == 0) {
-        a.remap[t] = ok ? static_cast<int32_t>(t) : -1;
-        if (ok && a.stage_scale) a.stage_scale[t] = a.scale[r];
-    }
-    if (!ok) return;
-    const U* src = reinterpret_cast<const U*>(static_cast<const char*>(a.tab) + static_cast<int64_t>(r) * a.row_bytes);
-    U* dst = reinterpret_cast<U*>(static_cast<char*>(a.stage) + t * a.row_bytes);
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
     const int64_t nu = a.row_bytes / static_cast<int64_t>(sizeof(U));
-    for (int64_t q = lane; q < nu; q += 64) dst[q] = src[q];
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); t < a.nrows;
+         t += waves) {
+        const int32_t r = a.rows[t];
+        const bool ok = r >= 0 && r < a.R;
+        if (lane == 0) {
+            a.remap[t] = ok ? static_cast<int32_t>(t) : -1;
+            if (ok && a.stage_scale) a.stage_scale[t] = a.scale[r];
+        }
+        if (!ok) continue;
+        const U* src = reinterpret_cast<const U*>(static_cast<const char*>(a.tab) + static_cast<int64_t>(r) * a.row_bytes);
+        U* dst = reinterpret_cast<U*>(static_cast<char*>(a.stage) + t * a.row_bytes);
+        for (int64_t q0 = 0; q0 < nu; q0 += 64 * kUnroll) {
+            U buf[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t q = q0 + u * 64 + lane;
+                if (q < nu) buf[u] = src[q];
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t q = q0 + u * 64 + lane;
+                if (q < nu) dst[q] = buf[u];
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -554,6 +579,7 @@ uint32_t c0_limit_for(const uint16_t* e1, int64_t V) {
 struct Shape {
     int waves;
     int tpw;
+    int64_t grid;
 };
 
 // Tokens per workgroup: 1 for bf16 rows; 4 for int8 rows, whose half-size
@@ -569,12 +595,28 @@ Shape slice_shape(int64_t n, int32_t d, int32_t dtype) {
     if (tpw <= 0) tpw = dtype == NGRAM_TABLE_INT8_ROWSCALE ? 4 : 1;
     if (tpw > 64) tpw = 64;
     s.tpw = tpw;
+    s.grid = (n + tpw - 1) / tpw;
     return s;
+}
+
+// A table in pinned host memory is read over PCIe, which a few workgroups
+// saturate; a capped, persistent grid leaves the other compute units to the
+// work it overlaps with on other streams.  Measured on MI355X (8192 tokens,
+// 5M x 2560 bf16 host table, against a bf16 GEMM loop on another stream):
+// 8 workgroups read at 58 GB/s and leave 4.3 ms of an 11.6 ms gather
+// exposed; 64 leave 9.5 ms, 256 leave 12.5 ms.
+int host_workgroups() {
+    const int v = env_int("NGRAM_HOST_WORKGROUPS", 0);
+    return v > 0 ? v : 8;
+}
+
+void cap_for_host(Shape& sh, const ngram_table* T) {
+    if (T->location == NGRAM_IN_HOST && sh.grid > host_workgroups()) sh.grid = host_workgroups();
 }
 
 template <int DT, bool E1, bool RES>
 void launch_fwd(const FwdArgs& a, const Shape& sh, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>((a.n + sh.tpw - 1) / sh.tpw));
+    const dim3 grid(static_cast<unsigned>(sh.grid));
     const dim3 block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * (kK + 1) * sizeof(int32_t);
     hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES>), grid, block, lds, st, a);
@@ -650,9 +692,10 @@ int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float*
     BagArgs a;
     a.tab = tab; a.scale = T->row_scale; a.rows = rows; a.eN = eN_out;
     a.n = n; a.R = T->R; a.d = T->d;
-    const Shape sh = slice_shape(n, T->d, T->dtype);
+    Shape sh = slice_shape(n, T->d, T->dtype);
+    cap_for_host(sh, T);
     a.tpw = sh.tpw;
-    const dim3 grid(static_cast<unsigned>((n + sh.tpw - 1) / sh.tpw)), block(64 * sh.waves);
+    const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
     if (T->dtype == NGRAM_TABLE_BF16)
         hipLaunchKernelGGL(ngram_bag_kernel<NGRAM_TABLE_BF16>, grid, block, lds, stream, a);
@@ -713,7 +756,8 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
     a.n = n; a.R = static_cast<uint64_t>(T->R); a.S = S; a.d = T->d;
     a.c0_limit = c0_limit_for(e1, V);
     a.sd = make_seeds(seeds);
-    const Shape sh = slice_shape(n, T->d, T->dtype);
+    Shape sh = slice_shape(n, T->d, T->dtype);
+    cap_for_host(sh, T);
     a.tpw = sh.tpw;
     if (T->dtype == NGRAM_TABLE_BF16) launch_fwd_dt<NGRAM_TABLE_BF16>(a, sh, stream);
     else launch_fwd_dt<NGRAM_TABLE_INT8_ROWSCALE>(a, sh, stream);
@@ -768,9 +812,11 @@ int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
     a.stage_scale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? stage_scale_out : nullptr;
     a.remap = remap_out; a.nrows = n * kK; a.R = T_host->R;
     a.row_bytes = static_cast<int64_t>(T_host->d) * (T_host->dtype == NGRAM_TABLE_BF16 ? 2 : 1);
-    const dim3 grid(static_cast<unsigned>((a.nrows + 3) / 4)), block(256);
-    if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(ngram_stage_kernel<uint4>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(ngram_stage_kernel<uint2>, grid, block, 0, stream, a);
+    int64_t blocks = (a.nrows + 15) / 16;
+    if (blocks > host_workgroups()) blocks = host_workgroups();
+    const dim3 grid(static_cast<unsigned>(blocks)), block(1024);
+    if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x4>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(ngram_stage_kernel<u32x2>, grid, block, 0, stream, a);
     return hip_status("ngram_gather_host launch");
 }
 

@@ -254,3 +254,49 @@ def test_repeated_calls_are_deterministic():
     a, ra = run_forward(di)
     b, rb = run_forward(di)
     assert np.array_equal(a, b) and np.array_equal(ra, rb)
+
+
+@pytest.mark.parametrize("wgs,tpw,table", [("3", "1", "bf16"), ("5", "3", "bf16"), ("64", "4", "bf16"),
+                                           ("7", "2", "int8")])
+def test_host_table_paths(wgs, tpw, table, monkeypatch):
+    """Pinned-host table with a capped, persistent grid (several ragged tiles
+    per workgroup): fused forward, zero-copy sum and staged gather all equal
+    the oracle."""
+    from synth.workloads import fill_host_table
+    monkeypatch.setenv("NGRAM_HOST_WORKGROUPS", wgs)
+    monkeypatch.setenv("NGRAM_TOKENS_PER_WG", tpw)
+    kw = dict(table="int8", table_kind=synth.KIND_I8_NORMAL) if table == "int8" else \
+        dict(table_kind=synth.KIND_BF16_WIDE)
+    sp = Spec(f"host_{table}_{wgs}_{tpw}", (1, 40, 0, 300, 2), 151936, 20_011, 2560, residual=True,
+              config_id=27, **kw)
+    say(sp.name)
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h, table=False)
+    esize = 2 if table == "bf16" else 1
+    hb = ng.HostBuffer(sp.R * sp.d * esize)
+    try:
+        fill_host_table(sp, hb.numpy(np.int16 if table == "bf16" else np.int8, (sp.R, sp.d)))
+        scale = None
+        if table == "int8":
+            scale = synth.fill_gpu(synth.KIND_F32_SCALE, sp.seed, synth.TAG_SCALE,
+                                   torch.empty(sp.R, dtype=torch.float32, device="cuda:0"))
+        T = ng.Table(hb, sp.R, sp.d, ng.TABLE_INT8_ROWSCALE if table == "int8" else ng.TABLE_BF16,
+                     row_scale=scale)
+        want_rows, want_eN, want_out = expected(h)
+        out = torch.empty(sp.n * sp.d, dtype=torch.int16, device="cuda:0")
+        rows = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+        ng.ngram_forward(di.tokens, di.offsets, T, di.W_g, out, e1=di.e1, residual=di.residual, rows_out=rows)
+        eN = ng.ngram_embed_bag(T, rows)
+        stage = torch.empty(sp.n * 16 * sp.d * esize, dtype=torch.int8, device="cuda:0")
+        remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+        sscale = torch.empty(sp.n * 16, dtype=torch.float32, device="cuda:0") if table == "int8" else None
+        ng.ngram_gather_host(T, rows, stage, remap, stage_scale_out=sscale)
+        st = stage.view(torch.int16) if table == "bf16" else stage
+        eN2 = ng.ngram_embed_bag(ng.Table(st, sp.n * 16, sp.d, T.dtype, row_scale=sscale), remap)
+        torch.cuda.synchronize()
+        assert np.array_equal(rows.cpu().numpy(), want_rows)
+        assert_bf16_equal(bits16(out).reshape(sp.n, -1), want_out, sp.name)
+        assert np.array_equal(eN.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+        assert np.array_equal(eN2.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+    finally:
+        hb.free()
