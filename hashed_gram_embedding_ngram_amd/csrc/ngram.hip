@@ -92,6 +92,11 @@ struct Ctx {
 __device__ inline Ctx token_context(const int32_t* __restrict__ tok, int64_t i,
                                     const int32_t* __restrict__ so, int S,
                                     const int32_t* __restrict__ hist, uint32_t c0_limit) {
+    // The three token loads do not depend on the sequence, so they are issued
+    // before the search and overlap its loads.
+    const uint32_t t0 = static_cast<uint32_t>(tok[i]);
+    const uint32_t t1 = i >= 1 ? static_cast<uint32_t>(tok[i - 1]) : kPad;
+    const uint32_t t2 = i >= 2 ? static_cast<uint32_t>(tok[i - 2]) : kPad;
     int lo = 0, hi = S - 1;     // the last sequence s with so[s] <= i
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -101,9 +106,9 @@ __device__ inline Ctx token_context(const int32_t* __restrict__ tok, int64_t i,
     const uint32_t h0 = hist ? static_cast<uint32_t>(hist[2 * lo]) : kPad;
     const uint32_t h1 = hist ? static_cast<uint32_t>(hist[2 * lo + 1]) : kPad;
     Ctx c;
-    c.c0 = static_cast<uint32_t>(tok[i]);
-    c.c1 = (p >= 1 && i >= 1) ? static_cast<uint32_t>(tok[i - 1]) : h1;
-    c.c2 = (p >= 2 && i >= 2) ? static_cast<uint32_t>(tok[i - 2]) : (p == 1 ? h1 : h0);
+    c.c0 = t0;
+    c.c1 = p >= 1 ? t1 : h1;
+    c.c2 = p >= 2 ? t2 : (p == 1 ? h1 : h0);
     c.ok = c.c0 < c0_limit && c.c1 <= kPad && c.c2 <= kPad;
     return c;
 }
@@ -276,64 +281,74 @@ struct FwdArgs {
     Seeds sd;
 };
 
+// One tile: hash its tokens' rows into LDS, then each wavefront gathers,
+// sums, gates and stores its slices of every token of the tile.
 template <int DT, bool E1, bool RES>
-__global__ void __launch_bounds__(1024) ngram_fwd_kernel(const FwdArgs a) {
-    extern __shared__ int32_t lds[];
-    int32_t* lrows = lds;                 // [tpw][16] row ids (-1: invalid token)
-    int32_t* ltok = lds + a.tpw * kK;     // [tpw] w_t (-1: invalid token)
+__device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const int nslices = (a.d + kSlice - 1) / kSlice;
-    const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
+    for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
+        const int tl = t >> 4, k = t & (kK - 1);
+        const int64_t i = tile0 + tl;
+        int32_t row = -1, c0 = -1;
+        if (i < a.n) {
+            const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
+            if (c.ok) {
+                row = hashed_row(c, k, a.sd, a.R);
+                c0 = static_cast<int32_t>(c.c0);
+            }
+            if (a.rows_out) a.rows_out[i * kK + k] = row;
+        }
+        lrows[t] = row;
+        if (k == 0) ltok[tl] = c0;
+    }
+    __syncthreads();
 
-    // One tile per workgroup, or several when the grid is capped (host tables).
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t tile0 = tile * a.tpw;
-        for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
-            const int tl = t >> 4, k = t & (kK - 1);
+    const int64_t rem = a.n - tile0;
+    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+    for (int sl = wave; sl < nslices; sl += nwaves) {
+        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+        if (j0 >= d) continue;
+        float w[8];
+        load_w8(w, a.wg, j0);
+        for (int tl = 0; tl < tile_n; ++tl) {
             const int64_t i = tile0 + tl;
-            int32_t row = -1, c0 = -1;
-            if (i < a.n) {
-                const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
-                if (c.ok) {
-                    row = hashed_row(c, k, a.sd, a.R);
-                    c0 = static_cast<int32_t>(c.c0);
-                }
-                if (a.rows_out) a.rows_out[i * kK + k] = row;
+            uint16_t* o = a.out + i * d + j0;
+            const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
+            if (c0 < 0) {
+                const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
+                *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
+                continue;
             }
-            lrows[t] = row;
-            if (k == 0) ltok[tl] = c0;
-        }
-        __syncthreads();
-
-        const int64_t rem = a.n - tile0;
-        const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
-        for (int sl = wave; sl < nslices; sl += nwaves) {
-            const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
-            if (j0 >= d) continue;
-            float w[8];
-            load_w8(w, a.wg, j0);
-            for (int tl = 0; tl < tile_n; ++tl) {
-                const int64_t i = tile0 + tl;
-                uint16_t* o = a.out + i * d + j0;
-                const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
-                if (c0 < 0) {
-                    const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
-                    *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
-                    continue;
-                }
-                int32_t r[kK];
+            int32_t r[kK];
 #pragma unroll
-                for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
-                float acc[8];
-                gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
-                const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
-                const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
-                store_out(o, gate8<E1, RES>(acc, w, e1row, resrow));
-            }
+            for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
+            float acc[8];
+            gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+            const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
+            const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
+            store_out(o, gate8<E1, RES>(acc, w, e1row, resrow));
         }
-        __syncthreads();                  // the next tile rewrites the LDS lists
+    }
+}
+
+// PERSIST = false: one tile per workgroup (tables in HBM).  PERSIST = true:
+// a capped grid loops over the tiles (tables in host memory, read over PCIe).
+template <int DT, bool E1, bool RES, bool PERSIST>
+__global__ void __launch_bounds__(1024) ngram_fwd_kernel(const FwdArgs a) {
+    extern __shared__ int32_t lds[];
+    int32_t* lrows = lds;                 // [tpw][16] row ids (-1: invalid token)
+    int32_t* ltok = lds + a.tpw * kK;     // [tpw] w_t (-1: invalid token)
+    if constexpr (!PERSIST) {
+        fwd_tile<DT, E1, RES>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lrows, ltok);
+    } else {
+        const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+            fwd_tile<DT, E1, RES>(a, tile * a.tpw, lrows, ltok);
+            __syncthreads();              // the next tile rewrites the LDS lists
+        }
     }
 }
 
@@ -372,51 +387,59 @@ struct BagArgs {
 };
 
 template <int DT>
-__global__ void __launch_bounds__(1024) ngram_bag_kernel(const BagArgs a) {
-    extern __shared__ int32_t lds[];
+__device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const int nslices = (a.d + kSlice - 1) / kSlice;
-    const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t tile0 = tile * a.tpw;
-        for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
-            const int64_t i = tile0 + (t >> 4);
-            int32_t r = -1;
-            if (i < a.n) {
-                r = a.rows[i * kK + (t & (kK - 1))];
-                if (r < 0 || r >= a.R) r = -1;
-            }
-            lds[t] = r;
+    for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
+        const int64_t i = tile0 + (t >> 4);
+        int32_t r = -1;
+        if (i < a.n) {
+            r = a.rows[i * kK + (t & (kK - 1))];
+            if (r < 0 || r >= a.R) r = -1;
         }
-        __syncthreads();
-        const int64_t rem = a.n - tile0;
-        const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
-        for (int sl = wave; sl < nslices; sl += nwaves) {
-            const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
-            if (j0 >= d) continue;
-            for (int tl = 0; tl < tile_n; ++tl) {
-                float* o = a.eN + (tile0 + tl) * d + j0;
-                int32_t r[kK];
-                bool ok = true;
+        lds[t] = r;
+    }
+    __syncthreads();
+    const int64_t rem = a.n - tile0;
+    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+    for (int sl = wave; sl < nslices; sl += nwaves) {
+        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+        if (j0 >= d) continue;
+        for (int tl = 0; tl < tile_n; ++tl) {
+            float* o = a.eN + (tile0 + tl) * d + j0;
+            int32_t r[kK];
+            bool ok = true;
 #pragma unroll
-                for (int k = 0; k < kK; ++k) {
-                    r[k] = __builtin_amdgcn_readfirstlane(lds[tl * kK + k]);
-                    ok = ok && r[k] >= 0;
-                }
-                float acc[8];
-                if (ok) {
-                    gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
-                }
-                reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+            for (int k = 0; k < kK; ++k) {
+                r[k] = __builtin_amdgcn_readfirstlane(lds[tl * kK + k]);
+                ok = ok && r[k] >= 0;
             }
+            float acc[8];
+            if (ok) {
+                gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
+            }
+            reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
-        __syncthreads();
+    }
+}
+
+template <int DT, bool PERSIST>
+__global__ void __launch_bounds__(1024) ngram_bag_kernel(const BagArgs a) {
+    extern __shared__ int32_t lds[];
+    if constexpr (!PERSIST) {
+        bag_tile<DT>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lds);
+    } else {
+        const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+            bag_tile<DT>(a, tile * a.tpw, lds);
+            __syncthreads();
+        }
     }
 }
 
@@ -580,6 +603,7 @@ struct Shape {
     int waves;
     int tpw;
     int64_t grid;
+    bool persist;
 };
 
 // Tokens per workgroup: 1 for bf16 rows; 4 for int8 rows, whose half-size
@@ -596,6 +620,7 @@ Shape slice_shape(int64_t n, int32_t d, int32_t dtype) {
     if (tpw > 64) tpw = 64;
     s.tpw = tpw;
     s.grid = (n + tpw - 1) / tpw;
+    s.persist = false;
     return s;
 }
 
@@ -611,7 +636,10 @@ int host_workgroups() {
 }
 
 void cap_for_host(Shape& sh, const ngram_table* T) {
-    if (T->location == NGRAM_IN_HOST && sh.grid > host_workgroups()) sh.grid = host_workgroups();
+    if (T->location == NGRAM_IN_HOST && sh.grid > host_workgroups()) {
+        sh.grid = host_workgroups();
+        sh.persist = true;
+    }
 }
 
 template <int DT, bool E1, bool RES>
@@ -619,7 +647,8 @@ void launch_fwd(const FwdArgs& a, const Shape& sh, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(sh.grid));
     const dim3 block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * (kK + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES>), grid, block, lds, st, a);
+    if (sh.persist) hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, true>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, false>), grid, block, lds, st, a);
 }
 
 template <int DT>
@@ -697,10 +726,13 @@ int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float*
     a.tpw = sh.tpw;
     const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
-    if (T->dtype == NGRAM_TABLE_BF16)
-        hipLaunchKernelGGL(ngram_bag_kernel<NGRAM_TABLE_BF16>, grid, block, lds, stream, a);
-    else
-        hipLaunchKernelGGL(ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE>, grid, block, lds, stream, a);
+    if (T->dtype == NGRAM_TABLE_BF16) {
+        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, false>), grid, block, lds, stream, a);
+    } else {
+        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, false>), grid, block, lds, stream, a);
+    }
     return hip_status("ngram_embed_bag launch");
 }
 
