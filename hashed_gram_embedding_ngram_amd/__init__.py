@@ -35,6 +35,11 @@ class _Table(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class _Pool(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("row_scale", ctypes.c_void_p), ("slot_of_row", ctypes.c_void_p),
+                ("pool_rows", ctypes.c_int64), ("cached", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -51,6 +56,13 @@ _SIGNATURES = {
     "ngram_host_alloc": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
     "ngram_host_free": (ctypes.c_int, [_P]),
     "ngram_gather_host": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, _P, _P, _P]),
+    "ngram_pool_workspace_bytes": (ctypes.c_int64, [_I64]),
+    "ngram_pool_reset": (ctypes.c_int, [ctypes.POINTER(_Table), ctypes.POINTER(_Pool), _P]),
+    "ngram_pool_cache_rows": (ctypes.c_int, [ctypes.POINTER(_Table), ctypes.POINTER(_Pool), _P, _I64, _P]),
+    "ngram_pool_gather": (ctypes.c_int, [ctypes.POINTER(_Table), ctypes.POINTER(_Pool), _P, _I64, _P, _P, _P,
+                                         _I64, _P]),
+    "ngram_count_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P]),
+    "ngram_select_hot_rows": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.POINTER(ctypes.c_int64), _P, _I64, _P]),
 }
 
 _lib = None
@@ -278,3 +290,100 @@ def ngram_gather_host(table: Table, rows, stage_out, remap_out, stage_scale_out=
     _check(lib().ngram_gather_host(table.c, _ptr(rows), n, _ptr(stage_out), _ptr(stage_scale_out),
                                    _ptr(remap_out), _stream(stream)), "ngram_gather_host")
     return stage_out, remap_out
+
+
+class RowPool:
+    """Device-memory row pool in front of a pinned-host table: ``pool_rows``
+    rows of the table's dtype (a hot-row cache in the first ``cached`` rows,
+    staged misses after them), per-row scales for int8, and the [R] map
+    ``slot_of_row``.  The buffers are torch device tensors."""
+
+    def __init__(self, table: Table, pool_rows: int, device="cuda:0", stream=None):
+        if table.location != IN_HOST:
+            raise NgramError("a row pool fronts a table in host memory")
+        self.table = table
+        self.pool_rows = int(pool_rows)
+        dt = torch.int16 if table.dtype == TABLE_BF16 else torch.int8
+        self.data = torch.empty(self.pool_rows * table.d, dtype=dt, device=device)
+        self.row_scale = (torch.empty(self.pool_rows, dtype=torch.float32, device=device)
+                          if table.dtype == TABLE_INT8_ROWSCALE else None)
+        self.slot_of_row = torch.empty(table.R, dtype=torch.int32, device=device)
+        self._c = _Pool(self.data.data_ptr(), None if self.row_scale is None else self.row_scale.data_ptr(),
+                        self.slot_of_row.data_ptr(), self.pool_rows, 0)
+        _check(lib().ngram_pool_reset(table.c, ctypes.byref(self._c), _stream(stream)), "ngram_pool_reset")
+
+    @property
+    def cached(self):
+        return int(self._c.cached)
+
+    def device_table(self) -> Table:
+        """The pool as a device table of ``pool_rows`` rows."""
+        return Table(self.data, self.pool_rows, self.table.d, self.table.dtype, row_scale=self.row_scale)
+
+
+def ngram_pool_workspace_bytes(n: int) -> int:
+    return int(lib().ngram_pool_workspace_bytes(int(n)))
+
+
+def pool_workspace(n: int, device="cuda:0"):
+    nbytes = ngram_pool_workspace_bytes(n)
+    return torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def ngram_pool_reset(pool: RowPool, stream=None):
+    _check(lib().ngram_pool_reset(pool.table.c, ctypes.byref(pool._c), _stream(stream)), "ngram_pool_reset")
+
+
+def ngram_pool_cache_rows(pool: RowPool, hot_rows, C=None, stream=None):
+    _dev(hot_rows, _I32T, "hot_rows")
+    C = hot_rows.numel() if C is None else int(C)
+    _need(hot_rows, C, "hot_rows")
+    _check(lib().ngram_pool_cache_rows(pool.table.c, ctypes.byref(pool._c), _ptr(hot_rows), C, _stream(stream)),
+           "ngram_pool_cache_rows")
+
+
+def ngram_pool_gather(pool: RowPool, rows, pool_rows_out=None, fetched_out=None, workspace=None, stream=None):
+    _dev(rows, _I32T, "rows")
+    n = rows.shape[0] if rows.dim() == 2 else rows.numel() // K
+    _need(rows, n * K, "rows")
+    if pool_rows_out is None:
+        pool_rows_out = torch.empty((n, K), dtype=torch.int32, device=rows.device)
+    _dev(pool_rows_out, _I32T, "pool_rows_out")
+    _need(pool_rows_out, n * K, "pool_rows_out")
+    if fetched_out is not None:
+        _dev(fetched_out, (torch.int64,), "fetched_out")
+    if workspace is None:
+        workspace = pool_workspace(n, rows.device)
+    _check(lib().ngram_pool_gather(pool.table.c, ctypes.byref(pool._c), _ptr(rows), n, _ptr(pool_rows_out),
+                                   _ptr(fetched_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "ngram_pool_gather")
+    return pool_rows_out
+
+
+def ngram_count_rows(rows, R, counts=None, accumulate=False, stream=None):
+    _dev(rows, _I32T, "rows")
+    n = rows.shape[0] if rows.dim() == 2 else rows.numel() // K
+    if counts is None:
+        counts = torch.empty(int(R), dtype=torch.int32, device=rows.device)
+        accumulate = False
+    _dev(counts, _I32T, "counts")
+    _need(counts, int(R), "counts")
+    _check(lib().ngram_count_rows(_ptr(rows), n, int(R), _ptr(counts), 1 if accumulate else 0, _stream(stream)),
+           "ngram_count_rows")
+    return counts
+
+
+def ngram_select_hot_rows(counts, C, hot_rows_out=None, workspace=None, stream=None):
+    """Returns (hot_rows_out, selected); synchronizes the stream."""
+    _dev(counts, _I32T, "counts")
+    if hot_rows_out is None:
+        hot_rows_out = torch.empty(max(int(C), 1), dtype=torch.int32, device=counts.device)
+    _dev(hot_rows_out, _I32T, "hot_rows_out")
+    _need(hot_rows_out, int(C), "hot_rows_out")
+    if workspace is None:
+        workspace = pool_workspace(0, counts.device)
+    sel = ctypes.c_int64(0)
+    _check(lib().ngram_select_hot_rows(_ptr(counts), counts.numel(), int(C), _ptr(hot_rows_out), ctypes.byref(sel),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "ngram_select_hot_rows")
+    return hot_rows_out, int(sel.value)

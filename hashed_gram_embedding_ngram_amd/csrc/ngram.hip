@@ -529,6 +529,170 @@ __global__ void __launch_bounds__(1024) ngram_stage_kernel(const StageArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Row pool: hot-row cache and per-batch dedup of misses for host tables.
+template <typename U>
+__device__ inline void copy_row(const U* __restrict__ src, U* __restrict__ dst, int64_t nu, int lane) {
+    constexpr int kUnroll = 8;
+    for (int64_t q0 = 0; q0 < nu; q0 += 64 * kUnroll) {
+        U buf[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t q = q0 + u * 64 + lane;
+            if (q < nu) buf[u] = src[q];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t q = q0 + u * 64 + lane;
+            if (q < nu) dst[q] = buf[u];
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) p[i] = v;
+}
+
+struct PoolArgs {
+    const void* tab;           // host table (device-side address)
+    const float* scale;        // host table's row scales (device) or null
+    const int32_t* rows;       // [n*16]
+    void* pool;                // [pool_rows][row_bytes]
+    float* pool_scale;         // [pool_rows] or null
+    const int32_t* slot_of_row;
+    int32_t* pool_rows_out;    // [n*16]
+    int32_t* keys;             // [H] hash set of missing row ids (-1: empty)
+    int32_t* vals;             // [H] their staging index
+    int32_t* miss;             // [n*16] distinct missing row ids, in staging order
+    uint32_t* counter;         // number of distinct missing rows
+    int64_t* fetched_out;
+    int64_t nrows;             // n * 16
+    int64_t R;
+    int64_t cached;
+    int64_t row_bytes;
+    uint32_t mask;             // H - 1
+    uint32_t shift;            // 32 - log2(H)
+};
+
+__device__ inline uint32_t set_home(int32_t r, uint32_t shift) {
+    return (static_cast<uint32_t>(r) * 0x9E3779B1u) >> shift;
+}
+
+__global__ void __launch_bounds__(256) pool_insert_kernel(const PoolArgs a) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= a.nrows) return;
+    const int32_t r = a.rows[t];
+    if (r < 0 || r >= a.R || a.slot_of_row[r] >= 0) return;
+    uint32_t h = set_home(r, a.shift);
+    for (uint32_t probe = 0; probe <= a.mask; ++probe) {
+        const int32_t prev = atomicCAS(&a.keys[h], -1, r);
+        if (prev == -1) {
+            const uint32_t u = atomicAdd(a.counter, 1u);
+            a.vals[h] = static_cast<int32_t>(u);
+            a.miss[u] = r;
+            return;
+        }
+        if (prev == r) return;
+        h = (h + 1) & a.mask;
+    }
+}
+
+__global__ void __launch_bounds__(256) pool_resolve_kernel(const PoolArgs a) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= a.nrows) return;
+    const int32_t r = a.rows[t];
+    int32_t out = -1;
+    if (r >= 0 && r < a.R) {
+        const int32_t s = a.slot_of_row[r];
+        if (s >= 0) {
+            out = s;
+        } else {
+            uint32_t h = set_home(r, a.shift);
+            for (uint32_t probe = 0; probe <= a.mask; ++probe) {
+                const int32_t k = a.keys[h];
+                if (k == r) {
+                    out = static_cast<int32_t>(a.cached + a.vals[h]);
+                    break;
+                }
+                if (k == -1) break;
+                h = (h + 1) & a.mask;
+            }
+        }
+    }
+    a.pool_rows_out[t] = out;
+}
+
+// Copy the distinct missing rows from the host table into the pool, one
+// wavefront per row, on a capped persistent grid.
+template <typename U>
+__global__ void __launch_bounds__(1024) pool_fetch_kernel(const PoolArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nmiss = static_cast<int64_t>(*a.counter);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.fetched_out) *a.fetched_out = nmiss;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
+    const int64_t nu = a.row_bytes / static_cast<int64_t>(sizeof(U));
+    for (int64_t u = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); u < nmiss;
+         u += waves) {
+        const int32_t r = a.miss[u];
+        const int64_t dst_row = a.cached + u;
+        if (lane == 0 && a.pool_scale) a.pool_scale[dst_row] = a.scale[r];
+        copy_row<U>(reinterpret_cast<const U*>(static_cast<const char*>(a.tab) + static_cast<int64_t>(r) * a.row_bytes),
+                    reinterpret_cast<U*>(static_cast<char*>(a.pool) + dst_row * a.row_bytes), nu, lane);
+    }
+}
+
+// Cache hot rows: wavefront per pool slot s, claiming slot_of_row[hot[s]].
+template <typename U>
+__global__ void __launch_bounds__(1024) pool_cache_kernel(const void* tab, const float* scale, const int32_t* hot,
+                                                          int64_t C, int64_t R, void* pool, float* pool_scale,
+                                                          int32_t* slot_of_row, int64_t row_bytes) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
+    const int64_t nu = row_bytes / static_cast<int64_t>(sizeof(U));
+    for (int64_t s = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); s < C; s += waves) {
+        const int32_t r = hot[s];
+        if (r < 0 || r >= R) continue;
+        int claimed = 0;
+        if (lane == 0) claimed = atomicCAS(&slot_of_row[r], -1, static_cast<int32_t>(s)) == -1;
+        claimed = __shfl(claimed, 0);
+        if (!claimed) continue;
+        if (lane == 0 && pool_scale) pool_scale[s] = scale[r];
+        copy_row<U>(reinterpret_cast<const U*>(static_cast<const char*>(tab) + static_cast<int64_t>(r) * row_bytes),
+                    reinterpret_cast<U*>(static_cast<char*>(pool) + s * row_bytes), nu, lane);
+    }
+}
+
+__global__ void __launch_bounds__(256) count_rows_kernel(const int32_t* rows, int64_t nrows, int64_t R, int32_t* counts) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= nrows) return;
+    const int32_t r = rows[t];
+    if (r >= 0 && r < R) atomicAdd(&counts[r], 1);
+}
+
+constexpr int kHistBins = 1024;
+
+__global__ void __launch_bounds__(256) count_hist_kernel(const int32_t* counts, int64_t R, int32_t* hist) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < R; r += stride) {
+        const int32_t c = counts[r];
+        if (c > 0) atomicAdd(&hist[c < kHistBins - 1 ? c : kHistBins - 1], 1);
+    }
+}
+
+__global__ void __launch_bounds__(256) select_kernel(const int32_t* counts, int64_t R, int32_t tau, int64_t C,
+                                                     int32_t* hot, uint32_t* sel) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < R; r += stride) {
+        int32_t c = counts[r];
+        if (c > kHistBins - 1) c = kHistBins - 1;
+        if (c >= tau) {
+            const uint32_t idx = atomicAdd(sel, 1u);
+            if (idx < C) hot[idx] = static_cast<int32_t>(r);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 int env_int(const char* name, int dflt) {
     const char* v = getenv(name);
@@ -633,6 +797,50 @@ Shape slice_shape(int64_t n, int32_t d, int32_t dtype) {
 int host_workgroups() {
     const int v = env_int("NGRAM_HOST_WORKGROUPS", 0);
     return v > 0 ? v : 8;
+}
+
+int64_t table_row_bytes(const ngram_table* T) {
+    return static_cast<int64_t>(T->d) * (T->dtype == NGRAM_TABLE_BF16 ? 2 : 1);
+}
+
+unsigned grid_for(int64_t count) {
+    int64_t g = (count + 255) / 256;
+    if (g > 65536) g = 65536;
+    if (g < 1) g = 1;
+    return static_cast<unsigned>(g);
+}
+
+// Workspace of ngram_pool_gather: a hash set of 2^k >= 2 * 16 n slots (keys and
+// staging indices), the list of distinct missing rows, a counter; the
+// selection call reuses the front for a 1024-bin histogram and a counter.
+struct PoolLayout {
+    int64_t H, log2H, keys, vals, miss, counter, total;
+};
+
+PoolLayout pool_layout(int64_t n) {
+    PoolLayout L;
+    L.log2H = 6;
+    while ((int64_t{1} << L.log2H) < 2 * kK * n) ++L.log2H;
+    L.H = int64_t{1} << L.log2H;
+    L.keys = 0;
+    L.vals = 4 * L.H;
+    L.miss = 8 * L.H;
+    L.counter = ((8 * L.H + 4 * kK * n) + 15) & ~int64_t{15};
+    L.total = L.counter + 16;
+    const int64_t select_need = 4 * (kHistBins + 4);
+    if (L.total < select_need) L.total = select_need;
+    return L;
+}
+
+int check_pool(const ngram_table* T, const ngram_row_pool* P) {
+    int rc = check_table(T);
+    if (rc) return rc;
+    if (T->location != NGRAM_IN_HOST) return fail(NGRAM_ENOTSUP, "the row pool fronts a host table");
+    if (!P || !P->data || !P->slot_of_row) return fail(NGRAM_EINVAL, "pool, pool data or slot_of_row is NULL");
+    if (!aligned(P->data, 16)) return fail(NGRAM_EALIGN, "pool data not 16-byte aligned");
+    if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE && !P->row_scale) return fail(NGRAM_EINVAL, "int8 pool needs row_scale");
+    if (P->pool_rows < 0 || P->pool_rows > NGRAM_MAX_ROWS) return fail(NGRAM_ERANGE, "pool_rows out of range");
+    return NGRAM_OK;
 }
 
 void cap_for_host(Shape& sh, const ngram_table* T) {
@@ -850,6 +1058,151 @@ int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
     if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x4>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(ngram_stage_kernel<u32x2>, grid, block, 0, stream, a);
     return hip_status("ngram_gather_host launch");
+}
+
+int64_t ngram_pool_workspace_bytes(int64_t n) {
+    if (n < 0) return -1;
+    return pool_layout(n).total;
+}
+
+int ngram_pool_reset(const ngram_table* T_host, ngram_row_pool* P, ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_table(T_host);
+    if (rc) return rc;
+    if (!P || !P->slot_of_row) return fail(NGRAM_EINVAL, "pool or slot_of_row is NULL");
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(T_host->R)), dim3(256), 0, stream, P->slot_of_row, T_host->R, -1);
+    rc = hip_status("ngram_pool_reset launch");
+    if (!rc) P->cached = 0;
+    return rc;
+}
+
+int ngram_pool_cache_rows(const ngram_table* T_host, ngram_row_pool* P, const int32_t* hot_rows, int64_t C,
+                          ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_pool(T_host, P);
+    if (rc) return rc;
+    if (C < 0 || C > P->pool_rows) return fail(NGRAM_ERANGE, "C=%lld outside [0, pool_rows]", (long long)C);
+    if (C > 0 && !hot_rows) return fail(NGRAM_EINVAL, "hot_rows is NULL");
+    const void* tab = nullptr;
+    rc = table_device_ptr(T_host, &tab);
+    if (rc) return rc;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(T_host->R)), dim3(256), 0, stream, P->slot_of_row, T_host->R, -1);
+    if (C > 0) {
+        const int64_t row_bytes = table_row_bytes(T_host);
+        int64_t blocks = (C + 15) / 16;
+        if (blocks > host_workgroups()) blocks = host_workgroups();
+        float* pscale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? P->row_scale : nullptr;
+        if (row_bytes % 16 == 0)
+            hipLaunchKernelGGL(pool_cache_kernel<u32x4>, dim3(blocks), dim3(1024), 0, stream, tab, T_host->row_scale,
+                               hot_rows, C, T_host->R, P->data, pscale, P->slot_of_row, row_bytes);
+        else
+            hipLaunchKernelGGL(pool_cache_kernel<u32x2>, dim3(blocks), dim3(1024), 0, stream, tab, T_host->row_scale,
+                               hot_rows, C, T_host->R, P->data, pscale, P->slot_of_row, row_bytes);
+    }
+    rc = hip_status("ngram_pool_cache_rows launch");
+    if (!rc) P->cached = C;
+    return rc;
+}
+
+int ngram_pool_gather(const ngram_table* T_host, const ngram_row_pool* P, const int32_t* rows, int64_t n,
+                      int32_t* pool_rows_out, int64_t* fetched_out, void* workspace, int64_t workspace_bytes,
+                      ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_pool(T_host, P);
+    if (rc) return rc;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > (1 << 26)) return fail(NGRAM_ERANGE, "n=%lld above 2^26", (long long)n);
+    if (P->cached < 0 || P->pool_rows < P->cached + kK * n)
+        return fail(NGRAM_ERANGE, "pool_rows=%lld < cached %lld + 16 n", (long long)P->pool_rows, (long long)P->cached);
+    if (n > 0 && (!rows || !pool_rows_out)) return fail(NGRAM_EINVAL, "rows or pool_rows_out is NULL");
+    const PoolLayout L = pool_layout(n);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < L.total)
+        return fail(NGRAM_EINVAL, "workspace needs %lld bytes, 16-byte aligned", (long long)L.total);
+    if (n == 0) return NGRAM_OK;
+    const void* tab = nullptr;
+    rc = table_device_ptr(T_host, &tab);
+    if (rc) return rc;
+    char* ws = static_cast<char*>(workspace);
+    PoolArgs a;
+    a.tab = tab; a.scale = T_host->row_scale; a.rows = rows; a.pool = P->data;
+    a.pool_scale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? P->row_scale : nullptr;
+    a.slot_of_row = P->slot_of_row; a.pool_rows_out = pool_rows_out;
+    a.keys = reinterpret_cast<int32_t*>(ws + L.keys);
+    a.vals = reinterpret_cast<int32_t*>(ws + L.vals);
+    a.miss = reinterpret_cast<int32_t*>(ws + L.miss);
+    a.counter = reinterpret_cast<uint32_t*>(ws + L.counter);
+    a.fetched_out = fetched_out;
+    a.nrows = n * kK; a.R = T_host->R; a.cached = P->cached; a.row_bytes = table_row_bytes(T_host);
+    a.mask = static_cast<uint32_t>(L.H - 1);
+    a.shift = 32u - static_cast<uint32_t>(L.log2H);
+    // keys := -1 and counter := 0 with one fill (the counter word follows the keys' region)
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(L.H)), dim3(256), 0, stream, a.keys, L.H, -1);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, stream, reinterpret_cast<int32_t*>(a.counter), 4, 0);
+    const dim3 g(static_cast<unsigned>((a.nrows + 255) / 256)), b(256);
+    hipLaunchKernelGGL(pool_insert_kernel, g, b, 0, stream, a);
+    hipLaunchKernelGGL(pool_resolve_kernel, g, b, 0, stream, a);
+    int64_t blocks = (a.nrows + 15) / 16;
+    if (blocks > host_workgroups()) blocks = host_workgroups();
+    if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(pool_fetch_kernel<u32x4>, dim3(blocks), dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL(pool_fetch_kernel<u32x2>, dim3(blocks), dim3(1024), 0, stream, a);
+    return hip_status("ngram_pool_gather launch");
+}
+
+int ngram_count_rows(const int32_t* rows, int64_t n, int64_t R, int32_t* counts, int32_t accumulate,
+                     ngram_stream_t stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > INT32_MAX / kK) return fail(NGRAM_ERANGE, "n=%lld above (2^31-1)/16", (long long)n);
+    if (R < 1 || R > NGRAM_MAX_ROWS) return fail(NGRAM_ERANGE, "R=%lld outside [1, 2^31-1]", (long long)R);
+    if (!counts || (n > 0 && !rows)) return fail(NGRAM_EINVAL, "counts or rows is NULL");
+    if (!accumulate) hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(R)), dim3(256), 0, stream, counts, R, 0);
+    if (n > 0)
+        hipLaunchKernelGGL(count_rows_kernel, dim3(static_cast<unsigned>((n * kK + 255) / 256)), dim3(256), 0, stream,
+                           rows, n * kK, R, counts);
+    return hip_status("ngram_count_rows launch");
+}
+
+int ngram_select_hot_rows(const int32_t* counts, int64_t R, int64_t C, int32_t* hot_rows_out, int64_t* selected,
+                          void* workspace, int64_t workspace_bytes, ngram_stream_t stream) {
+    g_err[0] = 0;
+    if (R < 1 || R > NGRAM_MAX_ROWS) return fail(NGRAM_ERANGE, "R=%lld outside [1, 2^31-1]", (long long)R);
+    if (C < 0 || C > INT32_MAX) return fail(NGRAM_ERANGE, "C=%lld outside [0, 2^31-1]", (long long)C);
+    if (!counts || !selected || (C > 0 && !hot_rows_out)) return fail(NGRAM_EINVAL, "counts, hot_rows_out or selected is NULL");
+    const int64_t need = pool_layout(0).total;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+        return fail(NGRAM_EINVAL, "workspace needs %lld bytes, 16-byte aligned", (long long)need);
+    *selected = 0;
+    if (C == 0) return NGRAM_OK;
+    int32_t* hist = static_cast<int32_t*>(workspace);
+    uint32_t* sel = reinterpret_cast<uint32_t*>(hist + kHistBins);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(4), dim3(256), 0, stream, hist, kHistBins + 4, 0);
+    hipLaunchKernelGGL(count_hist_kernel, dim3(grid_for(R)), dim3(256), 0, stream, counts, R, hist);
+    int rc = hip_status("ngram_select_hot_rows launch");
+    if (rc) return rc;
+    int32_t h[kHistBins];
+    hipError_t e = hipMemcpyAsync(h, hist, sizeof(h), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(NGRAM_EHIP, "reading the count histogram: %s", hipGetErrorString(e));
+    // smallest threshold whose set {count >= tau} holds at most C rows
+    int32_t tau = 1;
+    int64_t cum = 0;
+    for (int b = kHistBins - 1; b >= 1; --b) {
+        if (cum + h[b] > C) {
+            tau = b + 1;
+            break;
+        }
+        cum += h[b];
+    }
+    if (tau > kHistBins - 1) tau = kHistBins - 1;    // the top value alone overflows C: take C of it
+    hipLaunchKernelGGL(select_kernel, dim3(grid_for(R)), dim3(256), 0, stream, counts, R, tau, C, hot_rows_out, sel);
+    rc = hip_status("ngram_select_hot_rows launch");
+    if (rc) return rc;
+    uint32_t got = 0;
+    e = hipMemcpyAsync(&got, sel, sizeof(got), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(NGRAM_EHIP, "reading the selection count: %s", hipGetErrorString(e));
+    *selected = got < static_cast<uint64_t>(C) ? static_cast<int64_t>(got) : C;
+    return NGRAM_OK;
 }
 
 }  // extern "C"

@@ -154,6 +154,72 @@ int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
                       void* stage_out, float* stage_scale_out, int32_t* remap_out,
                       ngram_stream_t stream);
 
+/* Row pool in front of a pinned-host table: a hot-row cache in HBM plus a
+ * per-batch gather of the distinct missing rows.  "Qwen 3.8 Flash-Next Deep
+ * Dive…", section 1, calls phrase frequency heavily Zipfian, so a small set of
+ * rows carries much of the traffic; "Qwen Brought Back N-Grams…", section
+ * "Which is why the offload matters more than the parameter count", reads the
+ * rows of a pinned-host shard over PCIe, which bounds the host gather.  Every pool
+ * row is an exact copy of a table row, so summing from the pool gives
+ * bit-identical results to summing from the host table.
+ *
+ * data [pool_rows][d] in the table's dtype (device, 16-byte aligned);
+ * row_scale [pool_rows] fp32 for int8 tables, else NULL; slot_of_row [R] int32
+ * (device): the pool row that caches table row r, or -1.  Pool rows
+ * [0, cached) hold cached rows; rows [cached, pool_rows) stage misses.  All
+ * three buffers are caller-owned. */
+typedef struct {
+    void* data;
+    float* row_scale;
+    int32_t* slot_of_row;
+    int64_t pool_rows;
+    int64_t cached;
+} ngram_row_pool;
+
+/* Bytes of device workspace ngram_pool_gather needs for n tokens, and that
+ * ngram_select_hot_rows needs (n = 0). */
+int64_t ngram_pool_workspace_bytes(int64_t n);
+
+/* Empty the cache: slot_of_row[r] = -1 for all r, P->cached = 0. */
+int ngram_pool_reset(const ngram_table* T_host, ngram_row_pool* P, ngram_stream_t stream);
+
+/* Cache table rows hot_rows[0..C) (device int32) in pool rows 0..C-1 (read
+ * over PCIe) and point slot_of_row at them, after clearing it; duplicate or
+ * out-of-range ids leave their pool row unused.  Sets P->cached = C.
+ * Errors: EINVAL, ERANGE (C > pool_rows), ENOTSUP (T_host not in host memory). */
+int ngram_pool_cache_rows(const ngram_table* T_host, ngram_row_pool* P, const int32_t* hot_rows,
+                          int64_t C, ngram_stream_t stream);
+
+/* Per batch: map rows[n][16] to pool rows.  A cached row maps to its slot;
+ * each distinct uncached row is read over PCIe exactly once into pool row
+ * cached + u (u = 0, 1, … in an unspecified order); an out-of-range row id
+ * maps to -1.  Writes pool_rows_out[n][16] (device int32) and, if non-NULL,
+ * *fetched_out (device int64) = the number of distinct rows read over PCIe.
+ * ngram_embed_bag on the pool (as a device table of pool_rows rows) with
+ * pool_rows_out then gives exactly ngram_embed_bag(T_host, rows).
+ * Needs P->pool_rows >= P->cached + 16 * n (ERANGE) and a device workspace of
+ * ngram_pool_workspace_bytes(n) bytes, 16-byte aligned (EINVAL). */
+int ngram_pool_gather(const ngram_table* T_host, const ngram_row_pool* P, const int32_t* rows,
+                      int64_t n, int32_t* pool_rows_out, int64_t* fetched_out, void* workspace,
+                      int64_t workspace_bytes, ngram_stream_t stream);
+
+/* counts[r] += number of (token, k) with rows[i][k] == r, for r in [0, R);
+ * accumulate = 0 clears counts first.  counts [R] int32, device. */
+int ngram_count_rows(const int32_t* rows, int64_t n, int64_t R, int32_t* counts, int32_t accumulate,
+                     ngram_stream_t stream);
+
+/* Choose up to C hot rows from counts[R]: every row whose count reaches the
+ * smallest threshold that keeps the set within C (counts above 1023 count as
+ * 1023; where even the top value holds more than C rows, C of them are taken
+ * in an unspecified order).  Rows never counted are not chosen.  Writes
+ * hot_rows_out[0..*selected) (device int32, C entries of room) and *selected
+ * (HOST int64).  Synchronizes `stream` (it reads a 1024-bin histogram back),
+ * so it belongs between batches, not in a captured graph.  Workspace:
+ * ngram_pool_workspace_bytes(0) bytes of device memory. */
+int ngram_select_hot_rows(const int32_t* counts, int64_t R, int64_t C, int32_t* hot_rows_out,
+                          int64_t* selected, void* workspace, int64_t workspace_bytes,
+                          ngram_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,54 @@ def test_product_package_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("oracle/", ""), f"{f} mentions the oracle"
+
+
+def _pool(data=A, scale=None, slots=A, pool_rows=10_000, cached=0):
+    return ng._Pool(data, scale, slots, pool_rows, cached)
+
+
+def test_pool_workspace_sizes():
+    L = ng.lib()
+    assert L.ngram_pool_workspace_bytes(-1) == -1
+    assert L.ngram_pool_workspace_bytes(0) >= 4 * (1024 + 4)
+    n = 8192
+    assert L.ngram_pool_workspace_bytes(n) >= 8 * (2 * 16 * n) + 4 * 16 * n
+
+
+def test_pool_argument_checks():
+    L = ng.lib()
+    host_t = ctypes.byref(_table(loc=1))
+    dev_t = ctypes.byref(_table())
+    P = _pool()
+    W = ctypes.c_int64(L.ngram_pool_workspace_bytes(4))
+    assert L.ngram_pool_gather(dev_t, ctypes.byref(P), A, 4, A, None, A, W, None) == ENOTSUP
+    assert L.ngram_pool_gather(host_t, None, A, 4, A, None, A, W, None) == EINVAL
+    assert L.ngram_pool_gather(host_t, ctypes.byref(_pool(data=A + 8)), A, 4, A, None, A, W, None) == EALIGN
+    assert L.ngram_pool_gather(host_t, ctypes.byref(_pool(pool_rows=63)), A, 4, A, None, A, W, None) == ERANGE
+    assert L.ngram_pool_gather(host_t, ctypes.byref(_pool(pool_rows=100, cached=40)), A, 4, A, None, A, W,
+                               None) == ERANGE
+    assert L.ngram_pool_gather(host_t, ctypes.byref(P), A, 4, A, None, A, 16, None) == EINVAL
+    assert L.ngram_pool_gather(host_t, ctypes.byref(P), A, 4, A, None, A + 8, W, None) == EINVAL
+    assert L.ngram_pool_gather(host_t, ctypes.byref(P), None, 4, A, None, A, W, None) == EINVAL
+    assert L.ngram_pool_gather(host_t, ctypes.byref(P), A, -1, A, None, A, W, None) == EINVAL
+    assert L.ngram_pool_gather(host_t, ctypes.byref(P), None, 0, None, None, A, W, None) == OK
+    h8 = ctypes.byref(_table(loc=1, dtype=1, scale=A))
+    assert L.ngram_pool_gather(h8, ctypes.byref(P), A, 4, A, None, A, W, None) == EINVAL  # no pool scale
+    assert L.ngram_pool_cache_rows(host_t, ctypes.byref(P), A, 10_001, None) == ERANGE
+    assert L.ngram_pool_cache_rows(host_t, ctypes.byref(P), None, 5, None) == EINVAL
+    assert L.ngram_pool_cache_rows(dev_t, ctypes.byref(P), A, 5, None) == ENOTSUP
+    assert L.ngram_pool_reset(host_t, None, None) == EINVAL
+
+
+def test_count_and_select_argument_checks():
+    L = ng.lib()
+    assert L.ngram_count_rows(A, -1, 100, A, 0, None) == EINVAL
+    assert L.ngram_count_rows(A, 4, 0, A, 0, None) == ERANGE
+    assert L.ngram_count_rows(A, 4, 100, None, 0, None) == EINVAL
+    W = L.ngram_pool_workspace_bytes(0)
+    sel = ctypes.c_int64(-1)
+    assert L.ngram_select_hot_rows(A, 0, 10, A, ctypes.byref(sel), A, W, None) == ERANGE
+    assert L.ngram_select_hot_rows(A, 100, -1, A, ctypes.byref(sel), A, W, None) == ERANGE
+    assert L.ngram_select_hot_rows(A, 100, 10, A, None, A, W, None) == EINVAL
+    assert L.ngram_select_hot_rows(A, 100, 10, A, ctypes.byref(sel), A, 64, None) == EINVAL
+    assert L.ngram_select_hot_rows(A, 100, 0, None, ctypes.byref(sel), A, W, None) == OK and sel.value == 0

@@ -300,3 +300,76 @@ def test_host_table_paths(wgs, tpw, table, monkeypatch):
         assert np.array_equal(eN2.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
     finally:
         hb.free()
+
+
+@pytest.mark.parametrize("table,C", [("bf16", 500), ("bf16", 0), ("int8", 300)])
+def test_row_pool(table, C):
+    """Hot-row cache + per-batch dedup in front of a host table: the sums from
+    the pool equal the oracle's bit for bit, every pool row is an exact copy
+    of its table row, and each distinct uncached row is fetched exactly once."""
+    from synth.workloads import fill_host_table
+    kw = dict(table="int8", table_kind=synth.KIND_I8_NORMAL) if table == "int8" else \
+        dict(table_kind=synth.KIND_BF16_WIDE)
+    sp = Spec(f"pool_{table}_{C}", (40, 0, 300, 3), 151936, 20_011, 2560, config_id=28, **kw)
+    say(sp.name)
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h, table=False)
+    npdt = np.int16 if table == "bf16" else np.int8
+    hb = ng.HostBuffer(sp.R * sp.d * np.dtype(npdt).itemsize)
+    try:
+        host_np = hb.numpy(npdt, (sp.R, sp.d))
+        fill_host_table(sp, host_np)
+        scale = None
+        if table == "int8":
+            scale = synth.fill_gpu(synth.KIND_F32_SCALE, sp.seed, synth.TAG_SCALE,
+                                   torch.empty(sp.R, dtype=torch.float32, device="cuda:0"))
+        T = ng.Table(hb, sp.R, sp.d, ng.TABLE_INT8_ROWSCALE if table == "int8" else ng.TABLE_BF16, row_scale=scale)
+        # frequencies from two other batches choose the cached rows
+        counts = None
+        for b in (1, 2):
+            hb_in = HostInputs(sp.replace(batch=b))
+            r_b = ng.ngram_hash(torch.from_numpy(hb_in.tokens).cuda(), torch.from_numpy(hb_in.offsets).cuda(), sp.R)
+            counts = ng.ngram_count_rows(r_b, sp.R, counts=counts, accumulate=counts is not None)
+        pool = ng.RowPool(T, C + 16 * sp.n)
+        hot, selected = ng.ngram_select_hot_rows(counts, C)
+        ng.ngram_pool_cache_rows(pool, hot, selected)
+        rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+        rows_bad = rows.clone()
+        rows_bad[5, 3] = sp.R
+        rows_bad[7, 0] = -1
+        fetched = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+        prow = ng.ngram_pool_gather(pool, rows_bad, fetched_out=fetched)
+        eN = ng.ngram_embed_bag(pool.device_table(), prow)
+        torch.cuda.synchronize()
+
+        want_rows, want_eN, _ = expected(h)
+        assert np.array_equal(rows.cpu().numpy(), want_rows)
+        e = eN.cpu().numpy()
+        good = np.ones(sp.n, bool)
+        good[[5, 7]] = False
+        assert np.all(np.isnan(e[~good]))
+        assert np.array_equal(e[good].view(np.uint32), want_eN[good].view(np.uint32))
+
+        cnt = counts.cpu().numpy()
+        hot_np = hot.cpu().numpy()[:selected]
+        assert selected <= C and len(set(hot_np.tolist())) == selected and np.all(cnt[hot_np] > 0)
+        if selected:
+            rest = np.ones(sp.R, bool)
+            rest[hot_np] = False
+            u = cnt[rest].max()
+            assert cnt[hot_np].min() > u                            # a threshold set
+            assert u == 0 or selected + int((cnt == u).sum()) > C   # the next level would not fit
+        slots = pool.slot_of_row.cpu().numpy()
+        assert set(np.nonzero(slots >= 0)[0].tolist()) == set(hot_np.tolist())
+        rb = rows_bad.cpu().numpy()
+        valid = (rb >= 0) & (rb < sp.R)
+        distinct = np.unique(rb[valid])
+        assert int(fetched.item()) == int((slots[distinct] < 0).sum())
+        pr = prow.cpu().numpy()
+        assert np.all(pr[~valid] == -1) and np.all(pr[valid] >= 0)
+        pool_np = pool.data.view(pool.pool_rows, sp.d).cpu().numpy()
+        assert np.array_equal(pool_np[pr[valid]].view(npdt), host_np[rb[valid]])
+        if table == "int8":
+            assert np.array_equal(pool.row_scale.cpu().numpy()[pr[valid]], scale.cpu().numpy()[rb[valid]])
+    finally:
+        hb.free()
