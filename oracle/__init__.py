@@ -44,6 +44,9 @@ def lib():
         L.oracle_gate_add.argtypes = [P, P, I64, I32, P, P, P, P]
         L.oracle_forward.argtypes = [P, I64, P, I32, P, P, I32, P, P, I64, I32,
                                      P, P, P, P, P, P]
+        L.oracle_grad_table_rows.argtypes = [P, I64, I32, P, P, P, I64, P]
+        L.oracle_grad_e1_tokens.argtypes = [P, P, I64, I32, P, P, I64, P]
+        L.oracle_grad_gate.argtypes = [P, P, P, I64, I32, P]
         _lib = L
     return _lib
 
@@ -145,3 +148,42 @@ def forward(tokens, seq_offsets, table, W_g, e1=None, residual=None, history=Non
                          _p(tab), _p(sc), R, d, _p(_c(e1, np.uint16)), _p(_c(W_g, np.float32)),
                          _p(_c(residual, np.uint16)), _p(out), _p(rows), _p(eN))
     return out, rows, eN
+
+
+def grad_table(rows, W_g, g, query=None):
+    """(query rows, dT [nq][d] fp32).  ``g`` is bf16 bits [n][d]; ``query``
+    defaults to every distinct valid row, ascending."""
+    rows = _c(rows, np.int32)
+    g = _c(g, np.uint16)
+    n, d = g.shape
+    if query is None:
+        query = np.unique(rows[rows >= 0])
+    query = _c(query, np.int32)
+    out = np.zeros((query.size, d), dtype=np.float32)
+    lib().oracle_grad_table_rows(_p(rows), n, d, _p(_c(W_g, np.float32)), _p(g), _p(query), query.size, _p(out))
+    return query, out
+
+
+def grad_e1(tokens, rows, g, query=None):
+    """(query tokens, de1 [nq][d] fp32); ``query`` defaults to every distinct
+    token of a valid position, ascending."""
+    tokens = _c(tokens, np.int32)
+    rows = _c(rows, np.int32).reshape(-1, K)
+    g = _c(g, np.uint16)
+    n, d = g.shape
+    if query is None:
+        query = np.unique(tokens[rows[:, 0] >= 0])
+    query = _c(query, np.int32)
+    out = np.zeros((query.size, d), dtype=np.float32)
+    lib().oracle_grad_e1_tokens(_p(tokens), _p(rows), n, d, _p(g), _p(query), query.size, _p(out))
+    return query, out
+
+
+def grad_gate(rows, g, eN):
+    rows = _c(rows, np.int32)
+    g = _c(g, np.uint16)
+    eN = _c(eN, np.float32)
+    n, d = g.shape
+    out = np.zeros(d, dtype=np.float32)
+    lib().oracle_grad_gate(_p(rows), _p(g), _p(eN), n, d, _p(out))
+    return out

@@ -207,3 +207,69 @@ void oracle_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets
     if (!eN_out)
         free(eN);
 }
+
+/*
+ * Gradients.  The pages define only the forward pass of a "learned" table
+ * ("Qwen Brought Back N-Grams…", section "N-grams, of all things"); these
+ * follow from it by the chain rule, with the bf16 output rounding passed
+ * straight through.  g is dL/dout, bf16 [n][d].  A token whose row ids are
+ * -1 (invalid input) contributes nothing.  The order of each sum is fixed:
+ *   table:  dT[r][j]  = sum over positions t = 16 i + k with rows[t] == r, in
+ *           ascending t, of acc = fmaf(W_g[j], g[i][j], acc), from +0;
+ *   e1:     de1[v][j] = sum over tokens i with tokens[i] == v, ascending i,
+ *           of acc = acc + g[i][j], from +0;
+ *   gate:   dW_g[j]   = sum over chunks c = 0, 1, … of 256 tokens, in order,
+ *           of part_c, each part_c = fmaf(g[i][j], eN[i][j], part) over the
+ *           chunk's tokens in ascending i, from +0.
+ * The residual's gradient is g itself.
+ */
+void oracle_grad_table_rows(const int32_t* rows, int64_t n, int32_t d, const float* W_g,
+                            const uint16_t* g, const int32_t* query, int64_t nq, float* out)
+{
+    for (int64_t q = 0; q < nq; ++q) {
+        float* acc = out + q * d;
+        for (int32_t j = 0; j < d; ++j)
+            acc[j] = 0.0f;
+        for (int64_t t = 0; t < n * ORACLE_K; ++t) {
+            if (rows[t] != query[q] || rows[t] < 0)
+                continue;
+            const int64_t i = t / ORACLE_K;
+            for (int32_t j = 0; j < d; ++j)
+                acc[j] = fmaf(W_g[j], oracle_bf16_to_f32(g[i * d + j]), acc[j]);
+        }
+    }
+}
+
+void oracle_grad_e1_tokens(const int32_t* tokens, const int32_t* rows, int64_t n, int32_t d,
+                           const uint16_t* g, const int32_t* query, int64_t nq, float* out)
+{
+    for (int64_t q = 0; q < nq; ++q) {
+        float* acc = out + q * d;
+        for (int32_t j = 0; j < d; ++j)
+            acc[j] = 0.0f;
+        for (int64_t i = 0; i < n; ++i) {
+            if (tokens[i] != query[q] || rows[i * ORACLE_K] < 0)
+                continue;
+            for (int32_t j = 0; j < d; ++j)
+                acc[j] = acc[j] + oracle_bf16_to_f32(g[i * d + j]);
+        }
+    }
+}
+
+void oracle_grad_gate(const int32_t* rows, const uint16_t* g, const float* eN, int64_t n, int32_t d,
+                      float* out)
+{
+    for (int32_t j = 0; j < d; ++j) {
+        float total = 0.0f;
+        for (int64_t c0 = 0; c0 < n; c0 += 256) {
+            float part = 0.0f;
+            for (int64_t i = c0; i < n && i < c0 + 256; ++i) {
+                if (rows[i * ORACLE_K] < 0)
+                    continue;
+                part = fmaf(oracle_bf16_to_f32(g[i * d + j]), eN[i * d + j], part);
+            }
+            total = total + part;
+        }
+        out[j] = total;
+    }
+}

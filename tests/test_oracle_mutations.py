@@ -44,6 +44,21 @@ MUTATIONS = {
                       "return (uint16_t)((u + 0x8000u) >> 16);"),
     "round_truncate": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
                        "return (uint16_t)(u >> 16);"),
+    "grad_table_token_index": ("const int64_t i = t / ORACLE_K;", "const int64_t i = t % ORACLE_K;"),
+    "grad_table_no_weight": ("acc[j] = fmaf(W_g[j], oracle_bf16_to_f32(g[i * d + j]), acc[j]);",
+                             "acc[j] = acc[j] + oracle_bf16_to_f32(g[i * d + j]);"),
+    "grad_table_unfused": ("acc[j] = fmaf(W_g[j], oracle_bf16_to_f32(g[i * d + j]), acc[j]);",
+                           "acc[j] = W_g[j] * oracle_bf16_to_f32(g[i * d + j]) + acc[j];"),
+    "grad_e1_keeps_invalid": ("if (tokens[i] != query[q] || rows[i * ORACLE_K] < 0)",
+                              "if (tokens[i] != query[q])"),
+    "grad_gate_chunk_128": ("for (int64_t c0 = 0; c0 < n; c0 += 256) {\n            float part = 0.0f;\n"
+                            "            for (int64_t i = c0; i < n && i < c0 + 256; ++i) {",
+                            "for (int64_t c0 = 0; c0 < n; c0 += 128) {\n            float part = 0.0f;\n"
+                            "            for (int64_t i = c0; i < n && i < c0 + 128; ++i) {"),
+    "grad_gate_unfused": ("part = fmaf(oracle_bf16_to_f32(g[i * d + j]), eN[i * d + j], part);",
+                          "part = oracle_bf16_to_f32(g[i * d + j]) * eN[i * d + j] + part;"),
+    "grad_gate_keeps_invalid": ("if (rows[i * ORACLE_K] < 0)\n                    continue;\n                part",
+                                "part"),
 }
 
 
@@ -59,6 +74,7 @@ def test_pins_catch_mutation(name, tmp_path):
                     "-o", str(mlib), str(msrc), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(mlib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py"],
+                        "tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py",
+                        "tests/test_oracle_grad.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
