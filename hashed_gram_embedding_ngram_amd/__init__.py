@@ -62,6 +62,10 @@ _SIGNATURES = {
     "ngram_pool_gather": (ctypes.c_int, [ctypes.POINTER(_Table), ctypes.POINTER(_Pool), _P, _I64, _P, _P, _P,
                                          _I64, _P]),
     "ngram_count_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P]),
+    "ngram_grad_workspace_bytes": (ctypes.c_int64, [_I64, _I32]),
+    "ngram_grad_table": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "ngram_grad_e1": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _P, _P, _P, _P, _I64, _P]),
+    "ngram_grad_gate": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _P, _P, _I64, _P]),
     "ngram_select_hot_rows": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.POINTER(ctypes.c_int64), _P, _I64, _P]),
 }
 
@@ -387,3 +391,76 @@ def ngram_select_hot_rows(counts, C, hot_rows_out=None, workspace=None, stream=N
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(stream)), "ngram_select_hot_rows")
     return hot_rows_out, int(sel.value)
+
+
+def grad_workspace(n: int, d: int, device="cuda:0"):
+    nbytes = int(lib().ngram_grad_workspace_bytes(int(n), int(d)))
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ws_args(workspace):
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def ngram_grad_table(rows, W_g, dout, R, grad_rows_out=None, grad_out=None, n_unique_out=None,
+                     workspace=None, stream=None):
+    """Sparse table gradient: (grad_rows_out [16n], grad_out [16n][d], n_unique_out [1] int64);
+    the first n_unique_out rows are valid."""
+    _dev(rows, _I32T, "rows")
+    _dev(W_g, _F32, "W_g")
+    _dev(dout, _BF16, "dout")
+    n = rows.shape[0] if rows.dim() == 2 else rows.numel() // K
+    d = dout.numel() // max(n, 1) if n else W_g.numel()
+    _need(rows, n * K, "rows")
+    _need(W_g, d, "W_g")
+    dev = rows.device
+    grad_rows_out = torch.empty(n * K, dtype=torch.int32, device=dev) if grad_rows_out is None else grad_rows_out
+    grad_out = torch.empty((n * K, d), dtype=torch.float32, device=dev) if grad_out is None else grad_out
+    n_unique_out = torch.empty(1, dtype=torch.int64, device=dev) if n_unique_out is None else n_unique_out
+    _dev(grad_rows_out, _I32T, "grad_rows_out")
+    _dev(grad_out, _F32, "grad_out")
+    _dev(n_unique_out, (torch.int64,), "n_unique_out")
+    _need(grad_rows_out, n * K, "grad_rows_out")
+    _need(grad_out, n * K * d, "grad_out")
+    workspace = grad_workspace(n, d, dev) if workspace is None else workspace
+    _check(lib().ngram_grad_table(_ptr(rows), n, d, int(R), _ptr(W_g), _ptr(dout), _ptr(grad_rows_out),
+                                  _ptr(grad_out), _ptr(n_unique_out), *_ws_args(workspace), _stream(stream)),
+           "ngram_grad_table")
+    return grad_rows_out, grad_out, n_unique_out
+
+
+def ngram_grad_e1(tokens, rows, dout, V, grad_tokens_out=None, grad_out=None, n_unique_out=None,
+                  workspace=None, stream=None):
+    _dev(tokens, _I32T, "tokens")
+    _dev(rows, _I32T, "rows")
+    _dev(dout, _BF16, "dout")
+    n = tokens.numel()
+    d = dout.numel() // max(n, 1)
+    _need(rows, n * K, "rows")
+    dev = tokens.device
+    grad_tokens_out = torch.empty(n, dtype=torch.int32, device=dev) if grad_tokens_out is None else grad_tokens_out
+    grad_out = torch.empty((n, d), dtype=torch.float32, device=dev) if grad_out is None else grad_out
+    n_unique_out = torch.empty(1, dtype=torch.int64, device=dev) if n_unique_out is None else n_unique_out
+    _need(grad_tokens_out, n, "grad_tokens_out")
+    _need(grad_out, n * d, "grad_out")
+    workspace = grad_workspace(n, d, dev) if workspace is None else workspace
+    _check(lib().ngram_grad_e1(_ptr(tokens), _ptr(rows), n, d, int(V), _ptr(dout), _ptr(grad_tokens_out),
+                               _ptr(grad_out), _ptr(n_unique_out), *_ws_args(workspace), _stream(stream)),
+           "ngram_grad_e1")
+    return grad_tokens_out, grad_out, n_unique_out
+
+
+def ngram_grad_gate(rows, dout, eN, grad_Wg_out=None, workspace=None, stream=None):
+    _dev(rows, _I32T, "rows")
+    _dev(dout, _BF16, "dout")
+    _dev(eN, _F32, "eN")
+    n, d = eN.shape
+    _need(rows, n * K, "rows")
+    _need(dout, n * d, "dout")
+    grad_Wg_out = torch.empty(d, dtype=torch.float32, device=eN.device) if grad_Wg_out is None else grad_Wg_out
+    _need(grad_Wg_out, d, "grad_Wg_out")
+    workspace = grad_workspace(n, d, eN.device) if workspace is None else workspace
+    _check(lib().ngram_grad_gate(_ptr(rows), _ptr(dout), _ptr(eN), n, d, _ptr(grad_Wg_out), *_ws_args(workspace),
+                                 _stream(stream)), "ngram_grad_gate")
+    return grad_Wg_out

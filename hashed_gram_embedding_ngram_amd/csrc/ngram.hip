@@ -693,6 +693,269 @@ __global__ void __launch_bounds__(256) select_kernel(const int32_t* counts, int6
 }
 
 // ---------------------------------------------------------------------------
+// Gradients (the forward's chain rule, bf16 output rounding passed through):
+// a stable LSD radix sort of (key, position) pairs groups equal row ids (or
+// token ids) with their positions still ascending, then a segmented reduce
+// sums each group in that fixed order.  No floating-point atomics, so every
+// result is reproducible bit for bit.
+constexpr int kSortItems = 8;                  // items per thread
+constexpr int kSortTile = 256 * kSortItems;    // 2048 items per 256-thread tile
+constexpr int kScanTile = 4096;                // 1024 threads x 4 items
+
+__global__ void __launch_bounds__(256) radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t N, int shift,
+                                                         uint32_t* __restrict__ block_hist, int64_t nblocks) {
+    __shared__ uint32_t h[256];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kSortTile;
+    for (int q = 0; q < kSortItems; ++q) {
+        const int64_t idx = tile0 + q * 256 + threadIdx.x;
+        if (idx < N) atomicAdd(&h[(keys[idx] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    block_hist[static_cast<int64_t>(threadIdx.x) * nblocks + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter of one 8-bit digit.  Tile order is (wavefront, round, lane):
+// an item's rank among equal digits of its tile = equal digits in earlier
+// wavefronts + in earlier rounds of its wavefront + in lower lanes of its
+// round (lanes with an equal digit found by eight ballots).
+__global__ void __launch_bounds__(256) radix_scatter_kernel(const uint32_t* __restrict__ kin,
+                                                            const int32_t* __restrict__ vin, int64_t N, int shift,
+                                                            const uint32_t* __restrict__ offs, int64_t nblocks,
+                                                            uint32_t* __restrict__ kout, int32_t* __restrict__ vout) {
+    __shared__ uint32_t cnt[4][256];
+    __shared__ uint32_t wpre[4][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int q = threadIdx.x; q < 4 * 256; q += 256) (&cnt[0][0])[q] = 0;
+    __syncthreads();
+    const int64_t base0 = static_cast<int64_t>(blockIdx.x) * kSortTile + w * (64 * kSortItems);
+    const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    uint32_t key[kSortItems], local[kSortItems];
+    int32_t val[kSortItems];
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int64_t idx = base0 + r * 64 + lane;
+        const bool active = idx < N;
+        key[r] = active ? kin[idx] : 0u;
+        val[r] = active ? vin[idx] : 0;
+        const uint32_t dg = (key[r] >> shift) & 255u;
+        uint64_t same = __ballot(active);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (dg >> b) & 1u;
+            const uint64_t m = __ballot(active && bit);
+            same &= bit ? m : ~m;
+        }
+        const uint32_t rank = static_cast<uint32_t>(__popcll(same & lower));
+        uint32_t before = 0;
+        if (active) before = cnt[w][dg];
+        if (active && rank == 0) cnt[w][dg] = before + static_cast<uint32_t>(__popcll(same));
+        local[r] = before + rank;
+    }
+    __syncthreads();
+    {
+        uint32_t acc = 0;
+        for (int ww = 0; ww < 4; ++ww) {
+            wpre[ww][threadIdx.x] = acc;
+            acc += cnt[ww][threadIdx.x];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int64_t idx = base0 + r * 64 + lane;
+        if (idx < N) {
+            const uint32_t dg = (key[r] >> shift) & 255u;
+            const uint32_t pos = offs[static_cast<int64_t>(dg) * nblocks + blockIdx.x] + wpre[w][dg] + local[r];
+            kout[pos] = key[r];
+            vout[pos] = val[r];
+        }
+    }
+}
+
+// Exclusive scan of M uint32 (tiles of 4096; tile totals to `tile_sums`).
+__global__ void __launch_bounds__(1024) scan_tiles_kernel(const uint32_t* in, uint32_t* out, int64_t M,
+                                                          uint32_t* tile_sums) {
+    __shared__ uint32_t wsum[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile + threadIdx.x * 4;
+    uint32_t v[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[q] = base + q < M ? in[base + q] : 0u;
+        s += v[q];
+    }
+    uint32_t x = s;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t t = lane < 16 ? wsum[lane] : 0u;
+        for (int off = 1; off < 16; off <<= 1) {
+            const uint32_t y = __shfl_up(t, off);
+            if (lane >= off) t += y;
+        }
+        if (lane < 16) wsum[lane] = t;
+    }
+    __syncthreads();
+    uint32_t prefix = (wave > 0 ? wsum[wave - 1] : 0u) + x - s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (base + q < M) out[base + q] = prefix;
+        prefix += v[q];
+    }
+    if (threadIdx.x == 0 && tile_sums) tile_sums[blockIdx.x] = wsum[15];
+}
+
+__global__ void __launch_bounds__(256) scan_add_kernel(uint32_t* out, int64_t M, const uint32_t* tile_prefix) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x + kScanTile;
+    if (i < M) out[i] += tile_prefix[i / kScanTile];
+}
+
+__global__ void __launch_bounds__(256) sort_init_kernel(const int32_t* __restrict__ ids, int64_t N, int stride,
+                                                        const int32_t* __restrict__ valid_rows, uint32_t limit,
+                                                        uint32_t* __restrict__ keys, int32_t* __restrict__ vals) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= N) return;
+    const int32_t id = ids[t];
+    bool ok = id >= 0 && static_cast<uint32_t>(id) < limit;
+    if (valid_rows) ok = ok && valid_rows[t * stride] >= 0;
+    keys[t] = ok ? static_cast<uint32_t>(id) : limit;
+    vals[t] = static_cast<int32_t>(t);
+}
+
+__global__ void __launch_bounds__(256) seg_flags_kernel(const uint32_t* keys, int64_t N, uint32_t limit, uint32_t* flags) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= N) return;
+    const uint32_t k = keys[t];
+    flags[t] = (k < limit && (t == 0 || keys[t - 1] != k)) ? 1u : 0u;
+}
+
+// seg[t]: exclusive scan of the flags.  Writes each group's first index, its
+// id, the end sentinel and the group count.
+__global__ void __launch_bounds__(256) seg_bounds_kernel(const uint32_t* keys, const uint32_t* seg, int64_t N,
+                                                         uint32_t limit, int32_t* seg_start, int32_t* ids_out,
+                                                         int64_t* n_unique) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= N) return;
+    const uint32_t k = keys[t];
+    if (k >= limit) return;
+    const bool first = t == 0 || keys[t - 1] != k;
+    if (first) {
+        seg_start[seg[t]] = static_cast<int32_t>(t);
+        ids_out[seg[t]] = static_cast<int32_t>(k);
+    }
+    if (t + 1 == N || keys[t + 1] >= limit) {
+        const uint32_t U = seg[t] + (first ? 1u : 0u);
+        seg_start[U] = static_cast<int32_t>(t + 1);
+        *n_unique = U;
+    }
+}
+
+__global__ void __launch_bounds__(64) set_i64_kernel(int64_t* p, int64_t v) {
+    if (threadIdx.x == 0) *p = v;
+}
+
+// One workgroup per group (persistent), one wavefront per 512-column slice:
+// acc = fmaf(W_g, g[i], acc) (table) or acc + g[i] (e1) over the group's
+// positions in ascending order, i = position >> pos_shift.
+template <bool WEIGHT>
+__global__ void __launch_bounds__(1024) seg_reduce_kernel(const int32_t* __restrict__ seg_start,
+                                                          const int64_t* __restrict__ n_unique,
+                                                          const int32_t* __restrict__ sorted_pos, int pos_shift,
+                                                          const uint16_t* __restrict__ g, const float* __restrict__ W,
+                                                          int32_t d, float* __restrict__ out) {
+    const int64_t U = *n_unique;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int nslices = (d + kSlice - 1) / kSlice;
+    for (int64_t u = blockIdx.x; u < U; u += gridDim.x) {
+        const int32_t s0 = seg_start[u], s1 = seg_start[u + 1];
+        for (int sl = wave; sl < nslices; sl += nwaves) {
+            const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+            if (j0 >= d) continue;
+            float w[8];
+            if (WEIGHT) load_w8(w, W, j0);
+            float acc[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+            int32_t t = s0;
+            for (; t + 4 <= s1; t += 4) {
+                uint4 gv[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(sorted_pos[t + m]) >> pos_shift);
+                    gv[m] = *reinterpret_cast<const uint4*>(g + i * d + j0);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float x[8] = {bf16lo(gv[m].x), bf16hi(gv[m].x), bf16lo(gv[m].y), bf16hi(gv[m].y),
+                                        bf16lo(gv[m].z), bf16hi(gv[m].z), bf16lo(gv[m].w), bf16hi(gv[m].w)};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[q] = WEIGHT ? __builtin_fmaf(w[q], x[q], acc[q]) : acc[q] + x[q];
+                }
+            }
+            for (; t < s1; ++t) {
+                const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(sorted_pos[t]) >> pos_shift);
+                const uint4 gv = *reinterpret_cast<const uint4*>(g + i * d + j0);
+                const float x[8] = {bf16lo(gv.x), bf16hi(gv.x), bf16lo(gv.y), bf16hi(gv.y),
+                                    bf16lo(gv.z), bf16hi(gv.z), bf16lo(gv.w), bf16hi(gv.w)};
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = WEIGHT ? __builtin_fmaf(w[q], x[q], acc[q]) : acc[q] + x[q];
+            }
+            float* o = out + u * d + j0;
+            reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+    }
+}
+
+// dW_g: per chunk of 256 tokens, part = fmaf(g, eN, part) in ascending token
+// order (skipping invalid tokens); then the chunk parts summed in order.
+constexpr int kGateChunk = 256;
+
+__global__ void __launch_bounds__(1024) gate_grad_partial_kernel(const int32_t* __restrict__ rows,
+                                                                 const uint16_t* __restrict__ g,
+                                                                 const float* __restrict__ eN, int64_t n, int32_t d,
+                                                                 float* __restrict__ partials) {
+    const int64_t c = blockIdx.x;
+    const int64_t i0 = c * kGateChunk;
+    const int64_t i1 = i0 + kGateChunk < n ? i0 + kGateChunk : n;
+    for (int64_t j0 = static_cast<int64_t>(threadIdx.x) * kVec; j0 < d; j0 += static_cast<int64_t>(blockDim.x) * kVec) {
+        float part[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) part[q] = 0.0f;
+        for (int64_t i = i0; i < i1; ++i) {
+            if (rows[i * kK] < 0) continue;
+            const uint4 gv = *reinterpret_cast<const uint4*>(g + i * d + j0);
+            const float4 e0 = reinterpret_cast<const float4*>(eN + i * d + j0)[0];
+            const float4 e1v = reinterpret_cast<const float4*>(eN + i * d + j0)[1];
+            const float x[8] = {bf16lo(gv.x), bf16hi(gv.x), bf16lo(gv.y), bf16hi(gv.y),
+                                bf16lo(gv.z), bf16hi(gv.z), bf16lo(gv.w), bf16hi(gv.w)};
+            const float e[8] = {e0.x, e0.y, e0.z, e0.w, e1v.x, e1v.y, e1v.z, e1v.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) part[q] = __builtin_fmaf(x[q], e[q], part[q]);
+        }
+        float* o = partials + c * d + j0;
+        reinterpret_cast<float4*>(o)[0] = make_float4(part[0], part[1], part[2], part[3]);
+        reinterpret_cast<float4*>(o)[1] = make_float4(part[4], part[5], part[6], part[7]);
+    }
+}
+
+__global__ void __launch_bounds__(256) gate_grad_total_kernel(const float* __restrict__ partials, int64_t nchunks,
+                                                              int32_t d, float* __restrict__ out) {
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (j >= d) return;
+    float total = 0.0f;
+    for (int64_t c = 0; c < nchunks; ++c) total = total + partials[c * d + j];
+    out[j] = total;
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 int env_int(const char* name, int dflt) {
     const char* v = getenv(name);
@@ -841,6 +1104,100 @@ int check_pool(const ngram_table* T, const ngram_row_pool* P) {
     if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE && !P->row_scale) return fail(NGRAM_EINVAL, "int8 pool needs row_scale");
     if (P->pool_rows < 0 || P->pool_rows > NGRAM_MAX_ROWS) return fail(NGRAM_ERANGE, "pool_rows out of range");
     return NGRAM_OK;
+}
+
+// Workspace of the gradient calls, for N = 16 n sort items (the table) and
+// the gate's chunk partials.
+struct GradLayout {
+    int64_t N, nblocks, keysA, valsA, keysB, valsB, flags, segs, hist, tiles, parts, total;
+};
+
+GradLayout grad_layout(int64_t n, int32_t d) {
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t{255}; };
+    GradLayout L;
+    L.N = kK * n;
+    L.nblocks = (L.N + kSortTile - 1) / kSortTile;
+    int64_t o = 0;
+    L.keysA = o; o = up(o + 4 * L.N);
+    L.valsA = o; o = up(o + 4 * L.N);
+    L.keysB = o; o = up(o + 4 * L.N);
+    L.valsB = o; o = up(o + 4 * L.N);
+    L.flags = o; o = up(o + 4 * L.N);
+    L.segs = o; o = up(o + 4 * (L.N + 1));
+    L.hist = o; o = up(o + 4 * 256 * (L.nblocks > 0 ? L.nblocks : 1));
+    L.tiles = o; o = up(o + 4 * 2 * kScanTile);
+    L.parts = o; o = up(o + 4 * ((n + kGateChunk - 1) / kGateChunk) * static_cast<int64_t>(d > 0 ? d : 1));
+    L.total = o;
+    return L;
+}
+
+// Exclusive scan of M <= 4096^2 uint32 values, in place allowed.
+void scan_u32(const uint32_t* in, uint32_t* out, int64_t M, uint32_t* tiles, hipStream_t st) {
+    const int64_t ntiles = (M + kScanTile - 1) / kScanTile;
+    hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(1024), 0, st, in, out, M, tiles);
+    if (ntiles > 1) {
+        hipLaunchKernelGGL(scan_tiles_kernel, dim3(1), dim3(1024), 0, st, tiles, tiles + kScanTile, ntiles,
+                           static_cast<uint32_t*>(nullptr));
+        const int64_t rest = M - kScanTile;
+        hipLaunchKernelGGL(scan_add_kernel, dim3(static_cast<unsigned>((rest + 255) / 256)), dim3(256), 0, st, out, M,
+                           tiles + kScanTile);
+    }
+}
+
+// Stable sort of N (key, value) pairs by key (keys <= limit), ping-ponging
+// between the A and B buffers; returns the buffers that hold the result.
+void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStream_t st, uint32_t** keys_out,
+                int32_t** vals_out) {
+    uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.keysA);
+    int32_t* vA = reinterpret_cast<int32_t*>(ws + L.valsA);
+    uint32_t* kB = reinterpret_cast<uint32_t*>(ws + L.keysB);
+    int32_t* vB = reinterpret_cast<int32_t*>(ws + L.valsB);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
+    const int64_t nblocks = (N + kSortTile - 1) / kSortTile;
+    int bits = 1;
+    while (bits < 32 && (limit >> bits) != 0) ++bits;
+    const int passes = (bits + 7) / 8;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        hipLaunchKernelGGL(radix_hist_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st, kA, N, shift,
+                           hist, nblocks);
+        scan_u32(hist, hist, 256 * nblocks, tiles, st);
+        hipLaunchKernelGGL(radix_scatter_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st, kA, vA, N,
+                           shift, hist, nblocks, kB, vB);
+        uint32_t* tk = kA; kA = kB; kB = tk;
+        int32_t* tv = vA; vA = vB; vB = tv;
+    }
+    *keys_out = kA;
+    *vals_out = vA;
+}
+
+// Sort, find the groups of equal ids and reduce each group in position order.
+template <bool WEIGHT>
+int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* valid_rows, uint32_t limit, int pos_shift,
+                   const uint16_t* g, const float* W, int32_t d, int32_t* ids_out, float* grad_out, int64_t* n_unique,
+                   void* workspace, const GradLayout& L, hipStream_t st) {
+    char* ws = static_cast<char*>(workspace);
+    hipLaunchKernelGGL(set_i64_kernel, dim3(1), dim3(64), 0, st, n_unique, int64_t{0});
+    if (N == 0) return hip_status("gradient launch");
+    uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.keysA);
+    int32_t* vA = reinterpret_cast<int32_t*>(ws + L.valsA);
+    const unsigned gN = static_cast<unsigned>((N + 255) / 256);
+    hipLaunchKernelGGL(sort_init_kernel, dim3(gN), dim3(256), 0, st, ids, N, stride, valid_rows, limit, kA, vA);
+    uint32_t* keys = nullptr;
+    int32_t* pos = nullptr;
+    radix_sort(ws, L, N, limit, st, &keys, &pos);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+    int32_t* segs = reinterpret_cast<int32_t*>(ws + L.segs);
+    hipLaunchKernelGGL(seg_flags_kernel, dim3(gN), dim3(256), 0, st, keys, N, limit, flags);
+    scan_u32(flags, flags, N, reinterpret_cast<uint32_t*>(ws + L.tiles), st);
+    hipLaunchKernelGGL(seg_bounds_kernel, dim3(gN), dim3(256), 0, st, keys, flags, N, limit, segs, ids_out, n_unique);
+    const int nslices = (d + kSlice - 1) / kSlice;
+    const int waves = nslices < 16 ? nslices : 16;
+    int64_t grid = N < 16384 ? N : 16384;
+    hipLaunchKernelGGL(seg_reduce_kernel<WEIGHT>, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, segs,
+                       n_unique, pos, pos_shift, g, W, d, grad_out);
+    return hip_status("gradient launch");
 }
 
 void cap_for_host(Shape& sh, const ngram_table* T) {
@@ -1203,6 +1560,75 @@ int ngram_select_hot_rows(const int32_t* counts, int64_t R, int64_t C, int32_t* 
     if (e != hipSuccess) return fail(NGRAM_EHIP, "reading the selection count: %s", hipGetErrorString(e));
     *selected = got < static_cast<uint64_t>(C) ? static_cast<int64_t>(got) : C;
     return NGRAM_OK;
+}
+
+int64_t ngram_grad_workspace_bytes(int64_t n, int32_t d) {
+    if (n < 0 || d <= 0) return -1;
+    return grad_layout(n, d).total;
+}
+
+static int check_grad_common(int64_t n, int32_t d, const uint16_t* dout, void* workspace, int64_t workspace_bytes) {
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    // two-level scans of at most 4096^2 entries: 16 n <= 2^24
+    if (n > (1 << 20)) return fail(NGRAM_ERANGE, "n=%lld above 2^20", (long long)n);
+    if (d <= 0 || d % kVec != 0) return fail(NGRAM_EINVAL, "d=%d must be a positive multiple of 8", d);
+    if (d > NGRAM_MAX_D) return fail(NGRAM_ERANGE, "d=%d above %d", d, NGRAM_MAX_D);
+    if (n > 0 && (!dout || !aligned(dout, 16))) return fail(NGRAM_EINVAL, "dout is NULL or not 16-byte aligned");
+    const int64_t need = grad_layout(n, d).total;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+        return fail(NGRAM_EINVAL, "workspace needs %lld bytes, 256-byte aligned", (long long)need);
+    return NGRAM_OK;
+}
+
+int ngram_grad_table(const int32_t* rows, int64_t n, int32_t d, int64_t R, const float* W_g, const uint16_t* dout,
+                     int32_t* grad_rows_out, float* grad_out, int64_t* n_unique_out, void* workspace,
+                     int64_t workspace_bytes, ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_grad_common(n, d, dout, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (R < 1 || R > NGRAM_MAX_ROWS) return fail(NGRAM_ERANGE, "R=%lld outside [1, 2^31-1]", (long long)R);
+    if (!n_unique_out || !W_g || !aligned(W_g, 16)) return fail(NGRAM_EINVAL, "n_unique_out or W_g is NULL/misaligned");
+    if (n > 0 && (!rows || !grad_rows_out || !grad_out || !aligned(grad_out, 16)))
+        return fail(NGRAM_EINVAL, "rows, grad_rows_out or grad_out is NULL/misaligned");
+    const GradLayout L = grad_layout(n, d);
+    return grad_by_groups<true>(rows, kK * n, 0, nullptr, static_cast<uint32_t>(R), 4, dout, W_g, d, grad_rows_out,
+                                grad_out, n_unique_out, workspace, L, stream);
+}
+
+int ngram_grad_e1(const int32_t* tokens, const int32_t* rows, int64_t n, int32_t d, int64_t V, const uint16_t* dout,
+                  int32_t* grad_tokens_out, float* grad_out, int64_t* n_unique_out, void* workspace,
+                  int64_t workspace_bytes, ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_grad_common(n, d, dout, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (V < 1 || V > static_cast<int64_t>(kPad)) return fail(NGRAM_ERANGE, "V=%lld outside [1, 2^21-1]", (long long)V);
+    if (!n_unique_out) return fail(NGRAM_EINVAL, "n_unique_out is NULL");
+    if (n > 0 && (!tokens || !rows || !grad_tokens_out || !grad_out || !aligned(grad_out, 16)))
+        return fail(NGRAM_EINVAL, "tokens, rows, grad_tokens_out or grad_out is NULL/misaligned");
+    const GradLayout L = grad_layout(n, d);
+    return grad_by_groups<false>(tokens, n, kK, rows, static_cast<uint32_t>(V), 0, dout, nullptr, d, grad_tokens_out,
+                                 grad_out, n_unique_out, workspace, L, stream);
+}
+
+int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, int64_t n, int32_t d,
+                    float* grad_Wg_out, void* workspace, int64_t workspace_bytes, ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_grad_common(n, d, dout, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (!grad_Wg_out) return fail(NGRAM_EINVAL, "grad_Wg_out is NULL");
+    if (n > 0 && (!rows || !eN || !aligned(eN, 16))) return fail(NGRAM_EINVAL, "rows or eN is NULL/misaligned");
+    const GradLayout L = grad_layout(n, d);
+    float* parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.parts);
+    const int64_t nchunks = (n + kGateChunk - 1) / kGateChunk;
+    if (nchunks > 0) {
+        int threads = ((d / kVec) + 63) / 64 * 64;
+        if (threads > 1024) threads = 1024;
+        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks)), dim3(threads), 0, stream,
+                           rows, dout, eN, n, d, parts);
+    }
+    hipLaunchKernelGGL(gate_grad_total_kernel, dim3(static_cast<unsigned>((d + 255) / 256)), dim3(256), 0, stream,
+                       parts, nchunks, d, grad_Wg_out);
+    return hip_status("ngram_grad_gate launch");
 }
 
 }  // extern "C"

@@ -220,6 +220,46 @@ int ngram_select_hot_rows(const int32_t* counts, int64_t R, int64_t C, int32_t* 
                           int64_t* selected, void* workspace, int64_t workspace_bytes,
                           ngram_stream_t stream);
 
+/* Gradients of a learned table ("Qwen Brought Back N-Grams…", section
+ * "N-grams, of all things": "a learned, hash-addressed embedding table").  The
+ * pages define only the forward; these follow from it by the chain rule, with
+ * the bf16 output rounding passed straight through.  dout = dL/dout, bf16
+ * [n][d]; rows = the forward's row ids [n][16] (a token whose ids are -1 or
+ * outside [0, R) contributes nothing).  Each sum runs in a fixed order, so
+ * every result is reproducible bit for bit, with no floating-point atomics:
+ * the ids are grouped by a stable radix sort that keeps positions ascending.
+ * Workspace: ngram_grad_workspace_bytes(n, d) bytes of device memory,
+ * 256-byte aligned, shared by the three calls.  n <= 2^20 (ERANGE). */
+int64_t ngram_grad_workspace_bytes(int64_t n, int32_t d);
+
+/* Table gradient, sparse: for each distinct valid row id r in ascending order
+ * u = 0, 1, …: grad_rows_out[u] = r and grad_out[u][j] = acc over positions
+ * t = 16 i + k with rows[t] == r, ascending t, of acc = fmaf(W_g[j],
+ * dout[i][j], acc) from +0.  *n_unique_out (device int64) = the number of
+ * rows.  grad_rows_out holds 16 n int32, grad_out 16 n x d fp32 (16-byte
+ * aligned); entries from *n_unique_out on are unspecified. */
+int ngram_grad_table(const int32_t* rows, int64_t n, int32_t d, int64_t R, const float* W_g,
+                     const uint16_t* dout, int32_t* grad_rows_out, float* grad_out,
+                     int64_t* n_unique_out, void* workspace, int64_t workspace_bytes,
+                     ngram_stream_t stream);
+
+/* e1 gradient, sparse: for each distinct token v in [0, V) of a valid
+ * position, ascending: grad_tokens_out[u] = v, grad_out[u][j] = acc over
+ * tokens i with tokens[i] == v, ascending i, of acc = acc + dout[i][j] from
+ * +0.  grad_tokens_out holds n int32, grad_out n x d fp32. */
+int ngram_grad_e1(const int32_t* tokens, const int32_t* rows, int64_t n, int32_t d, int64_t V,
+                  const uint16_t* dout, int32_t* grad_tokens_out, float* grad_out,
+                  int64_t* n_unique_out, void* workspace, int64_t workspace_bytes,
+                  ngram_stream_t stream);
+
+/* Gate gradient: grad_Wg_out[j] = sum over chunks of 256 tokens, in order, of
+ * the chunk's acc = fmaf(dout[i][j], eN[i][j], acc) over its valid tokens in
+ * ascending i, from +0.  eN [n][d] fp32 is the forward's sum (ngram_embed_bag);
+ * grad_Wg_out [d] fp32. */
+int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, int64_t n, int32_t d,
+                    float* grad_Wg_out, void* workspace, int64_t workspace_bytes,
+                    ngram_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -203,3 +203,23 @@ def test_count_and_select_argument_checks():
     assert L.ngram_select_hot_rows(A, 100, 10, A, None, A, W, None) == EINVAL
     assert L.ngram_select_hot_rows(A, 100, 10, A, ctypes.byref(sel), A, 64, None) == EINVAL
     assert L.ngram_select_hot_rows(A, 100, 0, None, ctypes.byref(sel), A, W, None) == OK and sel.value == 0
+
+
+def test_grad_argument_checks():
+    L = ng.lib()
+    W = L.ngram_grad_workspace_bytes(4, 64)
+    assert W > 0 and L.ngram_grad_workspace_bytes(-1, 64) == -1 and L.ngram_grad_workspace_bytes(4, 0) == -1
+    AW = 0x100000                                          # 256-byte aligned
+    assert L.ngram_grad_table(A, -1, 64, 100, A, A, A, A, A, AW, W, None) == EINVAL
+    assert L.ngram_grad_table(A, 2**20 + 1, 64, 100, A, A, A, A, A, AW, W, None) == ERANGE
+    assert L.ngram_grad_table(A, 4, 12, 100, A, A, A, A, A, AW, W, None) == EINVAL
+    assert L.ngram_grad_table(A, 4, 64, 0, A, A, A, A, A, AW, W, None) == ERANGE
+    assert L.ngram_grad_table(A, 4, 64, 100, A, A, A, A, A, AW + 16, W, None) == EINVAL
+    assert L.ngram_grad_table(A, 4, 64, 100, A, A, A, A, A, AW, W - 1, None) == EINVAL
+    assert L.ngram_grad_table(A, 4, 64, 100, None, A, A, A, A, AW, W, None) == EINVAL
+    assert L.ngram_grad_table(A, 4, 64, 100, A, A + 2, A, A, A, AW, W, None) == EINVAL
+    assert L.ngram_grad_e1(A, A, 4, 64, 0, A, A, A, A, AW, W, None) == ERANGE
+    assert L.ngram_grad_e1(A, A, 4, 64, 2**21, A, A, A, A, AW, W, None) == ERANGE
+    assert L.ngram_grad_e1(A, A, 4, 64, 100, A, A, A, None, AW, W, None) == EINVAL
+    assert L.ngram_grad_gate(A, A, A, 4, 64, None, AW, W, None) == EINVAL
+    assert L.ngram_grad_gate(A, A, A + 4, 4, 64, A, AW, W, None) == EINVAL

@@ -1,0 +1,134 @@
+"""GPU gradients against the oracle, bit for bit: the distinct row and token
+lists (ascending) and every fp32 gradient value."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import hashed_gram_embedding_ngram_amd as ng  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from tests.test_gpu_parity import say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(lengths, R, V, d, seed, kind=synth.KIND_BF16_WIDE, bad=()):
+    offs = synth.ragged_offsets(lengths)
+    n = int(offs[-1])
+    toks = synth.tokens(seed, n, V, 1.1)
+    rows = oracle.hash_rows(toks, offs, R)
+    for b in bad:
+        rows[b] = -1
+    g = synth.tensor(kind, seed, synth.TAG_RESIDUAL, n * d).reshape(n, d)
+    W = synth.as_f32(synth.tensor(synth.KIND_F32_UNIT, seed, synth.TAG_WG, d))
+    return toks, rows, g, W
+
+
+def _dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a).view(dt) if a.dtype != dt else a).to("cuda:0")
+
+
+@pytest.mark.parametrize("lengths,R,d,bad", [
+    ((40, 0, 57), 61, 64, ()),              # long groups, ragged unroll tails
+    ((300, 7), 100_003, 520, (3, 17)),      # invalid tokens, ragged slices
+    ((2000,), 4001, 2560, ()),              # two-level scans (32000 sort items)
+    ((1,), 7, 8, ()),
+])
+def test_table_grad(lengths, R, d, bad):
+    say(f"grad table {lengths} R={R} d={d}")
+    toks, rows, g, W = _inputs(lengths, R, 151936, d, seed=len(lengths) + R, bad=bad)
+    gr, gv, nu = ng.ngram_grad_table(_dev(rows, np.int32), _dev(W, np.float32), _dev(g.view(np.int16), np.int16), R)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    q, want = oracle.grad_table(rows, W, g)
+    assert U == q.size
+    assert np.array_equal(gr.cpu().numpy()[:U], q)
+    assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
+
+
+def test_table_grad_many_items_sampled():
+    """70000 tokens (1.12M sort items, multi-tile histogram scans): the
+    distinct-row list in full, gradients of sampled rows (the most frequent
+    ones and random ones)."""
+    n, R, d = 70_000, 2_000_003, 64
+    say("grad table 70000 tokens")
+    toks, rows, g, W = _inputs((n,), R, 151936, d, seed=5)
+    gr, gv, nu = ng.ngram_grad_table(_dev(rows, np.int32), _dev(W, np.float32), _dev(g.view(np.int16), np.int16), R)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    uniq, cnt = np.unique(rows, return_counts=True)
+    assert U == uniq.size and np.array_equal(gr.cpu().numpy()[:U], uniq)
+    rng = np.random.default_rng(1)
+    pick = np.unique(np.concatenate([np.argsort(-cnt)[:20], rng.integers(0, U, 30)]))
+    _, want = oracle.grad_table(rows, W, g, query=uniq[pick])
+    assert np.array_equal(gv.cpu().numpy()[pick].view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("lengths,V,d,bad", [((40, 0, 57), 13, 64, ()), ((300, 7), 1024, 520, (3, 17)),
+                                             ((5000,), 151936, 128, ())])
+def test_e1_grad(lengths, V, d, bad):
+    say(f"grad e1 {lengths} V={V}")
+    toks, rows, g, W = _inputs(lengths, 4096, V, d, seed=7, bad=bad)
+    gt, gv, nu = ng.ngram_grad_e1(_dev(toks, np.int32), _dev(rows, np.int32), _dev(g.view(np.int16), np.int16), V)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    q, want = oracle.grad_e1(toks, rows, g)
+    assert U == q.size
+    assert np.array_equal(gt.cpu().numpy()[:U], q)
+    assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,d", [(1, 8), (255, 64), (257, 64), (1000, 2560)])
+def test_gate_grad(n, d):
+    say(f"grad gate n={n} d={d}")
+    toks, rows, g, W = _inputs((n,), 4096, 1024, d, seed=9)
+    rows[n // 2] = -1
+    eN = synth.as_f32(synth.tensor(synth.KIND_F32_UNIT, 11, synth.TAG_TABLE, n * d)).reshape(n, d) - 0.5
+    eN = eN.astype(np.float32)
+    eN[n // 2] = np.nan                      # an invalid token's sum is never read
+    gw = ng.ngram_grad_gate(_dev(rows, np.int32), _dev(g.view(np.int16), np.int16), _dev(eN, np.float32))
+    torch.cuda.synchronize()
+    want = oracle.grad_gate(rows, g, eN)
+    assert np.array_equal(gw.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_empty_grads():
+    z = torch.zeros((0, 16), dtype=torch.int32, device="cuda:0")
+    gr, gv, nu = ng.ngram_grad_table(z, torch.ones(8, device="cuda:0"), torch.zeros((0, 8), dtype=torch.int16,
+                                                                                   device="cuda:0"), 10)
+    torch.cuda.synchronize()
+    assert int(nu.item()) == 0
+
+
+def test_full_prefill_backward_sampled():
+    """Prefill shape (8 x 4096 tokens, R = 20M, d = 2560): table, e1 and gate
+    gradients of sampled rows / tokens / all columns, bit-exact."""
+    from synth.workloads import CONFIGS, HostInputs
+    sp = CONFIGS["prefill"]
+    say("grad prefill shape")
+    h = HostInputs(sp)
+    rows = oracle.hash_rows(h.tokens, h.offsets, sp.R)
+    n, d = sp.n, sp.d
+    g = synth.tensor(synth.KIND_BF16_NORMAL6, 3, synth.TAG_RESIDUAL, n * d).reshape(n, d)
+    W = h.W_g
+    t_rows = _dev(rows, np.int32)
+    t_g = _dev(g.view(np.int16), np.int16)
+    gr, gv, nu = ng.ngram_grad_table(t_rows, _dev(W, np.float32), t_g, sp.R)
+    gt, ge, nt = ng.ngram_grad_e1(_dev(h.tokens, np.int32), t_rows, t_g, sp.V)
+    eN = (synth.as_f32(synth.tensor(synth.KIND_F32_UNIT, 4, synth.TAG_TABLE, n * d)).reshape(n, d) - 0.5).astype(np.float32)
+    gw = ng.ngram_grad_gate(t_rows, t_g, _dev(eN, np.float32))
+    torch.cuda.synchronize()
+    uniq, cnt = np.unique(rows, return_counts=True)
+    U = int(nu.item())
+    assert U == uniq.size and np.array_equal(gr.cpu().numpy()[:U], uniq)
+    rng = np.random.default_rng(2)
+    pick = np.unique(np.concatenate([np.argsort(-cnt)[:8], rng.integers(0, U, 8)]))
+    _, want = oracle.grad_table(rows, W, g, query=uniq[pick])
+    assert np.array_equal(gv[torch.from_numpy(pick).cuda()].cpu().numpy().view(np.uint32), want.view(np.uint32))
+    ut = np.unique(h.tokens)
+    assert int(nt.item()) == ut.size and np.array_equal(gt.cpu().numpy()[:ut.size], ut)
+    tp = np.unique(np.concatenate([[0, 1, 2], rng.integers(0, ut.size, 8)]))
+    _, want_e = oracle.grad_e1(h.tokens, rows, g, query=ut[tp])
+    assert np.array_equal(ge[torch.from_numpy(tp).cuda()].cpu().numpy().view(np.uint32), want_e.view(np.uint32))
+    assert np.array_equal(gw.cpu().numpy().view(np.uint32), oracle.grad_gate(rows, g, eN).view(np.uint32))
