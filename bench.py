@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "int8", "decode1", "decode2", "decode4", "host"])
+                    choices=["prefill", "int8", "decode1", "decode2", "decode4", "host", "backward"])
     ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged", "pool"],
                     help="host workload: sum straight from pinned memory, stage rows in HBM first, or go "
                          "through an HBM row pool (hot-row cache + per-batch dedup)")
@@ -193,6 +193,9 @@ def main():
 
     if args.workload == "host":
         run_host(args)
+        return
+    if args.workload == "backward":
+        run_backward(args)
         return
 
     dev = torch.device("cuda:0")
@@ -346,6 +349,80 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def backward_bytes_per_token(d: int, rows_per_token_unique: float, tokens_unique: float) -> float:
+    """Algorithmic HBM bytes of one backward step per token: the 16 reads of
+    its dL/dout row by the table's segmented reduce (16 x 2d), its share of
+    the fp32 table-gradient rows written (unique rows per token x 4d), the
+    e1 reduce's read of dL/dout (2d) and write of unique-token rows
+    (x 4d), and the gate gradient's read of dL/dout and eN (2d + 4d)."""
+    return 16 * 2 * d + rows_per_token_unique * 4 * d + 2 * d + tokens_unique * 4 * d + 6 * d
+
+
+def run_backward(args):
+    """Gradients of one prefill batch (8 x 4096 tokens, R = 20M, d = 2560):
+    ngram_grad_table + ngram_grad_e1 + ngram_grad_gate, from the forward's
+    row ids and sums and a synthetic bf16 dL/dout."""
+    import numpy as np
+    import torch
+
+    import hashed_gram_embedding_ngram_amd as ng
+    import synth
+    from synth.workloads import CONFIGS, HostInputs
+
+    dev = torch.device("cuda:0")
+    spec = CONFIGS["prefill"].replace(dist=args.dist)
+    n, d, R = spec.n, spec.d, spec.R
+    h = HostInputs(spec)
+    tok = torch.from_numpy(h.tokens).to(dev)
+    off = torch.from_numpy(h.offsets).to(dev)
+    W = torch.from_numpy(h.W_g).to(dev)
+    table = synth.fill_gpu(spec.table_kind, spec.seed, synth.TAG_TABLE, torch.empty(R * d, dtype=torch.int16, device=dev))
+    rows = ng.ngram_hash(tok, off, R)
+    eN = ng.ngram_embed_bag(ng.Table(table, R, d), rows)
+    del table
+    g = synth.fill_gpu(synth.KIND_BF16_NORMAL6, 77, synth.TAG_RESIDUAL, torch.empty(n * d, dtype=torch.int16, device=dev))
+    ws = ng.grad_workspace(n, d, dev)
+    gr = torch.empty(n * 16, dtype=torch.int32, device=dev)
+    gt = torch.empty((n * 16, d), dtype=torch.float32, device=dev)
+    nu = torch.empty(1, dtype=torch.int64, device=dev)
+    et = torch.empty(n, dtype=torch.int32, device=dev)
+    ge = torch.empty((n, d), dtype=torch.float32, device=dev)
+    ne = torch.empty(1, dtype=torch.int64, device=dev)
+    gw = torch.empty(d, dtype=torch.float32, device=dev)
+
+    def step():
+        ng.ngram_grad_table(rows, W, g, R, grad_rows_out=gr, grad_out=gt, n_unique_out=nu, workspace=ws)
+        ng.ngram_grad_e1(tok, rows, g, spec.V, grad_tokens_out=et, grad_out=ge, n_unique_out=ne, workspace=ws)
+        ng.ngram_grad_gate(rows, g, eN, grad_Wg_out=gw, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s_ev.record()
+    for _ in range(args.steps):
+        step()
+    e_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
+    U, Ut = int(nu.item()), int(ne.item())
+    bpt = backward_bytes_per_token(d, U / n, Ut / n)
+    achieved = bpt * n / step_s / 1e9
+    print(json.dumps({
+        "metric": "n-gram backward (table + e1 + gate gradients) tokens/s",
+        "value": n * args.steps / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "backward", "tokens": n, "R": R, "d": d, "K": K_ROWS,
+                   "unique_rows": U, "unique_tokens": Ut},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "backward step",
+                     "algorithmic_bytes_per_token": bpt, "step_us": step_s * 1e6},
+        "cpu_baseline": None}), flush=True)
 
 
 def run_host(args):

@@ -860,54 +860,100 @@ __global__ void __launch_bounds__(64) set_i64_kernel(int64_t* p, int64_t v) {
     if (threadIdx.x == 0) *p = v;
 }
 
-// One workgroup per group (persistent), one wavefront per 512-column slice:
-// acc = fmaf(W_g, g[i], acc) (table) or acc + g[i] (e1) over the group's
-// positions in ascending order, i = position >> pos_shift.
-template <bool WEIGHT>
-__global__ void __launch_bounds__(1024) seg_reduce_kernel(const int32_t* __restrict__ seg_start,
-                                                          const int64_t* __restrict__ n_unique,
-                                                          const int32_t* __restrict__ sorted_pos, int pos_shift,
-                                                          const uint16_t* __restrict__ g, const float* __restrict__ W,
-                                                          int32_t d, float* __restrict__ out) {
+// Workgroup c owns the groups that start among sorted items [64 c, 64 c + 64)
+// and walks their items in order (past the chunk's end for the last group),
+// one wavefront per 512-column slice: acc = fmaf(W_g, g[i], acc) (table) or
+// acc + g[i] (e1), i = position >> pos_shift; a group's sum is stored when
+// the id changes.  The dL/dout rows of the next DEPTH items are loaded ahead
+// (groups can be thousands of items long: a Zipf-hot token's e1 gradient).
+constexpr int kWalkChunk = 64;
+
+template <bool WEIGHT, int DEPTH>
+__global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restrict__ keys,
+                                                        const uint32_t* __restrict__ seg,
+                                                        const int32_t* __restrict__ seg_start,
+                                                        const int64_t* __restrict__ n_unique,
+                                                        const int32_t* __restrict__ sorted_pos, int pos_shift,
+                                                        const uint16_t* __restrict__ g, const float* __restrict__ W,
+                                                        int32_t d, float* __restrict__ out) {
     const int64_t U = *n_unique;
+    if (U == 0) return;
+    const int64_t nvalid = seg_start[U];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWalkChunk;
+    if (t0 >= nvalid) return;
+    // group of item t0 = seg[t0] + flag[t0] - 1; it starts here or earlier
+    const uint32_t k0 = keys[t0];
+    const bool starts = t0 == 0 || keys[t0 - 1] != k0;
+    int64_t u = static_cast<int64_t>(seg[t0]) - (starts ? 0 : 1);
+    if (!starts) ++u;                               // that group belongs to an earlier chunk
+    if (u >= U || seg_start[u] >= t0 + kWalkChunk) return;
+    // last group that starts inside the chunk
+    const int64_t tl = (t0 + kWalkChunk < nvalid ? t0 + kWalkChunk : nvalid) - 1;
+    const bool tl_starts = keys[tl - 1 >= 0 ? tl - 1 : 0] != keys[tl] || tl == 0;
+    const int64_t u_last = static_cast<int64_t>(seg[tl]) - (tl_starts ? 0 : 1);
+    const int64_t t_begin = seg_start[u], t_end = seg_start[u_last + 1];
+
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int nslices = (d + kSlice - 1) / kSlice;
-    for (int64_t u = blockIdx.x; u < U; u += gridDim.x) {
-        const int32_t s0 = seg_start[u], s1 = seg_start[u + 1];
-        for (int sl = wave; sl < nslices; sl += nwaves) {
-            const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
-            if (j0 >= d) continue;
-            float w[8];
-            if (WEIGHT) load_w8(w, W, j0);
-            float acc[8];
+    // The walk stays in uniform control flow: every lane loads its share of
+    // the ids and positions that readlane then reads from any lane.  Lanes
+    // past the row's end work on column 0 and do not store.
+    for (int sl = wave; sl < nslices; sl += nwaves) {
+        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
+        const bool col_ok = j0 < d;
+        const int64_t jc = col_ok ? j0 : 0;
+        float w[8];
+        if (WEIGHT) load_w8(w, W, jc);
+        float acc[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-            int32_t t = s0;
-            for (; t + 4 <= s1; t += 4) {
-                uint4 gv[4];
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        int64_t uo = u;
+        uint32_t prev = keys[t_begin];
+        // ids and positions of 64 items per vector load, the next 64 loaded
+        // while the current ones are walked; lane m of (kl, pl) is item tb + m
+        uint32_t kl = t_begin + lane < t_end ? keys[t_begin + lane] : 0u;
+        int32_t pl = t_begin + lane < t_end ? sorted_pos[t_begin + lane] : 0;
+        for (int64_t tb = t_begin; tb < t_end; tb += 64) {
+            const int64_t tn = tb + 64 + lane;
+            const uint32_t kl_next = tn < t_end ? keys[tn] : 0u;
+            const int32_t pl_next = tn < t_end ? sorted_pos[tn] : 0;
+            for (int m0 = 0; m0 < 64 && tb + m0 < t_end; m0 += DEPTH) {
+                uint4 gv[DEPTH];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(sorted_pos[t + m]) >> pos_shift);
-                    gv[m] = *reinterpret_cast<const uint4*>(g + i * d + j0);
+                for (int m = 0; m < DEPTH; ++m) {
+                    const int src = tb + m0 + m < t_end ? m0 + m : m0;
+                    const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readlane(pl, src) >> pos_shift);
+                    gv[m] = *reinterpret_cast<const uint4*>(g + i * d + jc);
                 }
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float x[8] = {bf16lo(gv[m].x), bf16hi(gv[m].x), bf16lo(gv[m].y), bf16hi(gv[m].y),
-                                        bf16lo(gv[m].z), bf16hi(gv[m].z), bf16lo(gv[m].w), bf16hi(gv[m].w)};
+                for (int m = 0; m < DEPTH; ++m) {
+                    if (tb + m0 + m < t_end) {      // uniform predicate, so every index stays constant
+                        const uint32_t km = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kl), m0 + m));
+                        if (km != prev) {           // a new group: store the finished one
+                            float* o = out + uo * d + jc;
+                            if (col_ok) {
+                                reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                                reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+                            }
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) acc[q] = WEIGHT ? __builtin_fmaf(w[q], x[q], acc[q]) : acc[q] + x[q];
+                            for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+                            ++uo;
+                            prev = km;
+                        }
+                        const float x[8] = {bf16lo(gv[m].x), bf16hi(gv[m].x), bf16lo(gv[m].y), bf16hi(gv[m].y),
+                                            bf16lo(gv[m].z), bf16hi(gv[m].z), bf16lo(gv[m].w), bf16hi(gv[m].w)};
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            acc[q] = WEIGHT ? __builtin_fmaf(w[q], x[q], acc[q]) : acc[q] + x[q];
+                    }
                 }
             }
-            for (; t < s1; ++t) {
-                const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(sorted_pos[t]) >> pos_shift);
-                const uint4 gv = *reinterpret_cast<const uint4*>(g + i * d + j0);
-                const float x[8] = {bf16lo(gv.x), bf16hi(gv.x), bf16lo(gv.y), bf16hi(gv.y),
-                                    bf16lo(gv.z), bf16hi(gv.z), bf16lo(gv.w), bf16hi(gv.w)};
-#pragma unroll
-                for (int q = 0; q < 8; ++q) acc[q] = WEIGHT ? __builtin_fmaf(w[q], x[q], acc[q]) : acc[q] + x[q];
-            }
-            float* o = out + u * d + j0;
+            kl = kl_next;
+            pl = pl_next;
+        }
+        if (col_ok) {
+            float* o = out + uo * d + j0;
             reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
             reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
@@ -1194,9 +1240,10 @@ int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* val
     hipLaunchKernelGGL(seg_bounds_kernel, dim3(gN), dim3(256), 0, st, keys, flags, N, limit, segs, ids_out, n_unique);
     const int nslices = (d + kSlice - 1) / kSlice;
     const int waves = nslices < 16 ? nslices : 16;
-    int64_t grid = N < 16384 ? N : 16384;
-    hipLaunchKernelGGL(seg_reduce_kernel<WEIGHT>, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, segs,
-                       n_unique, pos, pos_shift, g, W, d, grad_out);
+    const int64_t grid = (N + kWalkChunk - 1) / kWalkChunk;
+    // 16 rows ahead: the deepest prefetch that stays in registers (no scratch)
+    hipLaunchKernelGGL((seg_walk_kernel<WEIGHT, 16>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, keys,
+                       flags, segs, n_unique, pos, pos_shift, g, W, d, grad_out);
     return hip_status("gradient launch");
 }
 
