@@ -44,6 +44,9 @@ def lib():
         L.oracle_gate_add.argtypes = [P, P, I64, I32, P, P, P, P]
         L.oracle_forward.argtypes = [P, I64, P, I32, P, P, I32, P, P, I64, I32,
                                      P, P, P, P, P, P]
+        L.oracle_e2m1.restype = ctypes.c_float
+        L.oracle_e2m1.argtypes = [ctypes.c_int]
+        L.oracle_embed_bag_mxfp4.argtypes = [P, I64, I32, P, I64, P]
         L.oracle_grad_table_rows.argtypes = [P, I64, I32, P, P, P, I64, P]
         L.oracle_grad_e1_tokens.argtypes = [P, P, I64, I32, P, P, I64, P]
         L.oracle_grad_gate.argtypes = [P, P, P, I64, I32, P]
@@ -116,6 +119,20 @@ def embed_bag_int8(Q, scale, rows) -> np.ndarray:
     return eN
 
 
+def e2m1(code: int) -> float:
+    return float(lib().oracle_e2m1(int(code)))
+
+
+def embed_bag_mxfp4(T, d, rows) -> np.ndarray:
+    """``T``: uint8 [R][d/2 + d/32] MXFP4 rows."""
+    T = _c(T, np.uint8)
+    rows = _c(rows, np.int32)
+    n = rows.shape[0]
+    eN = np.zeros((n, d), dtype=np.float32)
+    lib().oracle_embed_bag_mxfp4(_p(T), T.shape[0], d, _p(rows), n, _p(eN))
+    return eN
+
+
 def gate_add(eN, e1_rows, W_g, e1=None, residual=None) -> np.ndarray:
     eN = _c(eN, np.float32)
     n, d = eN.shape
@@ -129,22 +146,29 @@ def gate_add(eN, e1_rows, W_g, e1=None, residual=None) -> np.ndarray:
 
 
 def forward(tokens, seq_offsets, table, W_g, e1=None, residual=None, history=None,
-            seeds=None, scale=None):
-    """Whole path.  ``table`` is uint16 bf16 bits [R][d], or int8 [R][d] with
-    ``scale`` fp32 [R].  Returns (out bf16 bits [n][d], rows [n][16], eN fp32)."""
+            seeds=None, scale=None, mxfp4_d=None):
+    """Whole path.  ``table`` is uint16 bf16 bits [R][d], int8 [R][d] with
+    ``scale`` fp32 [R], or (``mxfp4_d`` = d) uint8 MXFP4 rows [R][d/2 + d/32].
+    Returns (out bf16 bits [n][d], rows [n][16], eN fp32)."""
     t = _c(tokens, np.int32)
     so = _c(seq_offsets, np.int32)
     h = _c(history, np.int32)
     sd = default_seeds() if seeds is None else _c(seeds, np.uint64)
     is_int8 = np.asarray(table).dtype == np.int8
-    tab = _c(table, np.int8 if is_int8 else np.uint16)
+    if mxfp4_d is not None:
+        tab = _c(table, np.uint8)
+        R, d = tab.shape[0], int(mxfp4_d)
+        dtype = 2
+    else:
+        tab = _c(table, np.int8 if is_int8 else np.uint16)
+        R, d = tab.shape
+        dtype = 1 if is_int8 else 0
     sc = _c(scale, np.float32)
-    R, d = tab.shape
     n = t.size
     out = np.zeros((n, d), dtype=np.uint16)
     rows = np.zeros((n, K), dtype=np.int32)
     eN = np.zeros((n, d), dtype=np.float32)
-    lib().oracle_forward(_p(t), n, _p(so), so.size - 1, _p(h), _p(sd), 1 if is_int8 else 0,
+    lib().oracle_forward(_p(t), n, _p(so), so.size - 1, _p(h), _p(sd), dtype,
                          _p(tab), _p(sc), R, d, _p(_c(e1, np.uint16)), _p(_c(W_g, np.float32)),
                          _p(_c(residual, np.uint16)), _p(out), _p(rows), _p(eN))
     return out, rows, eN

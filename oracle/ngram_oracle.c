@@ -169,6 +169,51 @@ void oracle_embed_bag_int8(const int8_t* Q, const float* scale, int64_t R, int32
 }
 
 /*
+ * 4-bit rows: "Qwen 3.8 Flash-Next Deep Dive…", section 1, sizes the table
+ * at FP4.  Format taken: OCP Microscaling (MX) FP4, i.e. E2M1 element codes
+ * with one E8M0 scale per 32 elements.  A row of d elements is d/2 + d/32
+ * bytes: bytes 0 .. d/2-1 hold the codes, element 2m in the low nibble of
+ * byte m and 2m+1 in the high nibble; bytes d/2 .. d/2+d/32-1 hold the scales,
+ * scale g for elements 32g .. 32g+31.  Element value = e2m1(code) * 2^(E-127)
+ * (exact in fp32), NaN when E = 255.  E2M1: sign bit 3, exponent bits 2-1
+ * (bias 1), mantissa bit 0; exponent 0 is subnormal (0 or 0.5).
+ */
+float oracle_e2m1(int code)
+{
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    float mag = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return sign ? -mag : mag;
+}
+
+float oracle_mxfp4_value(const uint8_t* row, int32_t d, int32_t j)
+{
+    uint8_t byte = row[j / 2];
+    int code = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+    int E = row[d / 2 + j / 32];
+    if (E == 255)
+        return NAN;
+    return ldexpf(oracle_e2m1(code), E - 127);
+}
+
+/* eN[i][j] = sum over k = 0..15, in order, of the MXFP4 value of row
+ * rows[i][k] at j (fp32, from +0). */
+void oracle_embed_bag_mxfp4(const uint8_t* T, int64_t R, int32_t d, const int32_t* rows,
+                            int64_t n, float* eN)
+{
+    (void)R;
+    const int64_t row_bytes = d / 2 + d / 32;
+    for (int64_t i = 0; i < n; ++i)
+        for (int32_t j = 0; j < d; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < ORACLE_K; ++k) {
+                int64_t r = rows[i * ORACLE_K + k];
+                acc = acc + oracle_mxfp4_value(T + r * row_bytes, d, j);
+            }
+            eN[i * d + j] = acc;
+        }
+}
+
+/*
  * out[i][j] = bf16(residual[i][j] + fmaf(W_g[j], eN[i][j], e1[e1_rows[i]][j])).
  * e1_rows[i] is the token w_t (the 1-gram id).  e1 and residual may be NULL.
  */
@@ -185,8 +230,9 @@ void oracle_gate_add(const float* eN, const int32_t* e1_rows, int64_t n, int32_t
         }
 }
 
-/* The whole path for a bf16 (dtype 0) or int8 (dtype 1) table, one step
- * after another: context and hash, then the sum, then gate and residual. */
+/* The whole path for a bf16 (dtype 0), int8 (dtype 1) or MXFP4 (dtype 2)
+ * table, one step after another: context and hash, then the sum, then gate
+ * and residual.  An MXFP4 table is passed as its [R][d/2 + d/32] bytes. */
 void oracle_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
                     const int32_t* history, const uint64_t* seeds, int32_t dtype,
                     const void* table, const float* scale, int64_t R, int32_t d,
@@ -199,8 +245,10 @@ void oracle_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets
     oracle_hash(tokens, n, seq_offsets, S, history, seeds, R, rows);
     if (dtype == 0)
         oracle_embed_bag_bf16((const uint16_t*)table, R, d, rows, n, eN);
-    else
+    else if (dtype == 1)
         oracle_embed_bag_int8((const int8_t*)table, scale, R, d, rows, n, eN);
+    else
+        oracle_embed_bag_mxfp4((const uint8_t*)table, R, d, rows, n, eN);
     oracle_gate_add(eN, tokens, n, d, e1, W_g, residual, out);
     if (!rows_out)
         free(rows);

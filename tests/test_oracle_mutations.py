@@ -57,6 +57,12 @@ MUTATIONS = {
                             "            for (int64_t i = c0; i < n && i < c0 + 128; ++i) {"),
     "grad_gate_unfused": ("part = fmaf(oracle_bf16_to_f32(g[i * d + j]), eN[i * d + j], part);",
                           "part = oracle_bf16_to_f32(g[i * d + j]) * eN[i * d + j] + part;"),
+    "mxfp4_nibbles_swapped": ("int code = (j % 2 == 0) ? (byte & 15) : (byte >> 4);",
+                              "int code = (j % 2 == 0) ? (byte >> 4) : (byte & 15);"),
+    "mxfp4_scale_group_16": ("int E = row[d / 2 + j / 32];", "int E = row[d / 2 + j / 16];"),
+    "mxfp4_scale_bias_128": ("return ldexpf(oracle_e2m1(code), E - 127);", "return ldexpf(oracle_e2m1(code), E - 128);"),
+    "e2m1_exponent_bias_0": ("ldexpf(1.0f + 0.5f * (float)m, e - 1);", "ldexpf(1.0f + 0.5f * (float)m, e);"),
+    "mxfp4_nan_scale_ignored": ("    if (E == 255)\n        return NAN;\n", ""),
     "grad_gate_keeps_invalid": ("if (rows[i * ORACLE_K] < 0)\n                    continue;\n                part",
                                 "part"),
 }
@@ -75,6 +81,6 @@ def test_pins_catch_mutation(name, tmp_path):
     env = dict(os.environ, ORACLE_LIB=str(mlib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py",
-                        "tests/test_oracle_grad.py"],
+                        "tests/test_oracle_grad.py", "tests/test_oracle_mxfp4.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
