@@ -37,10 +37,10 @@ K_ROWS = 16
 def nominal_bytes_per_token(d: int, table: str = "bf16", e1: bool = True, residual: bool = True) -> int:
     """Algorithmic HBM bytes one token moves through the fused kernel: its 16
     table rows (bf16: 2 B per element; int8: 1 B per element plus a 4-byte row
-    scale), its e1 row, its residual row read and its output row written (2 B
+    scale; MXFP4: half a byte per element plus one scale byte per 32), its e1 row, its residual row read and its output row written (2 B
     per element each), and its token id (4 B).  W_g (d x 4 B) is read once per
     launch and counted per launch, not per token."""
-    row = d * 2 if table == "bf16" else d + 4
+    row = {"bf16": d * 2, "int8": d + 4, "mxfp4": d // 2 + d // 32}[table]
     b = K_ROWS * row + 4
     if e1:
         b += 2 * d
@@ -58,7 +58,7 @@ def dma_time_estimate_us(K: int, d: int, elem_bytes: int, bandwidth_gbps: float)
 
 
 def table_bytes(R: int, d: int, table: str = "bf16") -> int:
-    return R * d * (2 if table == "bf16" else 1) + (0 if table == "bf16" else 4 * R)
+    return R * {"bf16": 2 * d, "int8": d + 4, "mxfp4": d // 2 + d // 32}[table]
 
 
 def source_sha256() -> str:
@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "int8", "decode1", "decode2", "decode4", "host", "backward"])
+                    choices=["prefill", "int8", "fp4", "decode1", "decode2", "decode4", "host", "backward"])
     ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged", "pool"],
                     help="host workload: sum straight from pinned memory, stage rows in HBM first, or go "
                          "through an HBM row pool (hot-row cache + per-batch dedup)")
@@ -105,7 +105,8 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, max_seconds=20.0):
+def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, max_seconds=20.0,
+                 mxfp4_d=None):
     """The oracle timed on the host cores on a bounded sample of the
     workload: the whole batch, sequence by sequence, hashed into a host copy
     of the first ``R_cpu`` table rows (the full table does not fit in host
@@ -126,7 +127,7 @@ def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, 
         a, b = int(offs[s]), int(offs[s + 1])
         oracle.forward(toks[a:b], np.array([0, b - a], np.int32), table_np, host_inputs.W_g,
                        e1=e1_np, residual=None if res_np is None else res_np[a:b],
-                       history=None if hist is None else hist[s:s + 1], scale=scale_np)
+                       history=None if hist is None else hist[s:s + 1], scale=scale_np, mxfp4_d=mxfp4_d)
         return b - a
 
     passes = tokens_done = 0
@@ -212,6 +213,11 @@ def main():
         scale = synth.fill_gpu(synth.KIND_F32_SCALE, s0, synth.TAG_SCALE,
                                torch.empty(spec.R, dtype=torch.float32, device=dev))
         T = ng.Table(table, spec.R, d, ng.TABLE_INT8_ROWSCALE, row_scale=scale)
+    elif spec.table == "mxfp4":
+        table = synth.fill_gpu_mxfp4(spec.table_kind, s0, synth.TAG_TABLE,
+                                     torch.empty(spec.R * synth.mxfp4_row_bytes(d), dtype=torch.uint8, device=dev), d)
+        scale = None
+        T = ng.Table(table, spec.R, d, ng.TABLE_MXFP4)
     else:
         table = synth.fill_gpu(spec.table_kind, s0, synth.TAG_TABLE,
                                torch.empty(spec.R * d, dtype=torch.int16, device=dev))
@@ -339,13 +345,18 @@ def main():
         if spec.table == "int8":
             table_np = table[: R_cpu * d].cpu().numpy().reshape(R_cpu, d)
             scale_np = scale[:R_cpu].cpu().numpy()
+        elif spec.table == "mxfp4":
+            rb = synth.mxfp4_row_bytes(d)
+            table_np = table[: R_cpu * rb].cpu().numpy().reshape(R_cpu, rb)
+            scale_np = None
         else:
             table_np = table[: R_cpu * d].cpu().numpy().view(np.uint16).reshape(R_cpu, d)
             scale_np = None
         e1_np = None if e1 is None else e1.cpu().numpy().view(np.uint16).reshape(spec.V, d)
         res_np = None if batches[0][3] is None else batches[0][3].cpu().numpy().view(np.uint16).reshape(n, d)
         result["cpu_baseline"] = cpu_baseline(HostInputs(spec.replace(R=R_cpu)), table_np, scale_np,
-                                              e1_np, res_np, R_cpu, time.time() - tp)
+                                              e1_np, res_np, R_cpu, time.time() - tp,
+                                              mxfp4_d=d if spec.table == "mxfp4" else None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

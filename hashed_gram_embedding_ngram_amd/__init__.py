@@ -21,6 +21,7 @@ K = 16
 PAD_ID = (1 << 21) - 1
 TABLE_BF16 = 0
 TABLE_INT8_ROWSCALE = 1
+TABLE_MXFP4 = 2
 IN_DEVICE = 0
 IN_HOST = 1
 
@@ -150,16 +151,19 @@ class Table:
         self.data = data
         self.row_scale = row_scale
         self.R, self.d, self.dtype = int(R), int(d), int(dtype)
+        nbytes = self.R * row_bytes(self.d, self.dtype)
         if isinstance(data, HostBuffer):
             self.location = IN_HOST
             ptr = data.ptr
+            if data.nbytes < nbytes:
+                raise NgramError("host table buffer is smaller than R rows")
         else:
-            _dev(data, _BF16 if dtype == TABLE_BF16 else (torch.int8,), "table")
-            _need(data, self.R * self.d, "table")
+            dts = {TABLE_BF16: _BF16, TABLE_INT8_ROWSCALE: (torch.int8,), TABLE_MXFP4: (torch.uint8, torch.int8)}
+            _dev(data, dts.get(self.dtype, _BF16), "table")
+            if data.numel() * data.element_size() < nbytes:
+                raise NgramError(f"table holds {data.numel() * data.element_size()} bytes, R rows need {nbytes}")
             self.location = IN_DEVICE
             ptr = data.data_ptr()
-        if isinstance(data, HostBuffer) and data.nbytes < self.R * self.d * (2 if dtype == TABLE_BF16 else 1):
-            raise NgramError("host table buffer is smaller than R * d elements")
         if dtype == TABLE_INT8_ROWSCALE:
             _dev(row_scale, _F32, "row_scale")
             _need(row_scale, self.R, "row_scale")
@@ -195,6 +199,15 @@ class HostBuffer:
             self.free()
         except Exception:
             pass
+
+
+def row_bytes(d: int, dtype: int) -> int:
+    """Bytes of one table row: 2d (bf16), d (int8) or d/2 + d/32 (MXFP4)."""
+    if dtype == TABLE_BF16:
+        return 2 * d
+    if dtype == TABLE_MXFP4:
+        return d // 2 + d // 32
+    return d
 
 
 def _vocab(e1, d):
@@ -286,8 +299,8 @@ def ngram_gather_host(table: Table, rows, stage_out, remap_out, stage_scale_out=
     n = rows.shape[0] if rows.dim() == 2 else rows.numel() // K
     _need(rows, n * K, "rows")
     _need(remap_out, n * K, "remap_out")
-    row_bytes = table.d * (2 if table.dtype == TABLE_BF16 else 1)
-    if stage_out.numel() * stage_out.element_size() < n * K * row_bytes:
+    rb = row_bytes(table.d, table.dtype)
+    if stage_out.numel() * stage_out.element_size() < n * K * rb:
         raise NgramError("stage_out is smaller than n * 16 rows")
     if table.dtype == TABLE_INT8_ROWSCALE:
         _need(stage_scale_out, n * K, "stage_scale_out")
@@ -307,8 +320,12 @@ class RowPool:
             raise NgramError("a row pool fronts a table in host memory")
         self.table = table
         self.pool_rows = int(pool_rows)
-        dt = torch.int16 if table.dtype == TABLE_BF16 else torch.int8
-        self.data = torch.empty(self.pool_rows * table.d, dtype=dt, device=device)
+        if table.dtype == TABLE_MXFP4:
+            self.data = torch.empty(self.pool_rows * row_bytes(table.d, table.dtype), dtype=torch.uint8,
+                                    device=device)
+        else:
+            dt = torch.int16 if table.dtype == TABLE_BF16 else torch.int8
+            self.data = torch.empty(self.pool_rows * table.d, dtype=dt, device=device)
         self.row_scale = (torch.empty(self.pool_rows, dtype=torch.float32, device=device)
                           if table.dtype == TABLE_INT8_ROWSCALE else None)
         self.slot_of_row = torch.empty(table.R, dtype=torch.int32, device=device)

@@ -37,6 +37,9 @@
 #ifndef NGRAM_SCHED_BARRIER
 #define NGRAM_SCHED_BARRIER 0      // 1: force all 16 row loads before the first add
 #endif
+#ifndef NGRAM_SADDR
+#define NGRAM_SADDR 1              // row loads as scalar row base + 32-bit lane offset
+#endif
 #ifndef NGRAM_NT_TABLE
 #define NGRAM_NT_TABLE 0           // nontemporal table-row loads
 #endif
@@ -132,13 +135,38 @@ __device__ inline uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Eight table elements of one row slice, as fp32.
+// MXFP4 slice of one row: 4 bytes of E2M1 codes (8 elements) and their E8M0
+// scale byte.  A row is d/2 code bytes then d/32 scale bytes.
+struct Fp4Slice {
+    uint32_t codes;
+    uint32_t scale;
+};
+
+// A wave-uniform address, passed through readfirstlane so that it stays in
+// scalar registers: a load from it plus a 32-bit lane offset is then one
+// scalar-base vector-offset global load, with no 64-bit address per lane.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+
+__device__ inline gbytes uniform_row(const void* base, int32_t r, int64_t row_bytes) {
+    const uint64_t u = reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(base) + static_cast<int64_t>(r) * row_bytes);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return reinterpret_cast<gbytes>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Eight table elements of one row slice, as raw bits.  `row` is the row's
+// wave-uniform start; `off` the lane's byte offset of the 8 elements (`aux`
+// the offset of an MXFP4 slice's scale byte).
 template <int DT> struct Row8;
 
 template <> struct Row8<NGRAM_TABLE_BF16> {
     using Raw = uint4;
-    __device__ static Raw load(const void* base, int64_t off) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off);
+    __device__ static int64_t row_bytes(int64_t d) { return 2 * d; }
+    __device__ static uint32_t lane_off(int64_t j0) { return static_cast<uint32_t>(j0) * 2u; }
+    __device__ static Raw load(gbytes row, uint32_t off, uint32_t aux) {
+        (void)aux;
+        const __attribute__((address_space(1))) u32x4* p =
+            reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(row + off);
 #if NGRAM_NT_TABLE
         const u32x4 v = __builtin_nontemporal_load(p);
 #else
@@ -149,14 +177,31 @@ template <> struct Row8<NGRAM_TABLE_BF16> {
 };
 template <> struct Row8<NGRAM_TABLE_INT8_ROWSCALE> {
     using Raw = uint2;
-    __device__ static Raw load(const void* base, int64_t off) {
-        const u32x2* p = reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(base) + off);
+    __device__ static int64_t row_bytes(int64_t d) { return d; }
+    __device__ static uint32_t lane_off(int64_t j0) { return static_cast<uint32_t>(j0); }
+    __device__ static Raw load(gbytes row, uint32_t off, uint32_t aux) {
+        (void)aux;
+        const __attribute__((address_space(1))) u32x2* p =
+            reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(row + off);
 #if NGRAM_NT_TABLE
         const u32x2 v = __builtin_nontemporal_load(p);
 #else
         const u32x2 v = *p;
 #endif
         return make_uint2(v.x, v.y);
+    }
+};
+// An MXFP4 row is d/2 code bytes then d/32 scale bytes: columns j0..j0+7
+// are code bytes j0/2 .. j0/2+3 and share scale byte d/2 + j0/32.
+template <> struct Row8<NGRAM_TABLE_MXFP4> {
+    using Raw = Fp4Slice;
+    __device__ static int64_t row_bytes(int64_t d) { return d / 2 + d / 32; }
+    __device__ static uint32_t lane_off(int64_t j0) { return static_cast<uint32_t>(j0) >> 1; }
+    __device__ static Raw load(gbytes row, uint32_t off, uint32_t aux) {
+        Fp4Slice f;
+        f.codes = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(row + off);
+        f.scale = row[aux];
+        return f;
     }
 };
 
@@ -168,6 +213,25 @@ __device__ inline void store_out(uint16_t* o, const uint4& v) {
 #else
     *reinterpret_cast<u32x4*>(o) = w;
 #endif
+}
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// acc += e2m1 * 2^(E-127) for the 8 elements; the hardware conversion takes
+// the scale's exponent (exact for the power-of-two E8M0 scale, including the
+// subnormal 2^-127).  E = 255 is reported through `nan`.
+__device__ inline void add_fp4(float acc[8], const Fp4Slice& f, bool& nan) {
+    const uint32_t E = f.scale;
+    nan = nan || E == 255u;
+    const float s = __uint_as_float(E == 0u ? 0x00400000u : (E << 23));
+    const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.codes, s, 0);
+    const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.codes, s, 1);
+    const v2f c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.codes, s, 2);
+    const v2f e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.codes, s, 3);
+    acc[0] = acc[0] + a.x; acc[1] = acc[1] + a.y;
+    acc[2] = acc[2] + b.x; acc[3] = acc[3] + b.y;
+    acc[4] = acc[4] + c.x; acc[5] = acc[5] + c.y;
+    acc[6] = acc[6] + e.x; acc[7] = acc[7] + e.y;
 }
 
 __device__ inline void add_row(float acc[8], const uint4& v) {
@@ -192,33 +256,65 @@ __device__ inline void fma_row(float acc[8], const uint2& v, float s) {
     acc[7] = __builtin_fmaf(i8f(v.y, 3), s, acc[7]);
 }
 
-// The fp32 sum over k = 0..15 of the lane's 8 columns of rows r[0..15].
-// All 16 loads are issued before the first add.
+// The lane's 8 columns of the 16 rows r[0..15], all loads issued back to
+// back ...
 template <int DT>
-__device__ inline void gather_sum(float acc[8], const void* __restrict__ tab,
-                                  const float* __restrict__ scale, const int32_t r[kK],
-                                  int64_t d, int64_t j0) {
-    using Raw = typename Row8<DT>::Raw;
-    Raw v[kK];
-#pragma unroll
-    for (int k = 0; k < kK; ++k) v[k] = Row8<DT>::load(tab, static_cast<int64_t>(r[k]) * d + j0);
-#if NGRAM_SCHED_BARRIER
-    // Keep the scheduler from sinking loads below the adds: all 16 row
-    // loads of the slice are in flight before the first one is consumed.
-    __builtin_amdgcn_sched_barrier(0);
+__device__ inline void gather_load(typename Row8<DT>::Raw v[kK], const void* __restrict__ tab, const int32_t r[kK],
+                                   int64_t d, int64_t j0) {
+    uint32_t off = Row8<DT>::lane_off(j0);
+    uint32_t aux = static_cast<uint32_t>(d >> 1) + (static_cast<uint32_t>(j0) >> 5);
+#if NGRAM_SADDR
+    // Materialise the lane offsets here as 32-bit registers: each row load is
+    // then the row's scalar base plus this offset, with no 64-bit address
+    // computed per lane and row.
+    if constexpr (DT == NGRAM_TABLE_MXFP4) __asm__ volatile("" : "+v"(off), "+v"(aux));
+    else __asm__ volatile("" : "+v"(off));
 #endif
+    const int64_t rb = Row8<DT>::row_bytes(d);
+#pragma unroll
+    for (int k = 0; k < kK; ++k) v[k] = Row8<DT>::load(uniform_row(tab, r[k], rb), off, aux);
+}
+
+// ... and summed in fp32 in k order.
+template <int DT>
+__device__ inline void gather_reduce(float acc[8], const typename Row8<DT>::Raw v[kK],
+                                     const float* __restrict__ scale, const int32_t r[kK]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     if constexpr (DT == NGRAM_TABLE_BF16) {
 #pragma unroll
         for (int k = 0; k < kK; ++k) add_row(acc, v[k]);
-    } else {
+    } else if constexpr (DT == NGRAM_TABLE_INT8_ROWSCALE) {
         float s[kK];
 #pragma unroll
         for (int k = 0; k < kK; ++k) s[k] = scale[r[k]];
 #pragma unroll
         for (int k = 0; k < kK; ++k) fma_row(acc, v[k], s[k]);
+    } else {
+        bool nan = false;
+#pragma unroll
+        for (int k = 0; k < kK; ++k) add_fp4(acc, v[k], nan);
+        if (nan) {
+            // a NaN term makes the in-order sum NaN
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __uint_as_float(kNaNf32);
+        }
     }
+}
+
+// The fp32 sum over k = 0..15 of the lane's 8 columns of rows r[0..15].
+template <int DT>
+__device__ inline void gather_sum(float acc[8], const void* __restrict__ tab,
+                                  const float* __restrict__ scale, const int32_t r[kK],
+                                  int64_t d, int64_t j0) {
+    typename Row8<DT>::Raw v[kK];
+    gather_load<DT>(v, tab, r, d, j0);
+#if NGRAM_SCHED_BARRIER
+    // Keep the scheduler from sinking loads below the adds: all 16 row
+    // loads of the slice are in flight before the first one is consumed.
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+    gather_reduce<DT>(acc, v, scale, r);
 }
 
 // out = bf16(res + fmaf(w, acc, e1)) for the lane's 8 columns.
@@ -481,8 +577,8 @@ __global__ void __launch_bounds__(256) ngram_gate_kernel(const GateArgs a) {
 }
 
 // Zero-copy staging of host-table rows: one wavefront per (token, k) row,
-// 16-byte lanes (8-byte when the row is not a multiple of 16 bytes), a whole
-// row's loads issued before its stores; stage row t = i*16 + k.
+// 16-byte lanes (8- or 4-byte when the row size is not a multiple of 16), a
+// whole row's loads issued before its stores; stage row t = i*16 + k.
 struct StageArgs {
     const void* tab;
     const float* scale;
@@ -1026,6 +1122,9 @@ int check_table(const ngram_table* T) {
         if (!aligned(T->data, 8)) return fail(NGRAM_EALIGN, "int8 table data not 8-byte aligned");
         if (!T->row_scale) return fail(NGRAM_EINVAL, "int8 table needs row_scale");
         if (!aligned(T->row_scale, 4)) return fail(NGRAM_EALIGN, "row_scale not 4-byte aligned");
+    } else if (T->dtype == NGRAM_TABLE_MXFP4) {
+        if (T->d % 128 != 0) return fail(NGRAM_EINVAL, "MXFP4 rows need d %% 128 == 0 (d=%d)", T->d);
+        if (!aligned(T->data, 16)) return fail(NGRAM_EALIGN, "MXFP4 table data not 16-byte aligned");
     } else {
         return fail(NGRAM_EINVAL, "unknown table dtype %d", T->dtype);
     }
@@ -1089,7 +1188,7 @@ Shape slice_shape(int64_t n, int32_t d, int32_t dtype) {
     Shape s;
     s.waves = nslices < 16 ? nslices : 16;
     int tpw = env_int("NGRAM_TOKENS_PER_WG", 0);
-    if (tpw <= 0) tpw = dtype == NGRAM_TABLE_INT8_ROWSCALE ? 4 : 1;
+    if (tpw <= 0) tpw = dtype == NGRAM_TABLE_BF16 ? 1 : 4;     // int8, MXFP4: 4
     if (tpw > 64) tpw = 64;
     s.tpw = tpw;
     s.grid = (n + tpw - 1) / tpw;
@@ -1109,7 +1208,10 @@ int host_workgroups() {
 }
 
 int64_t table_row_bytes(const ngram_table* T) {
-    return static_cast<int64_t>(T->d) * (T->dtype == NGRAM_TABLE_BF16 ? 2 : 1);
+    const int64_t d = T->d;
+    if (T->dtype == NGRAM_TABLE_BF16) return 2 * d;
+    if (T->dtype == NGRAM_TABLE_MXFP4) return d / 2 + d / 32;
+    return d;
 }
 
 unsigned grid_for(int64_t count) {
@@ -1341,9 +1443,12 @@ int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float*
     if (T->dtype == NGRAM_TABLE_BF16) {
         if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, true>), grid, block, lds, stream, a);
         else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, false>), grid, block, lds, stream, a);
-    } else {
+    } else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) {
         if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, true>), grid, block, lds, stream, a);
         else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, false>), grid, block, lds, stream, a);
+    } else {
+        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, false>), grid, block, lds, stream, a);
     }
     return hip_status("ngram_embed_bag launch");
 }
@@ -1404,7 +1509,8 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
     cap_for_host(sh, T);
     a.tpw = sh.tpw;
     if (T->dtype == NGRAM_TABLE_BF16) launch_fwd_dt<NGRAM_TABLE_BF16>(a, sh, stream);
-    else launch_fwd_dt<NGRAM_TABLE_INT8_ROWSCALE>(a, sh, stream);
+    else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) launch_fwd_dt<NGRAM_TABLE_INT8_ROWSCALE>(a, sh, stream);
+    else launch_fwd_dt<NGRAM_TABLE_MXFP4>(a, sh, stream);
     return hip_status("ngram_forward launch");
 }
 
@@ -1455,12 +1561,13 @@ int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
     a.tab = tab; a.scale = T_host->row_scale; a.rows = rows; a.stage = stage_out;
     a.stage_scale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? stage_scale_out : nullptr;
     a.remap = remap_out; a.nrows = n * kK; a.R = T_host->R;
-    a.row_bytes = static_cast<int64_t>(T_host->d) * (T_host->dtype == NGRAM_TABLE_BF16 ? 2 : 1);
+    a.row_bytes = table_row_bytes(T_host);
     int64_t blocks = (a.nrows + 15) / 16;
     if (blocks > host_workgroups()) blocks = host_workgroups();
     const dim3 grid(static_cast<unsigned>(blocks)), block(1024);
     if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x4>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(ngram_stage_kernel<u32x2>, grid, block, 0, stream, a);
+    else if (a.row_bytes % 8 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x2>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(ngram_stage_kernel<uint32_t>, grid, block, 0, stream, a);
     return hip_status("ngram_gather_host launch");
 }
 
@@ -1499,9 +1606,12 @@ int ngram_pool_cache_rows(const ngram_table* T_host, ngram_row_pool* P, const in
         if (row_bytes % 16 == 0)
             hipLaunchKernelGGL(pool_cache_kernel<u32x4>, dim3(blocks), dim3(1024), 0, stream, tab, T_host->row_scale,
                                hot_rows, C, T_host->R, P->data, pscale, P->slot_of_row, row_bytes);
-        else
+        else if (row_bytes % 8 == 0)
             hipLaunchKernelGGL(pool_cache_kernel<u32x2>, dim3(blocks), dim3(1024), 0, stream, tab, T_host->row_scale,
                                hot_rows, C, T_host->R, P->data, pscale, P->slot_of_row, row_bytes);
+        else
+            hipLaunchKernelGGL(pool_cache_kernel<uint32_t>, dim3(blocks), dim3(1024), 0, stream, tab,
+                               T_host->row_scale, hot_rows, C, T_host->R, P->data, pscale, P->slot_of_row, row_bytes);
     }
     rc = hip_status("ngram_pool_cache_rows launch");
     if (!rc) P->cached = C;
@@ -1548,7 +1658,8 @@ int ngram_pool_gather(const ngram_table* T_host, const ngram_row_pool* P, const 
     int64_t blocks = (a.nrows + 15) / 16;
     if (blocks > host_workgroups()) blocks = host_workgroups();
     if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(pool_fetch_kernel<u32x4>, dim3(blocks), dim3(1024), 0, stream, a);
-    else hipLaunchKernelGGL(pool_fetch_kernel<u32x2>, dim3(blocks), dim3(1024), 0, stream, a);
+    else if (a.row_bytes % 8 == 0) hipLaunchKernelGGL(pool_fetch_kernel<u32x2>, dim3(blocks), dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL(pool_fetch_kernel<uint32_t>, dim3(blocks), dim3(1024), 0, stream, a);
     return hip_status("ngram_pool_gather launch");
 }
 

@@ -19,7 +19,8 @@
  *   splitmix64 generator from state x, and the default seed_k is output k of
  *   that generator from state 0.
  * Arithmetic: acc = +0.0f; for k = 0..15: acc += (float)T[row_k][j] (bf16
- * table) or acc = fmaf((float)q[row_k][j], scale[row_k], acc) (int8 table);
+ * table), acc = fmaf((float)q[row_k][j], scale[row_k], acc) (int8 table) or
+ * acc += e2m1 * 2^(E-127) (MXFP4 table, the product exact);
  * h = fmaf(W_g[j], acc, e1[w_t][j]) (or + 0 without e1); y = residual + h (or h);
  * out = bf16 round-to-nearest-even of y (NaN -> 0x7FC0).  The order is fixed,
  * so results are reproducible bit for bit.
@@ -65,12 +66,16 @@ typedef enum {
     NGRAM_ENOTSUP = -5   /* a combination this build does not support */
 } ngram_status;
 
-typedef enum { NGRAM_TABLE_BF16 = 0, NGRAM_TABLE_INT8_ROWSCALE = 1 } ngram_dtype;
+typedef enum { NGRAM_TABLE_BF16 = 0, NGRAM_TABLE_INT8_ROWSCALE = 1, NGRAM_TABLE_MXFP4 = 2 } ngram_dtype;
 typedef enum { NGRAM_IN_DEVICE = 0, NGRAM_IN_HOST = 1 } ngram_location;
 
 /* The hashed table: [R][d] row-major.  bf16: data 16-byte aligned.  int8:
  * data 8-byte aligned and row_scale[R] fp32 (4-byte aligned), value of
- * element j of row r = q[r][j] * row_scale[r].  location NGRAM_IN_DEVICE: data
+ * element j of row r = q[r][j] * row_scale[r].  MXFP4 (OCP Microscaling FP4;
+ * "Qwen 3.8 Flash-Next Deep Dive…", section 1, sizes the table at FP4): each
+ * row is d/2 + d/32 bytes, the E2M1 codes (element 2m in the low nibble of
+ * byte m) then one E8M0 scale per 32 elements; value = e2m1 * 2^(E-127), NaN
+ * for E = 255; d a multiple of 128, data 16-byte aligned, row_scale unused.  location NGRAM_IN_DEVICE: data
  * and row_scale in device memory.  NGRAM_IN_HOST: data is pinned host memory
  * mapped for the device (ngram_host_alloc, or hipHostMalloc); rows are read
  * over PCIe by the GPU (zero copy); row_scale stays in device memory. */

@@ -56,6 +56,8 @@ KIND_BF16_WIDE = 2
 KIND_F32_UNIT = 3
 KIND_I8_NORMAL = 4
 KIND_F32_SCALE = 5
+KIND_MXFP4 = 6          # 4-bit rows: random codes, scales 2^-8 .. 2^-5
+KIND_MXFP4_WIDE = 7     # 4-bit rows: random codes, scales 2^-27 .. 2^4
 
 
 def philox4x32_10(c0, c1, c2, c3, k0, k1):
@@ -121,6 +123,27 @@ def value_bits(kind: int, x: np.ndarray) -> np.ndarray:
         m = (np.uint32(1 << 23) + (x & 0x7FFFFF)).astype(np.float32)  # exact
         return (m * np.float32(2.0 ** -34)).view(np.uint32)
     raise ValueError(f"unknown kind {kind}")
+
+
+def mxfp4_bytes(kind: int, x: np.ndarray, b: np.ndarray, d: int) -> np.ndarray:
+    """Bytes of 4-bit MXFP4 rows from generator words: the code bytes (two
+    4-bit codes each) are the word's low byte; the scale bytes are E8M0
+    exponents, 119 + (x & 3) or, for the wide kind, 100 + ((x >> 8) & 31)."""
+    x = x.astype(np.uint32)
+    scale = (119 + (x & 3)) if kind == KIND_MXFP4 else (100 + ((x >> 8) & 31))
+    return np.where(np.asarray(b) < d // 2, x & 0xFF, scale).astype(np.uint8)
+
+
+def mxfp4_row_bytes(d: int) -> int:
+    return d // 2 + d // 32
+
+
+def mxfp4_rows(kind: int, seed: int, tag: int, d: int, row_ids) -> np.ndarray:
+    """Rows ``row_ids`` of a generated MXFP4 table: uint8 [len][d/2 + d/32]."""
+    rb = mxfp4_row_bytes(d)
+    r = np.asarray(row_ids, dtype=np.uint64).reshape(-1, 1)
+    b = np.arange(rb, dtype=np.uint64)[None, :]
+    return mxfp4_bytes(kind, words(seed, tag, r * np.uint64(rb) + b), b, d)
 
 
 def tensor(kind: int, seed: int, tag: int, numel: int, offset: int = 0) -> np.ndarray:
@@ -210,4 +233,24 @@ def fill_gpu(kind: int, seed: int, tag: int, t, offset: int = 0, stream=None):
                            t.numel(), int(offset), stream.cuda_stream)
     if rc != 0:
         raise RuntimeError(f"synth_fill failed: {rc}")
+    return t
+
+
+def fill_gpu_mxfp4(kind: int, seed: int, tag: int, t, d: int, offset: int = 0, stream=None):
+    """Fill the uint8 CUDA tensor ``t`` with bytes ``offset ..`` of a
+    generated MXFP4 table of row width ``d``."""
+    import ctypes
+
+    import torch
+    assert t.is_cuda and t.is_contiguous() and t.element_size() == 1
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    L = _gpu()
+    L.synth_fill_mxfp4.restype = ctypes.c_int
+    L.synth_fill_mxfp4.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    rc = L.synth_fill_mxfp4(int(kind), seed & 0xFFFFFFFFFFFFFFFF, int(tag), t.data_ptr(), t.numel(), int(offset),
+                            int(d), stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_fill_mxfp4 failed: {rc}")
     return t

@@ -65,7 +65,49 @@ __global__ void __launch_bounds__(256) fill_kernel(void* dst, int64_t numel, int
     }
 }
 
+// Bytes of 4-bit MXFP4 rows (row width d, d/2 + d/32 bytes per row): code
+// bytes are the word's low byte, scale bytes an E8M0 exponent.
+template <bool WIDE>
+__global__ void __launch_bounds__(256) fill_mxfp4_kernel(uint8_t* dst, int64_t numel, int64_t offset, uint64_t seed,
+                                                         uint32_t tag, int32_t d) {
+    const int64_t rb = d / 2 + d / 32;
+    const int64_t g0 = offset >> 2;
+    const int64_t gend = (offset + numel + 3) >> 2;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t g = g0 + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < gend; g += stride) {
+        uint32_t c[4] = {static_cast<uint32_t>(g), static_cast<uint32_t>(static_cast<uint64_t>(g) >> 32), tag, 0u};
+        philox4x32_10(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int64_t e = 4 * g + w;
+            if (e < offset || e >= offset + numel) continue;
+            const int64_t b = e % rb;
+            const uint32_t x = c[w];
+            const uint32_t sc = WIDE ? 100u + ((x >> 8) & 31u) : 119u + (x & 3u);
+            dst[e - offset] = static_cast<uint8_t>(b < d / 2 ? (x & 0xFFu) : sc);
+        }
+    }
+}
+
 }  // namespace
+
+extern "C" int synth_fill_mxfp4(int kind, uint64_t seed, uint32_t tag, void* dst, int64_t numel, int64_t offset,
+                                int32_t d, hipStream_t stream) {
+    if (numel <= 0) return 0;
+    if (!dst || offset < 0 || d <= 0 || d % 32 != 0) return -1;
+    const int64_t blocks = ((offset + numel + 3) >> 2) - (offset >> 2);
+    int64_t grid = (blocks + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    if (kind == 6)
+        hipLaunchKernelGGL(fill_mxfp4_kernel<false>, dim3(grid), dim3(256), 0, stream, static_cast<uint8_t*>(dst), numel,
+                           offset, seed, tag, d);
+    else if (kind == 7)
+        hipLaunchKernelGGL(fill_mxfp4_kernel<true>, dim3(grid), dim3(256), 0, stream, static_cast<uint8_t*>(dst), numel,
+                           offset, seed, tag, d);
+    else
+        return -1;
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
 
 extern "C" int synth_fill(int kind, uint64_t seed, uint32_t tag, void* dst, int64_t numel, int64_t offset,
                           hipStream_t stream) {

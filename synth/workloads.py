@@ -24,7 +24,7 @@ import dataclasses
 import numpy as np
 
 from . import (KIND_BF16_NORMAL6, KIND_BF16_NORMAL12, KIND_F32_SCALE, KIND_F32_UNIT,
-               KIND_I8_NORMAL, TAG_E1, TAG_HISTORY, TAG_RESIDUAL, TAG_SCALE, TAG_TABLE,
+               KIND_I8_NORMAL, KIND_MXFP4, mxfp4_row_bytes, mxfp4_rows, TAG_E1, TAG_HISTORY, TAG_RESIDUAL, TAG_SCALE, TAG_TABLE,
                TAG_TOKENS, TAG_WG, as_f32, ragged_offsets, rows, tensor, tokens, value_bits,
                words, workload_seed)
 
@@ -38,7 +38,7 @@ class Spec:
     d: int
     zipf_s: float = 1.1
     dist: str = "zipf"
-    table: str = "bf16"                 # "bf16" | "int8"
+    table: str = "bf16"                 # "bf16" | "int8" | "mxfp4"
     table_kind: int = KIND_BF16_NORMAL12
     e1: bool = True
     residual: bool = False
@@ -72,6 +72,9 @@ CONFIGS = {
     "host": Spec("host", (8192,), VOCAB, HOST_R, D, residual=True, config_id=4),
     "int8": Spec("int8", (4096,) * 16, VOCAB, BIG_R, D, zipf_s=1.2, table="int8",
                  table_kind=KIND_I8_NORMAL, residual=True, config_id=5),
+    # the prefill batch over a 4-bit table: 20M x (1280 + 80) bytes = 27.2 GB
+    "fp4": Spec("fp4", (4096,) * 8, VOCAB, BIG_R, D, table="mxfp4", table_kind=KIND_MXFP4, residual=True,
+                config_id=6),
 }
 
 
@@ -89,6 +92,8 @@ class HostInputs:
 
     def table_rows(self, ids):
         s = self.spec
+        if s.table == "mxfp4":
+            return mxfp4_rows(s.table_kind, s.seed, TAG_TABLE, s.d, ids)
         return rows(s.table_kind, s.seed, TAG_TABLE, s.d, ids)
 
     def scale_rows(self, ids):
@@ -106,6 +111,8 @@ class HostInputs:
 
     def full_table(self):
         s = self.spec
+        if s.table == "mxfp4":
+            return self.table_rows(np.arange(s.R))
         return tensor(s.table_kind, s.seed, TAG_TABLE, s.R * s.d).reshape(s.R, s.d)
 
     def full_scale(self):
@@ -128,7 +135,7 @@ class DeviceInputs:
                  table=True, e1=True, residual=True):
         import torch
 
-        from . import fill_gpu
+        from . import fill_gpu, fill_gpu_mxfp4
         self.spec = spec
         h = host or HostInputs(spec)
         dev = torch.device(device)
@@ -139,7 +146,11 @@ class DeviceInputs:
         self.W_g = torch.from_numpy(h.W_g).to(dev)
         self.table = self.scale = self.e1 = self.residual = None
         if table:
-            if spec.table == "int8":
+            if spec.table == "mxfp4":
+                self.table = fill_gpu_mxfp4(spec.table_kind, s, TAG_TABLE,
+                                            torch.empty(spec.R * mxfp4_row_bytes(spec.d), dtype=torch.uint8,
+                                                        device=dev), spec.d)
+            elif spec.table == "int8":
                 self.table = fill_gpu(spec.table_kind, s, TAG_TABLE,
                                       torch.empty(spec.R * spec.d, dtype=torch.int8, device=dev))
                 self.scale = fill_gpu(KIND_F32_SCALE, s, TAG_SCALE,
@@ -159,6 +170,8 @@ class DeviceInputs:
         sp = self.spec
         if sp.table == "int8":
             return ng.Table(self.table, sp.R, sp.d, ng.TABLE_INT8_ROWSCALE, row_scale=self.scale)
+        if sp.table == "mxfp4":
+            return ng.Table(self.table, sp.R, sp.d, ng.TABLE_MXFP4)
         return ng.Table(self.table, sp.R, sp.d)
 
 
@@ -167,15 +180,21 @@ def fill_host_table(spec: Spec, buf_np: np.ndarray, device="cuda:0", chunk_rows=
     generated on the GPU chunk by chunk and copied down."""
     import torch
 
-    from . import fill_gpu
+    from . import fill_gpu, fill_gpu_mxfp4
     dev = torch.device(device)
     d = spec.d
-    dt = torch.int8 if spec.table == "int8" else torch.int16
-    tmp = torch.empty(chunk_rows * d, dtype=dt, device=dev)
+    if spec.table == "mxfp4":
+        per_row, dt = mxfp4_row_bytes(d), torch.uint8
+    else:
+        per_row, dt = d, (torch.int8 if spec.table == "int8" else torch.int16)
+    tmp = torch.empty(chunk_rows * per_row, dtype=dt, device=dev)
     host = torch.from_numpy(buf_np.reshape(-1))
     for r0 in range(0, spec.R, chunk_rows):
         nr = min(chunk_rows, spec.R - r0)
-        view = tmp[: nr * d]
-        fill_gpu(spec.table_kind, spec.seed, TAG_TABLE, view, offset=r0 * d)
-        host[r0 * d:(r0 + nr) * d].copy_(view, non_blocking=False)
+        view = tmp[: nr * per_row]
+        if spec.table == "mxfp4":
+            fill_gpu_mxfp4(spec.table_kind, spec.seed, TAG_TABLE, view, d, offset=r0 * per_row)
+        else:
+            fill_gpu(spec.table_kind, spec.seed, TAG_TABLE, view, offset=r0 * per_row)
+        host[r0 * per_row:(r0 + nr) * per_row].copy_(view, non_blocking=False)
     torch.cuda.synchronize()

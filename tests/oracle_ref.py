@@ -21,6 +21,8 @@ def expected(h, sample=None, rows_all=None):
     Tc = h.table_rows(uniq)
     if sp.table == "int8":
         eN = oracle.embed_bag_int8(Tc, h.scale_rows(uniq), remap)
+    elif sp.table == "mxfp4":
+        eN = oracle.embed_bag_mxfp4(Tc, sp.d, remap)
     else:
         eN = oracle.embed_bag_bf16(Tc, remap)
     toks = h.tokens[idx]

@@ -62,6 +62,10 @@ def test_int8_full_size():
     _check_forward("int8")
 
 
+def test_mxfp4_full_size():
+    _check_forward("fp4")
+
+
 def test_host_table_full_size():
     """R = 5M x 2560 bf16 (23.8 GiB) in pinned host memory: the zero-copy sum
     and the staged path both equal the oracle on sampled tokens, and the host

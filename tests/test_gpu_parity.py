@@ -373,3 +373,74 @@ def test_row_pool(table, C):
             assert np.array_equal(pool.row_scale.cpu().numpy()[pr[valid]], scale.cpu().numpy()[rb[valid]])
     finally:
         hb.free()
+
+
+@pytest.mark.parametrize("d", [128, 384, 2560])
+def test_mxfp4_table(d):
+    sp = Spec(f"mxfp4_d{d}", (1, 40, 0, 200, 3), 151936, 20_011, d, table="mxfp4",
+              table_kind=synth.KIND_MXFP4_WIDE, residual=True, config_id=29)
+    h, di = check_spec(sp)
+    say(f"mxfp4 embed_bag d={d}")
+    rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+    eN = ng.ngram_embed_bag(di.table_obj(), rows)
+    torch.cuda.synchronize()
+    _, want_eN, _ = expected(h)
+    assert np.array_equal(eN.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+
+
+def test_mxfp4_special_scales():
+    """E8M0 = 255 makes the row's 32-element group NaN; E8M0 = 0 (2^-127, an
+    fp32 subnormal) and large exponents decode exactly."""
+    d, R = 128, 5
+    rb = synth.mxfp4_row_bytes(d)
+    rng = np.random.default_rng(0)
+    T = rng.integers(0, 256, size=(R, rb)).astype(np.uint8)
+    T[0, d // 2:] = 0
+    T[1, d // 2:] = [255, 127, 200, 0]
+    T[2, d // 2:] = 254
+    T[3, d // 2:] = [1, 2, 3, 4]
+    T[4, d // 2:] = 127
+    rows = np.array([[0] * 16, [1] * 8 + [4] * 8, [2, 3] * 8, [4] * 16], dtype=np.int32)
+    say("mxfp4 special scales")
+    t = torch.from_numpy(T.reshape(-1)).cuda()
+    eN = ng.ngram_embed_bag(ng.Table(t, R, d, ng.TABLE_MXFP4), torch.from_numpy(rows).cuda())
+    torch.cuda.synchronize()
+    got = eN.cpu().numpy()
+    want = oracle.embed_bag_mxfp4(T, d, rows)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan[1, :32].all() and not nan[1, 32:].any()
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("d", [128, 2560])
+def test_mxfp4_host_table_paths(d, monkeypatch):
+    from synth.workloads import fill_host_table
+    monkeypatch.setenv("NGRAM_HOST_WORKGROUPS", "3")
+    sp = Spec(f"mxfp4_host_d{d}", (40, 0, 90), 151936, 20_011, d, table="mxfp4",
+              table_kind=synth.KIND_MXFP4_WIDE, config_id=30)
+    say(sp.name)
+    h = HostInputs(sp)
+    rb = synth.mxfp4_row_bytes(d)
+    hb = ng.HostBuffer(sp.R * rb)
+    try:
+        fill_host_table(sp, hb.numpy(np.uint8, (sp.R, rb)))
+        T = ng.Table(hb, sp.R, d, ng.TABLE_MXFP4)
+        di = DeviceInputs(sp, h, table=False)
+        rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+        eN = ng.ngram_embed_bag(T, rows)
+        stage = torch.empty(sp.n * 16 * rb, dtype=torch.uint8, device="cuda:0")
+        remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+        ng.ngram_gather_host(T, rows, stage, remap)
+        eN2 = ng.ngram_embed_bag(ng.Table(stage, sp.n * 16, d, ng.TABLE_MXFP4), remap)
+        pool = ng.RowPool(T, 50 + 16 * sp.n)
+        counts = ng.ngram_count_rows(rows, sp.R)
+        hot, sel = ng.ngram_select_hot_rows(counts, 50)
+        ng.ngram_pool_cache_rows(pool, hot, sel)
+        prow = ng.ngram_pool_gather(pool, rows)
+        eN3 = ng.ngram_embed_bag(pool.device_table(), prow)
+        torch.cuda.synchronize()
+        _, want, _ = expected(h)
+        for e in (eN, eN2, eN3):
+            assert np.array_equal(e.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    finally:
+        hb.free()

@@ -27,3 +27,16 @@ def test_fill_matches_numpy(kind, dt, npdt, offset):
     got = t.cpu().numpy().view(npdt)
     want = synth.tensor(kind, 0x1234_5678_9ABC_DEF0, 9, n, offset=offset).view(npdt)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("kind", [synth.KIND_MXFP4, synth.KIND_MXFP4_WIDE])
+@pytest.mark.parametrize("d,offset", [(128, 0), (2560, 3), (2560, 1360 * 7 + 5)])
+def test_mxfp4_fill_matches_numpy(kind, d, offset):
+    rb = synth.mxfp4_row_bytes(d)
+    nrows = 37
+    t = torch.empty(nrows * rb, dtype=torch.uint8, device="cuda:0")
+    synth.fill_gpu_mxfp4(kind, 0xABCDEF, 3, t, d, offset=offset)
+    torch.cuda.synchronize()
+    e = np.arange(offset, offset + nrows * rb, dtype=np.uint64)
+    want = synth.mxfp4_bytes(kind, synth.words(0xABCDEF, 3, e), e % np.uint64(rb), d)
+    assert np.array_equal(t.cpu().numpy(), want)
