@@ -552,13 +552,16 @@ def run_host(args):
     gate_s = timed(lambda: ng.ngram_gate_add(eN, di.tokens, di.W_g, out, e1=di.e1,
                                              residual=di.residual, stream=main), 5)
 
-    pcie_bytes = n * 16 * d * 2
-    achieved = pcie_bytes / gather_s / 1e9
+    # The bytes that cross PCIe: all 16 rows per token (zero copy, staged),
+    # or only the distinct uncached rows (pool).
+    pcie_bytes = nominal_pcie = n * 16 * d * 2
     if cache_info is not None:
         torch.cuda.synchronize()
         cache_info["rows_fetched_per_batch"] = int(fetched.item())
         cache_info["pcie_bytes_per_batch"] = int(fetched.item()) * d * 2
-        cache_info["pcie_GBps_actual"] = cache_info["pcie_bytes_per_batch"] / gather_s / 1e9
+        cache_info["nominal_GBps"] = nominal_pcie / gather_s / 1e9
+        pcie_bytes = cache_info["pcie_bytes_per_batch"]
+    achieved = pcie_bytes / gather_s / 1e9
     result = {
         "metric": METRIC,
         "value": n / gather_s,
