@@ -50,6 +50,12 @@ def lib():
         L.oracle_grad_table_rows.argtypes = [P, I64, I32, P, P, P, I64, P]
         L.oracle_grad_e1_tokens.argtypes = [P, P, I64, I32, P, P, I64, P]
         L.oracle_grad_gate.argtypes = [P, P, P, I64, I32, P]
+        F = ctypes.c_float
+        L.oracle_blocked_sumsq.restype = F
+        L.oracle_blocked_sumsq.argtypes = [P, I32]
+        L.oracle_blocked_dot2.restype = F
+        L.oracle_blocked_dot2.argtypes = [P, P, P, P, I32]
+        L.oracle_norm_gate_add.argtypes = [P, P, I64, I32, P, P, P, P, P, F, F, P, P, P, P]
         _lib = L
     return _lib
 
@@ -211,3 +217,28 @@ def grad_gate(rows, g, eN):
     out = np.zeros(d, dtype=np.float32)
     lib().oracle_grad_gate(_p(rows), _p(g), _p(eN), n, d, _p(out))
     return out
+
+
+def blocked_sumsq(x) -> np.float32:
+    x = _c(x, np.float32).reshape(-1)
+    return np.float32(lib().oracle_blocked_sumsq(_p(x), x.size))
+
+
+def blocked_dot2(a, b, c, e) -> np.float32:
+    a, b, c, e = (_c(z, np.float32).reshape(-1) for z in (a, b, c, e))
+    return np.float32(lib().oracle_blocked_dot2(_p(a), _p(b), _p(c), _p(e), a.size))
+
+
+def norm_gate_add(eN, e1_rows, e1, W_g, gamma, u, v, b, eps, residual=None):
+    """Normalised, input-gated fusion of the sums eN [n][d].  Returns (out
+    bf16 bits [n][d], stats fp32 [n][2] = (r, logit), y fp32 [n][d])."""
+    eN = _c(eN, np.float32)
+    n, d = eN.shape
+    out = np.zeros((n, d), dtype=np.uint16)
+    stats = np.zeros((n, 2), dtype=np.float32)
+    y = np.zeros((n, d), dtype=np.float32)
+    lib().oracle_norm_gate_add(_p(eN), _p(_c(e1_rows, np.int32)), n, d, _p(_c(e1, np.uint16)),
+                               _p(_c(W_g, np.float32)), _p(_c(gamma, np.float32)), _p(_c(u, np.float32)),
+                               _p(_c(v, np.float32)), float(np.float32(b)), float(np.float32(eps)),
+                               _p(_c(residual, np.uint16)), _p(out), _p(stats), _p(y))
+    return out, stats, y

@@ -321,3 +321,111 @@ void oracle_grad_gate(const int32_t* rows, const uint16_t* g, const float* eN, i
         out[j] = total;
     }
 }
+
+/*
+ * Normalised, input-gated fusion.  "Qwen 3.8 Flash-Next Deep Dive…" draws a
+ * "Projection / Normalization" stage between the table lookup and the trunk,
+ * and the summary of "Qwen3.8-Flash-Next: …" fuses the n-gram vector with the
+ * 1-gram embedding "via a gating network".  Neither page defines the two.
+ * Form taken (every step one IEEE fp32 operation):
+ *   S      = the blocked sum over j of eN[j] * eN[j];
+ *   r      = 1 / sqrt(S / d + eps);
+ *   n[j]   = (eN[j] * r) * gamma[j];                  RMS normalisation
+ *   Z      = the blocked sum over j of u[j] e1[j] + v[j] n[j];
+ *   logit  = Z + b;   alpha = 1 / (1 + exp(-logit));   sigmoid gate unit
+ *   h[j]   = fmaf(alpha * W_g[j], n[j], e1[j]);  y = residual + h (or h);
+ *   out[j] = bf16 round-to-nearest-even of y.
+ * The blocked sum fixes the order (d a multiple of 8):
+ *   - group g = columns 8g .. 8g+7: a chain of fmaf over its columns in
+ *     order, from +0 (for Z each column adds u e1, then v n);
+ *   - block c = groups 64c .. 64c+63 (512 columns; groups past the end are
+ *     +0): a pairwise tree, p[l] = p[l] + p[l + w] for w = 1, 2, 4, …, 32 and
+ *     l a multiple of 2w, the block's sum being p[0];
+ *   - the block sums added in block order, starting from block 0's.
+ */
+static float oracle_blocked_total(const float* group_sums, int32_t ngroups)
+{
+    float total = 0.0f;
+    for (int32_t c = 0; c * 64 < ngroups; ++c) {
+        float p[64];
+        for (int l = 0; l < 64; ++l)
+            p[l] = c * 64 + l < ngroups ? group_sums[c * 64 + l] : 0.0f;
+        for (int w = 1; w < 64; w *= 2)
+            for (int l = 0; l < 64; l += 2 * w)
+                p[l] = p[l] + p[l + w];
+        total = c == 0 ? p[0] : total + p[0];
+    }
+    return total;
+}
+
+/* Sum of squares of x[0..d) in the blocked order. */
+float oracle_blocked_sumsq(const float* x, int32_t d)
+{
+    const int32_t ng = d / 8;
+    float* gs = (float*)malloc(sizeof(float) * (size_t)(ng > 0 ? ng : 1));
+    for (int32_t g = 0; g < ng; ++g) {
+        float s = 0.0f;
+        for (int e = 0; e < 8; ++e)
+            s = fmaf(x[8 * g + e], x[8 * g + e], s);
+        gs[g] = s;
+    }
+    float total = oracle_blocked_total(gs, ng);
+    free(gs);
+    return total;
+}
+
+/* sum over j of a[j] b[j] + c[j] e[j] in the blocked order. */
+float oracle_blocked_dot2(const float* a, const float* b, const float* c, const float* e, int32_t d)
+{
+    const int32_t ng = d / 8;
+    float* gs = (float*)malloc(sizeof(float) * (size_t)(ng > 0 ? ng : 1));
+    for (int32_t g = 0; g < ng; ++g) {
+        float z = 0.0f;
+        for (int q = 0; q < 8; ++q) {
+            int32_t j = 8 * g + q;
+            z = fmaf(a[j], b[j], z);
+            z = fmaf(c[j], e[j], z);
+        }
+        gs[g] = z;
+    }
+    float total = oracle_blocked_total(gs, ng);
+    free(gs);
+    return total;
+}
+
+/* out[i][j] as above from the sums eN[n][d]; e1_rows[i] = w_t.  stats_out
+ * (may be NULL) gets {r, logit} per token, y_out (may be NULL) the fp32 y. */
+void oracle_norm_gate_add(const float* eN, const int32_t* e1_rows, int64_t n, int32_t d,
+                          const uint16_t* e1, const float* W_g, const float* gamma, const float* u,
+                          const float* v, float b, float eps, const uint16_t* residual,
+                          uint16_t* out, float* stats_out, float* y_out)
+{
+    float* nv = (float*)malloc(sizeof(float) * (size_t)d);
+    float* ev = (float*)malloc(sizeof(float) * (size_t)d);
+    for (int64_t i = 0; i < n; ++i) {
+        const float* x = eN + i * d;
+        float S = oracle_blocked_sumsq(x, d);
+        float r = 1.0f / sqrtf(S / (float)d + eps);
+        const uint16_t* e1_token = e1 + (int64_t)e1_rows[i] * d;
+        const uint16_t* res_token = residual ? residual + i * d : NULL;
+        for (int32_t j = 0; j < d; ++j) {
+            nv[j] = (x[j] * r) * gamma[j];
+            ev[j] = oracle_bf16_to_f32(e1_token[j]);
+        }
+        float logit = oracle_blocked_dot2(u, ev, v, nv, d) + b;
+        float alpha = 1.0f / (1.0f + expf(-logit));
+        for (int32_t j = 0; j < d; ++j) {
+            float h = fmaf(alpha * W_g[j], nv[j], ev[j]);
+            float y = res_token ? oracle_bf16_to_f32(res_token[j]) + h : h;
+            out[i * d + j] = oracle_bf16_rne(y);
+            if (y_out)
+                y_out[i * d + j] = y;
+        }
+        if (stats_out) {
+            stats_out[2 * i] = r;
+            stats_out[2 * i + 1] = logit;
+        }
+    }
+    free(nv);
+    free(ev);
+}

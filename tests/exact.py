@@ -44,3 +44,26 @@ def f(x) -> Fraction:
 
 def bf16_bits_to_f32(b) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _f32_neighbours(c: np.float32):
+    return (np.nextafter(c, np.float32(-np.inf), dtype=np.float32), c,
+            np.nextafter(c, np.float32(np.inf), dtype=np.float32))
+
+
+def round_sqrt_f32(q: Fraction) -> np.float32:
+    """The fp32 nearest to sqrt(q) for a rational q >= 0 (correct rounding),
+    found by bracketing sqrt(q) between the exact midpoints of fp32
+    neighbours: c is the answer iff mid(c-, c)^2 <= q <= mid(c, c+)^2."""
+    if q == 0:
+        return np.float32(0.0)
+    c = np.float32(np.sqrt(float(q)))
+    for _ in range(4):
+        lo_n, _, hi_n = _f32_neighbours(c)
+        lo = (f(lo_n) + f(c)) / 2
+        hi = (f(c) + f(hi_n)) / 2
+        if lo * lo <= q <= hi * hi:
+            assert lo * lo != q and hi * hi != q, "tie"
+            return c
+        c = lo_n if q < lo * lo else hi_n
+    raise AssertionError("no fp32 bracket found")

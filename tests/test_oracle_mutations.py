@@ -65,6 +65,26 @@ MUTATIONS = {
     "mxfp4_nan_scale_ignored": ("    if (E == 255)\n        return NAN;\n", ""),
     "grad_gate_keeps_invalid": ("if (rows[i * ORACLE_K] < 0)\n                    continue;\n                part",
                                 "part"),
+    "norm_drops_eps": ("sqrtf(S / (float)d + eps)", "sqrtf(S / (float)d)"),
+    "norm_mean_over_d_minus_1": ("sqrtf(S / (float)d + eps)", "sqrtf(S / (float)(d - 1) + eps)"),
+    "norm_no_gamma": ("nv[j] = (x[j] * r) * gamma[j];", "nv[j] = x[j] * r;"),
+    "norm_rsqrt_unfused_order": ("nv[j] = (x[j] * r) * gamma[j];", "nv[j] = x[j] * (r * gamma[j]);"),
+    "gate_sign_flipped": ("expf(-logit)", "expf(logit)"),
+    "gate_uv_swapped": ("oracle_blocked_dot2(u, ev, v, nv, d)", "oracle_blocked_dot2(v, ev, u, nv, d)"),
+    "gate_no_bias": ("oracle_blocked_dot2(u, ev, v, nv, d) + b;", "oracle_blocked_dot2(u, ev, v, nv, d);"),
+    "gate_alpha_not_applied": ("fmaf(alpha * W_g[j], nv[j], ev[j])", "fmaf(W_g[j], nv[j], ev[j])"),
+    "gate_uses_raw_sum": ("fmaf(alpha * W_g[j], nv[j], ev[j])", "fmaf(alpha * W_g[j], x[j], ev[j])"),
+    "blocked_tree_sequential": ("for (int w = 1; w < 64; w *= 2)\n            for (int l = 0; l < 64; l += 2 * w)\n"
+                                "                p[l] = p[l] + p[l + w];",
+                                "for (int l = 1; l < 64; ++l)\n            p[0] = p[0] + p[l];"),
+    "blocked_group_unfused": ("s = fmaf(x[8 * g + e], x[8 * g + e], s);", "s = x[8 * g + e] * x[8 * g + e] + s;"),
+    "blocked_skips_last_group": ("for (int32_t g = 0; g < ng; ++g) {\n        float s", "for (int32_t g = 0; g + 1 < ng; ++g) {\n        float s"),
+    "norm_gate_wrong_e1_row": ("const uint16_t* e1_token = e1 + (int64_t)e1_rows[i] * d;",
+                               "const uint16_t* e1_token = e1 + (int64_t)(e1_rows[i] + 1) * d;"),
+    "norm_gate_drops_residual": ("const uint16_t* res_token = residual ? residual + i * d : NULL;",
+                                 "const uint16_t* res_token = NULL;"),
+    "dot_terms_reordered": ("            z = fmaf(a[j], b[j], z);\n            z = fmaf(c[j], e[j], z);",
+                            "            z = fmaf(c[j], e[j], z);\n            z = fmaf(a[j], b[j], z);"),
 }
 
 
@@ -81,6 +101,7 @@ def test_pins_catch_mutation(name, tmp_path):
     env = dict(os.environ, ORACLE_LIB=str(mlib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py",
-                        "tests/test_oracle_grad.py", "tests/test_oracle_mxfp4.py"],
+                        "tests/test_oracle_grad.py", "tests/test_oracle_mxfp4.py",
+                        "tests/test_oracle_norm_gate.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
