@@ -86,7 +86,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "int8", "fp4", "decode1", "decode2", "decode4", "host", "backward"])
+                    choices=["prefill", "int8", "fp4", "gated", "decode1", "decode2", "decode4", "host",
+                             "backward"])
     ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged", "pool"],
                     help="host workload: sum straight from pinned memory, stage rows in HBM first, or go "
                          "through an HBM row pool (hot-row cache + per-batch dedup)")
@@ -106,7 +107,7 @@ def parse():
 
 
 def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, max_seconds=20.0,
-                 mxfp4_d=None):
+                 mxfp4_d=None, gate=None):
     """The oracle timed on the host cores on a bounded sample of the
     workload: the whole batch, sequence by sequence, hashed into a host copy
     of the first ``R_cpu`` table rows (the full table does not fit in host
@@ -125,9 +126,18 @@ def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, 
 
     def one(s):
         a, b = int(offs[s]), int(offs[s + 1])
-        oracle.forward(toks[a:b], np.array([0, b - a], np.int32), table_np, host_inputs.W_g,
-                       e1=e1_np, residual=None if res_np is None else res_np[a:b],
-                       history=None if hist is None else hist[s:s + 1], scale=scale_np, mxfp4_d=mxfp4_d)
+        so = np.array([0, b - a], np.int32)
+        res = None if res_np is None else res_np[a:b]
+        hs = None if hist is None else hist[s:s + 1]
+        if gate is None:
+            oracle.forward(toks[a:b], so, table_np, host_inputs.W_g, e1=e1_np, residual=res,
+                           history=hs, scale=scale_np, mxfp4_d=mxfp4_d)
+        else:
+            # the gated path's steps: hash, sum, normalised gated fusion
+            rows = oracle.hash_rows(toks[a:b], so, R_cpu, hs)
+            eN = oracle.embed_bag_bf16(table_np, rows)
+            oracle.norm_gate_add(eN, toks[a:b], e1_np, host_inputs.W_g, gate.gamma, gate.u, gate.v,
+                                 gate.b, gate.eps, res)
         return b - a
 
     passes = tokens_done = 0
@@ -144,8 +154,9 @@ def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, 
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{passes} pass(es) over the {len(toks)}-token batch ({nseq} sequences, one "
-                   f"oracle_forward call per sequence on {threads} threads); rows hashed mod "
+        "sample": (f"{passes} pass(es) over the {len(toks)}-token batch ({nseq} sequences, "
+                   f"{'the oracle hash, sum and normalised gated fusion' if gate is not None else 'one oracle_forward call'}"
+                   f" per sequence on {threads} threads); rows hashed mod "
                    f"{R_cpu} into a {table_np.nbytes / 2**30:.2f} GiB host copy of the first "
                    f"{R_cpu} table rows (the full table does not fit in host memory); "
                    f"host copy prep {prep_s:.1f} s, not timed"),
@@ -247,10 +258,22 @@ def main():
     setup_s = time.time() - t_setup
 
     stream = torch.cuda.current_stream()
+    gated = args.workload == "gated"
+    if gated:
+        from synth.workloads import gate_params
+        gp = gate_params(spec)
+        g_gamma, g_u, g_v = (torch.from_numpy(a).to(dev) for a in (gp.gamma, gp.u, gp.v))
+
+    def launch(tok, off, hist, res, out, stream=None):
+        if gated:
+            ng.ngram_forward_gated(tok, off, T, W_g, g_gamma, g_u, g_v, gp.b, gp.eps, out, e1,
+                                   residual=res, history=hist, stream=stream)
+        else:
+            ng.ngram_forward(tok, off, T, W_g, out, e1=e1, residual=res, history=hist, stream=stream)
 
     def step(i):
         tok, off, hist, res, out = batches[i % nb]
-        ng.ngram_forward(tok, off, T, W_g, out, e1=e1, residual=res, history=hist, stream=stream)
+        launch(tok, off, hist, res, out, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -261,8 +284,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(nb):
-                tok, off, hist, res, out = batches[i]
-                ng.ngram_forward(tok, off, T, W_g, out, e1=e1, residual=res, history=hist)
+                launch(*batches[i])
         reps = max(1, args.steps // nb)
         for _ in range(2):
             g.replay()
@@ -292,7 +314,7 @@ def main():
         mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
 
     bpt = nominal_bytes_per_token(d, spec.table, spec.e1, spec.residual)
-    bytes_per_launch = bpt * n + 4 * d
+    bytes_per_launch = bpt * n + 4 * d * (4 if gated else 1)          # W_g (+ gamma, u, v) once per launch
     achieved = bytes_per_launch / mean_launch_s / 1e9
     traffic = measured_traffic(args.workload if args.dist == "zipf" else f"{args.workload}_{args.dist}")
 
@@ -331,7 +353,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "kernel": "ngram_fwd_kernel",
+            "kernel": "ngram_gated_kernel" if gated else "ngram_fwd_kernel",
             "algorithmic_bytes_per_token": bpt,
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "mean_launch_us": mean_launch_s * 1e6,
@@ -356,7 +378,8 @@ def main():
         res_np = None if batches[0][3] is None else batches[0][3].cpu().numpy().view(np.uint16).reshape(n, d)
         result["cpu_baseline"] = cpu_baseline(HostInputs(spec.replace(R=R_cpu)), table_np, scale_np,
                                               e1_np, res_np, R_cpu, time.time() - tp,
-                                              mxfp4_d=d if spec.table == "mxfp4" else None)
+                                              mxfp4_d=d if spec.table == "mxfp4" else None,
+                                              gate=gp if gated else None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

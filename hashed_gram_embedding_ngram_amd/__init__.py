@@ -54,6 +54,8 @@ _SIGNATURES = {
     "ngram_gate_add": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P]),
     "ngram_forward": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, ctypes.POINTER(_Table), _P, _I64,
                                      _P, _P, _P, _P, _P]),
+    "ngram_forward_gated": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, ctypes.POINTER(_Table), _P, _I64,
+                                           _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _P]),
     "ngram_host_alloc": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
     "ngram_host_free": (ctypes.c_int, [_P]),
     "ngram_gather_host": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, _P, _P, _P]),
@@ -287,6 +289,37 @@ def ngram_forward(tokens, seq_offsets, table: Table, W_g, out, e1=None, residual
                                _ptr(history), _seeds_arg(seeds), table.c, _ptr(e1), V, _ptr(W_g),
                                _ptr(residual), _ptr(out), _ptr(rows_out), _stream(stream)),
            "ngram_forward")
+    return out
+
+
+def ngram_forward_gated(tokens, seq_offsets, table: Table, W_g, gamma, u, v, b, eps, out, e1,
+                        residual=None, history=None, seeds=None, rows_out=None, stats_out=None, stream=None):
+    """Normalised, input-gated forward (see ngram_forward_gated in ngram.h);
+    ``stats_out`` [n][2] fp32 receives (r, logit) per token."""
+    _dev(tokens, _I32T, "tokens")
+    _dev(seq_offsets, _I32T, "seq_offsets")
+    _dev(history, _I32T, "history", allow_none=True)
+    for t, name in ((W_g, "W_g"), (gamma, "gamma"), (u, "u"), (v, "v")):
+        _dev(t, _F32, name)
+    _dev(out, _BF16, "out")
+    _dev(e1, _BF16, "e1")
+    _dev(residual, _BF16, "residual", allow_none=True)
+    _dev(rows_out, _I32T, "rows_out", allow_none=True)
+    _dev(stats_out, _F32, "stats_out", allow_none=True)
+    V = _vocab(e1, table.d)
+    n, d = tokens.numel(), table.d
+    for t, name in ((W_g, "W_g"), (gamma, "gamma"), (u, "u"), (v, "v")):
+        _need(t, d, name)
+    _need(out, n * d, "out")
+    _need(residual, n * d, "residual")
+    _need(rows_out, n * K, "rows_out")
+    _need(stats_out, 2 * n, "stats_out")
+    _need(history, 2 * (seq_offsets.numel() - 1), "history")
+    _check(lib().ngram_forward_gated(_ptr(tokens), n, _ptr(seq_offsets), seq_offsets.numel() - 1,
+                                     _ptr(history), _seeds_arg(seeds), table.c, _ptr(e1), V, _ptr(W_g),
+                                     _ptr(gamma), _ptr(u), _ptr(v), float(b), float(eps), _ptr(residual),
+                                     _ptr(out), _ptr(rows_out), _ptr(stats_out), _stream(stream)),
+           "ngram_forward_gated")
     return out
 
 

@@ -25,6 +25,8 @@
 // lane: the residual is read once and written once.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -377,14 +379,9 @@ struct FwdArgs {
     Seeds sd;
 };
 
-// One tile: hash its tokens' rows into LDS, then each wavefront gathers,
-// sums, gates and stores its slices of every token of the tile.
-template <int DT, bool E1, bool RES>
-__device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nwaves = blockDim.x >> 6;
-    const int64_t d = a.d;
-    const int nslices = (a.d + kSlice - 1) / kSlice;
+// A tile's hash phase: one thread per (token, k) writes the row id into LDS
+// (and rows_out), and w_t per token; -1 marks an invalid token.
+__device__ inline void hash_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok) {
     for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
         const int tl = t >> 4, k = t & (kK - 1);
         const int64_t i = tile0 + tl;
@@ -401,6 +398,17 @@ __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows,
         if (k == 0) ltok[tl] = c0;
     }
     __syncthreads();
+}
+
+// One tile: hash its tokens' rows into LDS, then each wavefront gathers,
+// sums, gates and stores its slices of every token of the tile.
+template <int DT, bool E1, bool RES>
+__device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t d = a.d;
+    const int nslices = (a.d + kSlice - 1) / kSlice;
+    hash_tile(a, tile0, lrows, ltok);
 
     const int64_t rem = a.n - tile0;
     const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
@@ -426,6 +434,166 @@ __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows,
             const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
             const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
             store_out(o, gate8<E1, RES>(acc, w, e1row, resrow));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Normalised, input-gated fusion ("Qwen 3.8 Flash-Next Deep Dive…": a
+// "Projection / Normalization" stage after the lookup; "Qwen3.8-Flash-Next:
+// …", summary: fusion "via a gating network"; the pages define neither, the
+// form taken is):
+//   r = 1 / sqrt(S / d + eps),  S = blocked sum of eN[j]^2,
+//   n[j] = (eN[j] * r) * gamma[j],
+//   logit = Z + b,  Z = blocked sum of u[j] e1[j] + v[j] n[j],
+//   alpha = 1 / (1 + exp(-logit)),
+//   out[j] = bf16(residual[j] + fmaf(alpha * W_g[j], n[j], e1[j])).
+// The blocked order maps onto the workgroup: a lane's 8 columns are one group
+// (an fma chain), a wavefront's 64 groups one block (a pairwise tree, which
+// the xor butterfly below computes in every lane), and the block sums are
+// added in block order from LDS.
+struct GatedArgs {
+    FwdArgs f;
+    const float* gamma;
+    const float* u;
+    const float* v;
+    float* stats;       // [n][2] = (r, logit), or null
+    float b;
+    float eps;
+};
+
+// The pairwise tree over the wavefront's 64 lanes in lane order: at width w
+// lane l adds lane l ^ w, i.e. left + right in the tree's left lanes and the
+// same sum (commuted, hence bit-identical) in its right lanes.
+__device__ inline float wave_tree_sum(float x) {
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) x = x + __shfl_xor(x, w, 64);
+    return x;
+}
+
+__device__ inline void load_f8(float w[8], const float* __restrict__ p, int64_t j0) {
+    const float4 a = *reinterpret_cast<const float4*>(p + j0);
+    const float4 b = *reinterpret_cast<const float4*>(p + j0 + 4);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// One tile: wavefront w owns columns 512w .. 512w+511 (one block; the launch
+// has one wavefront per block).  Each token takes two workgroup barriers, one
+// per blocked sum; a token's validity is uniform over the workgroup, so every
+// wavefront reaches the same barriers.
+template <int DT, bool RES>
+__device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lrows, int32_t* ltok, float* lred) {
+    const FwdArgs& a = g.f;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t d = a.d;
+    const int64_t j0 = static_cast<int64_t>(wave) * kSlice + lane * kVec;
+    const bool col = j0 < d;
+    hash_tile(a, tile0, lrows, ltok);
+
+    const int64_t rem = a.n - tile0;
+    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+    for (int tl = 0; tl < tile_n; ++tl) {
+        const int64_t i = tile0 + tl;
+        uint16_t* o = a.out + i * d + j0;
+        const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
+        if (c0 < 0) {
+            if (col) {
+                const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
+                *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
+            }
+            if (g.stats && threadIdx.x == 0) {
+                g.stats[2 * i] = __uint_as_float(kNaNf32);
+                g.stats[2 * i + 1] = __uint_as_float(kNaNf32);
+            }
+            continue;
+        }
+        float* red = lred + tl * 2 * nwaves;         // [2][nwaves], one slot set per token
+        float acc[8];
+        if (col) {
+            int32_t r[kK];
+#pragma unroll
+            for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
+            gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+        }
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = __builtin_fmaf(acc[e], acc[e], s);
+        s = wave_tree_sum(s);
+        if (lane == 0) red[wave] = s;
+        __syncthreads();
+        float S = red[0];
+        for (int w = 1; w < nwaves; ++w) S = S + red[w];
+        const float rn = 1.0f / sqrtf(S / static_cast<float>(d) + g.eps);
+
+        float nv[8], ev[8];
+        float z = 0.0f;
+        if (col) {
+            float gm[8], uu[8], vv[8];
+            load_f8(gm, g.gamma, j0);
+            load_f8(uu, g.u, j0);
+            load_f8(vv, g.v, j0);
+            const uint4 e1v = *reinterpret_cast<const uint4*>(a.e1 + static_cast<int64_t>(c0) * d + j0);
+            ev[0] = bf16lo(e1v.x); ev[1] = bf16hi(e1v.x); ev[2] = bf16lo(e1v.y); ev[3] = bf16hi(e1v.y);
+            ev[4] = bf16lo(e1v.z); ev[5] = bf16hi(e1v.z); ev[6] = bf16lo(e1v.w); ev[7] = bf16hi(e1v.w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                nv[e] = (acc[e] * rn) * gm[e];
+                z = __builtin_fmaf(uu[e], ev[e], z);
+                z = __builtin_fmaf(vv[e], nv[e], z);
+            }
+        }
+        z = wave_tree_sum(z);
+        if (lane == 0) red[nwaves + wave] = z;
+        __syncthreads();
+        float Z = red[nwaves];
+        for (int w = 1; w < nwaves; ++w) Z = Z + red[nwaves + w];
+        const float logit = Z + g.b;
+        const float alpha = 1.0f / (1.0f + expf(-logit));
+        if (col) {
+            float w8[8];
+            load_w8(w8, a.wg, j0);
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = __builtin_fmaf(alpha * w8[e], nv[e], ev[e]);
+            if constexpr (RES) {
+                const uint4 rv = *reinterpret_cast<const uint4*>(a.res + i * d + j0);
+                y[0] = bf16lo(rv.x) + y[0]; y[1] = bf16hi(rv.x) + y[1];
+                y[2] = bf16lo(rv.y) + y[2]; y[3] = bf16hi(rv.y) + y[3];
+                y[4] = bf16lo(rv.z) + y[4]; y[5] = bf16hi(rv.z) + y[5];
+                y[6] = bf16lo(rv.w) + y[6]; y[7] = bf16hi(rv.w) + y[7];
+            }
+            uint4 ov;
+            ov.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
+            ov.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
+            ov.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
+            ov.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
+            store_out(o, ov);
+        }
+        if (g.stats && threadIdx.x == 0) {
+            g.stats[2 * i] = rn;
+            g.stats[2 * i + 1] = logit;
+        }
+    }
+}
+
+template <int DT, bool RES, bool PERSIST>
+__global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
+    extern __shared__ int32_t lds[];
+    int32_t* lrows = lds;                                            // [tpw][16]
+    int32_t* ltok = lds + g.f.tpw * kK;                              // [tpw]
+    float* lred = reinterpret_cast<float*>(lds + g.f.tpw * (kK + 1));  // [tpw][2][nwaves]
+    if constexpr (!PERSIST) {
+        gated_tile<DT, RES>(g, static_cast<int64_t>(blockIdx.x) * g.f.tpw, lrows, ltok, lred);
+    } else {
+        const int64_t ntiles = (g.f.n + g.f.tpw - 1) / g.f.tpw;
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+            gated_tile<DT, RES>(g, tile * g.f.tpw, lrows, ltok, lred);
+            __syncthreads();              // the next tile rewrites the LDS lists
         }
     }
 }
@@ -1374,6 +1542,22 @@ void launch_fwd_dt(const FwdArgs& a, const Shape& sh, hipStream_t st) {
     else launch_fwd<DT, false, false>(a, sh, st);
 }
 
+// The gated kernel: one wavefront per 512-column block (d <= 8192).
+template <int DT>
+void launch_gated_dt(const GatedArgs& g, const Shape& sh, hipStream_t st) {
+    const int nb = (g.f.d + kSlice - 1) / kSlice;
+    const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * nb);
+    const size_t lds = static_cast<size_t>(sh.tpw) * ((kK + 1) * sizeof(int32_t) + 2 * nb * sizeof(float));
+    const bool res = g.f.res != nullptr;
+    if (sh.persist) {
+        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, true>), grid, block, lds, st, g);
+        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, true>), grid, block, lds, st, g);
+    } else {
+        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, false>), grid, block, lds, st, g);
+        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, false>), grid, block, lds, st, g);
+    }
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1512,6 +1696,46 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
     else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) launch_fwd_dt<NGRAM_TABLE_INT8_ROWSCALE>(a, sh, stream);
     else launch_fwd_dt<NGRAM_TABLE_MXFP4>(a, sh, stream);
     return hip_status("ngram_forward launch");
+}
+
+int ngram_forward_gated(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                        const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                        const uint16_t* e1, int64_t V, const float* W_g, const float* gamma, const float* u,
+                        const float* v, float b, float eps, const uint16_t* residual, uint16_t* out,
+                        int32_t* rows_out, float* stats_out, ngram_stream_t stream) {
+    g_err[0] = 0;
+    int rc = check_tokens(tokens, n, seq_offsets, S);
+    if (rc) return rc;
+    rc = check_table(T);
+    if (rc) return rc;
+    if (T->d > 16 * kSlice) return fail(NGRAM_ERANGE, "d=%d above %d for the gated path", T->d, 16 * kSlice);
+    if (!W_g || !gamma || !u || !v || !e1) return fail(NGRAM_EINVAL, "W_g, gamma, u, v or e1 is NULL");
+    if (V < 1) return fail(NGRAM_ERANGE, "V=%lld must be >= 1", (long long)V);
+    if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(b))
+        return fail(NGRAM_EINVAL, "eps must be finite and >= 0, b finite");
+    if (n > 0 && !out) return fail(NGRAM_EINVAL, "out is NULL");
+    if (!aligned(W_g, 16) || !aligned(gamma, 16) || !aligned(u, 16) || !aligned(v, 16) || !aligned(e1, 16) ||
+        (residual && !aligned(residual, 16)) || (n > 0 && !aligned(out, 16)) || (stats_out && !aligned(stats_out, 8)))
+        return fail(NGRAM_EALIGN, "e1, W_g, gamma, u, v, residual and out must be 16-byte aligned, stats_out 8");
+    if (n == 0) return NGRAM_OK;
+    const void* tab = nullptr;
+    rc = table_device_ptr(T, &tab);
+    if (rc) return rc;
+    GatedArgs g;
+    FwdArgs& a = g.f;
+    a.tok = tokens; a.so = seq_offsets; a.hist = history; a.tab = tab; a.scale = T->row_scale;
+    a.e1 = e1; a.wg = W_g; a.res = residual; a.out = out; a.rows_out = rows_out;
+    a.n = n; a.R = static_cast<uint64_t>(T->R); a.S = S; a.d = T->d;
+    a.c0_limit = c0_limit_for(e1, V);
+    a.sd = make_seeds(seeds);
+    g.gamma = gamma; g.u = u; g.v = v; g.stats = stats_out; g.b = b; g.eps = eps;
+    Shape sh = slice_shape(n, T->d, T->dtype);
+    cap_for_host(sh, T);
+    a.tpw = sh.tpw;
+    if (T->dtype == NGRAM_TABLE_BF16) launch_gated_dt<NGRAM_TABLE_BF16>(g, sh, stream);
+    else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) launch_gated_dt<NGRAM_TABLE_INT8_ROWSCALE>(g, sh, stream);
+    else launch_gated_dt<NGRAM_TABLE_MXFP4>(g, sh, stream);
+    return hip_status("ngram_forward_gated launch");
 }
 
 int ngram_host_alloc(int64_t bytes, void** host_ptr) {

@@ -134,6 +134,32 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
                   const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
                   uint16_t* out, int32_t* rows_out, ngram_stream_t stream);
 
+/* Normalised, input-gated variant of ngram_forward.  "Qwen 3.8 Flash-Next
+ * Deep Dive…" draws a "Projection / Normalization" stage after the lookup and
+ * "Qwen3.8-Flash-Next: …" (summary) fuses the n-gram and 1-gram vectors "via a
+ * gating network"; neither is defined there.  Form taken, per token, from its
+ * fp32 sum eN:
+ *   r      = 1 / sqrt(S / d + eps),   S = blocked sum over j of eN[j]^2;
+ *   n[j]   = (eN[j] * r) * gamma[j];
+ *   logit  = Z + b,   Z = blocked sum over j of u[j] e1[j] + v[j] n[j];
+ *   alpha  = 1 / (1 + exp(-logit));
+ *   out[j] = bf16(residual[j] + fmaf(alpha * W_g[j], n[j], e1[w_t][j])).
+ * Blocked sum: groups of 8 columns (an fmaf chain in column order; for Z each
+ * column adds u e1 then v n), blocks of 64 groups (a pairwise tree in group
+ * order, missing groups +0), block sums added in block order.  Every step is
+ * one IEEE fp32 operation except exp, so r and logit are reproducible bit for
+ * bit; alpha may differ from another libm's by an ulp or so.
+ * e1 [V][d] bf16 is required; gamma, u, v [d] fp32 (device, 16-byte aligned);
+ * eps finite >= 0, b finite; d <= 8192 (ERANGE).  stats_out [n][2] fp32
+ * (device, may be NULL) receives (r, logit) per token, NaN for an invalid
+ * token.  Other arguments and rules as ngram_forward. */
+int ngram_forward_gated(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                        const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                        const uint16_t* e1, int64_t V, const float* W_g, const float* gamma,
+                        const float* u, const float* v, float b, float eps,
+                        const uint16_t* residual, uint16_t* out, int32_t* rows_out,
+                        float* stats_out, ngram_stream_t stream);
+
 /* Pinned-host-table path, "N-grams, of all things" / "Which is why the
  * offload matters more than the parameter count": the table shard sits in
  * pinned host memory and the selected rows are gathered by the GPU over PCIe

@@ -49,6 +49,9 @@ TAG_WG = 4
 TAG_RESIDUAL = 5
 TAG_SCALE = 6
 TAG_HISTORY = 7
+TAG_GAMMA = 8
+TAG_GATE_U = 9
+TAG_GATE_V = 10
 
 KIND_BF16_NORMAL12 = 0   # sigma 0.018
 KIND_BF16_NORMAL6 = 1    # sigma 1.15

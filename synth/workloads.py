@@ -16,6 +16,9 @@ Workload shapes (the model the pages describe: 20M-row, 2560-wide table,
             host memory; e1, W_g, residual as prefill.
 * int8:     16 x 4096 tokens, Zipf(1.2); table 20,000,000 x 2560 int8 with a
             per-row fp32 scale; e1, W_g, residual as prefill.
+* fp4:      the prefill batch over a 20,000,000 x 2560 MXFP4 table.
+* gated:    the prefill batch and bf16 table through the normalised, gated
+            fusion, with its parameters from gate_params().
 """
 from __future__ import annotations
 
@@ -24,7 +27,8 @@ import dataclasses
 import numpy as np
 
 from . import (KIND_BF16_NORMAL6, KIND_BF16_NORMAL12, KIND_F32_SCALE, KIND_F32_UNIT,
-               KIND_I8_NORMAL, KIND_MXFP4, mxfp4_row_bytes, mxfp4_rows, TAG_E1, TAG_HISTORY, TAG_RESIDUAL, TAG_SCALE, TAG_TABLE,
+               KIND_I8_NORMAL, KIND_MXFP4, mxfp4_row_bytes, mxfp4_rows, TAG_E1, TAG_GAMMA, TAG_GATE_U,
+               TAG_GATE_V, TAG_HISTORY, TAG_RESIDUAL, TAG_SCALE, TAG_TABLE,
                TAG_TOKENS, TAG_WG, as_f32, ragged_offsets, rows, tensor, tokens, value_bits,
                words, workload_seed)
 
@@ -75,7 +79,28 @@ CONFIGS = {
     # the prefill batch over a 4-bit table: 20M x (1280 + 80) bytes = 27.2 GB
     "fp4": Spec("fp4", (4096,) * 8, VOCAB, BIG_R, D, table="mxfp4", table_kind=KIND_MXFP4, residual=True,
                 config_id=6),
+    "gated": Spec("gated", (4096,) * 8, VOCAB, BIG_R, D, residual=True, config_id=7),
 }
+
+
+@dataclasses.dataclass
+class GateParams:
+    gamma: np.ndarray     # [d] fp32 in [0.5, 1.5)
+    u: np.ndarray         # [d] fp32 in [-0.5, 0.5)
+    v: np.ndarray         # [d] fp32 in [-2^-5, 2^-5)
+    b: float
+    eps: float
+
+
+def gate_params(spec: Spec, b: float = 0.25, eps: float = 1e-6) -> GateParams:
+    """Parameters of the normalised, gated fusion: exact fp32 shifts and
+    power-of-two scalings of unit uniforms (Philox, tags 8..10)."""
+    s, d = spec.seed, spec.d
+    unit = lambda tag: as_f32(tensor(KIND_F32_UNIT, s, tag, d))
+    gamma = (unit(TAG_GAMMA) + np.float32(0.5)).astype(np.float32)
+    u = (unit(TAG_GATE_U) - np.float32(0.5)).astype(np.float32)
+    v = ((unit(TAG_GATE_V) - np.float32(0.5)) * np.float32(2.0 ** -4)).astype(np.float32)
+    return GateParams(gamma, u, v, float(np.float32(b)), float(np.float32(eps)))
 
 
 class HostInputs:

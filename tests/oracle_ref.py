@@ -8,9 +8,10 @@ import numpy as np
 import oracle
 
 
-def expected(h, sample=None, rows_all=None):
-    """(rows [n][16] for all tokens, eN [m][d], out [m][d] bf16 bits) for the
-    m sampled tokens (all tokens when ``sample`` is None)."""
+def _sampled(h, sample, rows_all):
+    """The oracle's row ids for all tokens, and for the sampled tokens their
+    sums eN, their e1 row indices into a compact e1 (or the token ids when
+    the workload has no e1), that compact e1 and their residual rows."""
     sp = h.spec
     if rows_all is None:
         rows_all = oracle.hash_rows(h.tokens, h.offsets, sp.R, h.history)
@@ -26,15 +27,36 @@ def expected(h, sample=None, rows_all=None):
     else:
         eN = oracle.embed_bag_bf16(Tc, remap)
     toks = h.tokens[idx]
-    e1c = ids = None
+    e1c = None
     if sp.e1:
         u1, inv1 = np.unique(toks, return_inverse=True)
         e1c, ids = h.e1_rows(u1), inv1.astype(np.int32)
     else:
         ids = toks
     res = h.residual_rows(idx) if sp.residual else None
+    return rows_all, eN, ids, e1c, res
+
+
+def expected(h, sample=None, rows_all=None):
+    """(rows [n][16] for all tokens, eN [m][d], out [m][d] bf16 bits) for the
+    m sampled tokens (all tokens when ``sample`` is None)."""
+    rows_all, eN, ids, e1c, res = _sampled(h, sample, rows_all)
     out = oracle.gate_add(eN, ids, h.W_g, e1c, res)
     return rows_all, eN, out
+
+
+def expected_gated(h, gp, sample=None, rows_all=None):
+    """The normalised, gated fusion with parameters ``gp``: (rows [n][16],
+    out [m][d] bf16 bits, stats [m][2] = (r, logit), y [m][d] fp32, mag
+    [m][d] = |residual| + |e1| + |y - residual - e1| in float64, the size of
+    the terms y is made of)."""
+    rows_all, eN, ids, e1c, res = _sampled(h, sample, rows_all)
+    out, stats, y = oracle.norm_gate_add(eN, ids, e1c, h.W_g, gp.gamma, gp.u, gp.v, gp.b, gp.eps, res)
+    f = lambda b: (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    e1v = f(e1c[ids])
+    rv = f(res) if res is not None else np.zeros_like(e1v)
+    mag = np.abs(rv) + np.abs(e1v) + np.abs(y.astype(np.float64) - rv - e1v)
+    return rows_all, out, stats, y, mag
 
 
 def sample_tokens(spec, m=64, seed=0):

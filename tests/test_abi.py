@@ -223,3 +223,23 @@ def test_grad_argument_checks():
     assert L.ngram_grad_e1(A, A, 4, 64, 100, A, A, A, None, AW, W, None) == EINVAL
     assert L.ngram_grad_gate(A, A, A, 4, 64, None, AW, W, None) == EINVAL
     assert L.ngram_grad_gate(A, A, A + 4, 4, 64, A, AW, W, None) == EINVAL
+
+
+def test_gated_checks():
+    L = ng.lib()
+
+    def call(t=None, n=4, e1=A, W=A, gamma=A, u=A, v=A, b=0.0, eps=1e-6, res=None, out=A, stats=None, V=10):
+        t = t or _table(d=64)
+        return L.ngram_forward_gated(A, n, A, 1, None, None, ctypes.byref(t), e1, V, W, gamma, u, v, b, eps,
+                                     res, out, None, stats, None)
+
+    assert call(e1=None) == EINVAL
+    assert call(gamma=None) == EINVAL and call(u=None) == EINVAL and call(v=None) == EINVAL
+    assert call(W=None) == EINVAL
+    assert call(eps=-1.0) == EINVAL and call(eps=float("nan")) == EINVAL and call(eps=float("inf")) == EINVAL
+    assert call(b=float("inf")) == EINVAL and call(b=float("nan")) == EINVAL
+    assert call(V=0) == ERANGE
+    assert call(t=_table(d=8200)) == ERANGE and "gated" in _err()
+    assert call(gamma=A + 4) == EALIGN and call(u=A + 8) == EALIGN and call(stats=A + 4) == EALIGN
+    assert call(out=None) == EINVAL
+    assert call(n=0, out=None) == OK                                  # empty: no launch
