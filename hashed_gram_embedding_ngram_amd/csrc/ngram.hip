@@ -482,26 +482,25 @@ __device__ inline void load_f8(float w[8], const float* __restrict__ p, int64_t 
 // has one wavefront per block).  Each token takes two workgroup barriers, one
 // per blocked sum; a token's validity is uniform over the workgroup, so every
 // wavefront reaches the same barriers.
-template <int DT, bool RES>
+template <int DT, bool RES, bool FULL>
 __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lrows, int32_t* ltok, float* lred) {
     const FwdArgs& a = g.f;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
-    const int64_t j0 = static_cast<int64_t>(wave) * kSlice + lane * kVec;
-    const bool col = j0 < d;
+    const uint32_t jl = static_cast<uint32_t>(wave * kSlice + lane * kVec);   // the lane's first column
+    const bool col = FULL || jl < static_cast<uint32_t>(d);  // FULL: d a multiple of 512, all lanes have columns
     hash_tile(a, tile0, lrows, ltok);
 
     const int64_t rem = a.n - tile0;
     const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
     for (int tl = 0; tl < tile_n; ++tl) {
         const int64_t i = tile0 + tl;
-        uint16_t* o = a.out + i * d + j0;
         const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
         if (c0 < 0) {
             if (col) {
                 const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
-                *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
+                *reinterpret_cast<uint4*>(a.out + i * d + jl) = make_uint4(nn, nn, nn, nn);
             }
             if (g.stats && threadIdx.x == 0) {
                 g.stats[2 * i] = __uint_as_float(kNaNf32);
@@ -515,7 +514,7 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
             int32_t r[kK];
 #pragma unroll
             for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
-            gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+            gather_sum<DT>(acc, a.tab, a.scale, r, d, jl);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
@@ -530,21 +529,24 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
         for (int w = 1; w < nwaves; ++w) S = S + red[w];
         const float rn = 1.0f / sqrtf(S / static_cast<float>(d) + g.eps);
 
-        float nv[8], ev[8];
+        // n overwrites acc; the e1 slice stays packed until the output.
+        uint4 e1v = make_uint4(0u, 0u, 0u, 0u);
         float z = 0.0f;
         if (col) {
+            const gbytes e1row = uniform_row(a.e1, c0, 2 * d);
+            const u32x4 e1w = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(e1row + 2u * jl);
+            e1v = make_uint4(e1w.x, e1w.y, e1w.z, e1w.w);
+            const float ev[8] = {bf16lo(e1v.x), bf16hi(e1v.x), bf16lo(e1v.y), bf16hi(e1v.y),
+                                 bf16lo(e1v.z), bf16hi(e1v.z), bf16lo(e1v.w), bf16hi(e1v.w)};
             float gm[8], uu[8], vv[8];
-            load_f8(gm, g.gamma, j0);
-            load_f8(uu, g.u, j0);
-            load_f8(vv, g.v, j0);
-            const uint4 e1v = *reinterpret_cast<const uint4*>(a.e1 + static_cast<int64_t>(c0) * d + j0);
-            ev[0] = bf16lo(e1v.x); ev[1] = bf16hi(e1v.x); ev[2] = bf16lo(e1v.y); ev[3] = bf16hi(e1v.y);
-            ev[4] = bf16lo(e1v.z); ev[5] = bf16hi(e1v.z); ev[6] = bf16lo(e1v.w); ev[7] = bf16hi(e1v.w);
+            load_f8(gm, g.gamma, jl);
+            load_f8(uu, g.u, jl);
+            load_f8(vv, g.v, jl);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                nv[e] = (acc[e] * rn) * gm[e];
+                acc[e] = (acc[e] * rn) * gm[e];
                 z = __builtin_fmaf(uu[e], ev[e], z);
-                z = __builtin_fmaf(vv[e], nv[e], z);
+                z = __builtin_fmaf(vv[e], acc[e], z);
             }
         }
         z = wave_tree_sum(z);
@@ -555,13 +557,15 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
         const float logit = Z + g.b;
         const float alpha = 1.0f / (1.0f + expf(-logit));
         if (col) {
+            const float ev[8] = {bf16lo(e1v.x), bf16hi(e1v.x), bf16lo(e1v.y), bf16hi(e1v.y),
+                                 bf16lo(e1v.z), bf16hi(e1v.z), bf16lo(e1v.w), bf16hi(e1v.w)};
             float w8[8];
-            load_w8(w8, a.wg, j0);
+            load_w8(w8, a.wg, jl);
             float y[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = __builtin_fmaf(alpha * w8[e], nv[e], ev[e]);
+            for (int e = 0; e < 8; ++e) y[e] = __builtin_fmaf(alpha * w8[e], acc[e], ev[e]);
             if constexpr (RES) {
-                const uint4 rv = *reinterpret_cast<const uint4*>(a.res + i * d + j0);
+                const uint4 rv = *reinterpret_cast<const uint4*>(a.res + i * d + jl);
                 y[0] = bf16lo(rv.x) + y[0]; y[1] = bf16hi(rv.x) + y[1];
                 y[2] = bf16lo(rv.y) + y[2]; y[3] = bf16hi(rv.y) + y[3];
                 y[4] = bf16lo(rv.z) + y[4]; y[5] = bf16hi(rv.z) + y[5];
@@ -572,7 +576,7 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
             ov.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
             ov.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
             ov.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
-            store_out(o, ov);
+            store_out(a.out + i * d + jl, ov);
         }
         if (g.stats && threadIdx.x == 0) {
             g.stats[2 * i] = rn;
@@ -581,18 +585,18 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
     }
 }
 
-template <int DT, bool RES, bool PERSIST>
+template <int DT, bool RES, bool FULL, bool PERSIST>
 __global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
     extern __shared__ int32_t lds[];
     int32_t* lrows = lds;                                            // [tpw][16]
     int32_t* ltok = lds + g.f.tpw * kK;                              // [tpw]
     float* lred = reinterpret_cast<float*>(lds + g.f.tpw * (kK + 1));  // [tpw][2][nwaves]
     if constexpr (!PERSIST) {
-        gated_tile<DT, RES>(g, static_cast<int64_t>(blockIdx.x) * g.f.tpw, lrows, ltok, lred);
+        gated_tile<DT, RES, FULL>(g, static_cast<int64_t>(blockIdx.x) * g.f.tpw, lrows, ltok, lred);
     } else {
         const int64_t ntiles = (g.f.n + g.f.tpw - 1) / g.f.tpw;
         for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-            gated_tile<DT, RES>(g, tile * g.f.tpw, lrows, ltok, lred);
+            gated_tile<DT, RES, FULL>(g, tile * g.f.tpw, lrows, ltok, lred);
             __syncthreads();              // the next tile rewrites the LDS lists
         }
     }
@@ -1548,15 +1552,19 @@ void launch_gated_dt(const GatedArgs& g, const Shape& sh, hipStream_t st) {
     const int nb = (g.f.d + kSlice - 1) / kSlice;
     const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * nb);
     const size_t lds = static_cast<size_t>(sh.tpw) * ((kK + 1) * sizeof(int32_t) + 2 * nb * sizeof(float));
-    const bool res = g.f.res != nullptr;
+    const bool res = g.f.res != nullptr, full = g.f.d % kSlice == 0;
     if (sh.persist) {
-        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, true>), grid, block, lds, st, g);
-        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, true>), grid, block, lds, st, g);
+        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, false, true>), grid, block, lds, st, g);
+        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, false, true>), grid, block, lds, st, g);
+    } else if (full) {
+        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, true, false>), grid, block, lds, st, g);
+        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, true, false>), grid, block, lds, st, g);
     } else {
-        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, false>), grid, block, lds, st, g);
-        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, false>), grid, block, lds, st, g);
+        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, false, false>), grid, block, lds, st, g);
+        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, false, false>), grid, block, lds, st, g);
     }
 }
+
 
 }  // namespace
 
@@ -1730,6 +1738,13 @@ int ngram_forward_gated(const int32_t* tokens, int64_t n, const int32_t* seq_off
     a.sd = make_seeds(seeds);
     g.gamma = gamma; g.u = u; g.v = v; g.stats = stats_out; g.b = b; g.eps = eps;
     Shape sh = slice_shape(n, T->d, T->dtype);
+    if (T->dtype == NGRAM_TABLE_BF16 && env_int("NGRAM_TOKENS_PER_WG", 0) <= 0) {
+        // Two tokens per workgroup measured best for the gated bf16 path on
+        // MI355X at the prefill shape: 1 token 526 us, 2 tokens 514 us,
+        // 4 tokens 521 us per launch.
+        sh.tpw = 2;
+        sh.grid = (n + 1) / 2;
+    }
     cap_for_host(sh, T);
     a.tpw = sh.tpw;
     if (T->dtype == NGRAM_TABLE_BF16) launch_gated_dt<NGRAM_TABLE_BF16>(g, sh, stream);
