@@ -99,6 +99,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture one launch per batch in a HIP graph and time graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="backward: the three gradient calls in order on one stream")
     ap.add_argument("--cpu-rows", type=int, default=1_000_000,
                     help="table rows of the host copy the CPU oracle reads")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -426,10 +428,30 @@ def run_backward(args):
     ne = torch.empty(1, dtype=torch.int64, device=dev)
     gw = torch.empty(d, dtype=torch.float32, device=dev)
 
+    # The table gradient (HBM-bound) on the main stream; the e1 and gate
+    # gradients (bound by their in-order chains) on a side stream with their
+    # own workspace, joined at the end of the step.  --serial runs all three
+    # in order on one stream.
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ws2 = ng.grad_workspace(n, d, dev)
+    ev_in, ev_side = torch.cuda.Event(), torch.cuda.Event()
+
     def step():
-        ng.ngram_grad_table(rows, W, g, R, grad_rows_out=gr, grad_out=gt, n_unique_out=nu, workspace=ws)
-        ng.ngram_grad_e1(tok, rows, g, spec.V, grad_tokens_out=et, grad_out=ge, n_unique_out=ne, workspace=ws)
-        ng.ngram_grad_gate(rows, g, eN, grad_Wg_out=gw, workspace=ws)
+        if args.serial:
+            ng.ngram_grad_table(rows, W, g, R, grad_rows_out=gr, grad_out=gt, n_unique_out=nu, workspace=ws)
+            ng.ngram_grad_e1(tok, rows, g, spec.V, grad_tokens_out=et, grad_out=ge, n_unique_out=ne, workspace=ws)
+            ng.ngram_grad_gate(rows, g, eN, grad_Wg_out=gw, workspace=ws)
+            return
+        ev_in.record(main)
+        side.wait_event(ev_in)
+        ng.ngram_grad_e1(tok, rows, g, spec.V, grad_tokens_out=et, grad_out=ge, n_unique_out=ne, workspace=ws2,
+                         stream=side)
+        ng.ngram_grad_gate(rows, g, eN, grad_Wg_out=gw, workspace=ws2, stream=side)
+        ng.ngram_grad_table(rows, W, g, R, grad_rows_out=gr, grad_out=gt, n_unique_out=nu, workspace=ws,
+                            stream=main)
+        ev_side.record(side)
+        main.wait_event(ev_side)
 
     for _ in range(args.warmup):
         step()
@@ -452,7 +474,7 @@ def run_backward(args):
         "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "backward", "tokens": n, "R": R, "d": d, "K": K_ROWS,
-                   "unique_rows": U, "unique_tokens": Ut},
+                   "unique_rows": U, "unique_tokens": Ut, "streams": 1 if args.serial else 2},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "backward step",
                      "algorithmic_bytes_per_token": bpt, "step_us": step_s * 1e6},

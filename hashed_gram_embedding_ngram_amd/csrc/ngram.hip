@@ -1232,32 +1232,42 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
 // order (skipping invalid tokens); then the chunk parts summed in order.
 constexpr int kGateChunk = 256;
 
-__global__ void __launch_bounds__(1024) gate_grad_partial_kernel(const int32_t* __restrict__ rows,
-                                                                 const uint16_t* __restrict__ g,
-                                                                 const float* __restrict__ eN, int64_t n, int32_t d,
-                                                                 float* __restrict__ partials) {
+// One wavefront per (chunk, 256 columns): 4 columns per lane, 8 tokens'
+// loads issued before their fmas, which still run in token order.
+constexpr int kGateCols = 4;
+constexpr int kGateUnroll = 8;
+
+__global__ void __launch_bounds__(64) gate_grad_partial_kernel(const int32_t* __restrict__ rows,
+                                                               const uint16_t* __restrict__ g,
+                                                               const float* __restrict__ eN, int64_t n, int32_t d,
+                                                               float* __restrict__ partials) {
     const int64_t c = blockIdx.x;
+    const int64_t j0 = (static_cast<int64_t>(blockIdx.y) * 64 + threadIdx.x) * kGateCols;
+    if (j0 >= d) return;                      // no cross-lane operations below
     const int64_t i0 = c * kGateChunk;
     const int64_t i1 = i0 + kGateChunk < n ? i0 + kGateChunk : n;
-    for (int64_t j0 = static_cast<int64_t>(threadIdx.x) * kVec; j0 < d; j0 += static_cast<int64_t>(blockDim.x) * kVec) {
-        float part[8];
+    float part[kGateCols] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t ib = i0; ib < i1; ib += kGateUnroll) {
+        uint2 gv[kGateUnroll];
+        float4 ev[kGateUnroll];
+        bool ok[kGateUnroll];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) part[q] = 0.0f;
-        for (int64_t i = i0; i < i1; ++i) {
-            if (rows[i * kK] < 0) continue;
-            const uint4 gv = *reinterpret_cast<const uint4*>(g + i * d + j0);
-            const float4 e0 = reinterpret_cast<const float4*>(eN + i * d + j0)[0];
-            const float4 e1v = reinterpret_cast<const float4*>(eN + i * d + j0)[1];
-            const float x[8] = {bf16lo(gv.x), bf16hi(gv.x), bf16lo(gv.y), bf16hi(gv.y),
-                                bf16lo(gv.z), bf16hi(gv.z), bf16lo(gv.w), bf16hi(gv.w)};
-            const float e[8] = {e0.x, e0.y, e0.z, e0.w, e1v.x, e1v.y, e1v.z, e1v.w};
-#pragma unroll
-            for (int q = 0; q < 8; ++q) part[q] = __builtin_fmaf(x[q], e[q], part[q]);
+        for (int u = 0; u < kGateUnroll; ++u) {
+            const int64_t i = ib + u < i1 ? ib + u : ib;
+            ok[u] = ib + u < i1 && rows[i * kK] >= 0;
+            gv[u] = *reinterpret_cast<const uint2*>(g + i * d + j0);
+            ev[u] = *reinterpret_cast<const float4*>(eN + i * d + j0);
         }
-        float* o = partials + c * d + j0;
-        reinterpret_cast<float4*>(o)[0] = make_float4(part[0], part[1], part[2], part[3]);
-        reinterpret_cast<float4*>(o)[1] = make_float4(part[4], part[5], part[6], part[7]);
+#pragma unroll
+        for (int u = 0; u < kGateUnroll; ++u) {
+            if (!ok[u]) continue;
+            part[0] = __builtin_fmaf(bf16lo(gv[u].x), ev[u].x, part[0]);
+            part[1] = __builtin_fmaf(bf16hi(gv[u].x), ev[u].y, part[1]);
+            part[2] = __builtin_fmaf(bf16lo(gv[u].y), ev[u].z, part[2]);
+            part[3] = __builtin_fmaf(bf16hi(gv[u].y), ev[u].w, part[3]);
+        }
     }
+    *reinterpret_cast<float4*>(partials + c * d + j0) = make_float4(part[0], part[1], part[2], part[3]);
 }
 
 __global__ void __launch_bounds__(256) gate_grad_total_kernel(const float* __restrict__ partials, int64_t nchunks,
@@ -2018,10 +2028,9 @@ int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, 
     float* parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.parts);
     const int64_t nchunks = (n + kGateChunk - 1) / kGateChunk;
     if (nchunks > 0) {
-        int threads = ((d / kVec) + 63) / 64 * 64;
-        if (threads > 1024) threads = 1024;
-        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks)), dim3(threads), 0, stream,
-                           rows, dout, eN, n, d, parts);
+        const unsigned colblocks = static_cast<unsigned>((d / kGateCols + 63) / 64);
+        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks), colblocks), dim3(64), 0,
+                           stream, rows, dout, eN, n, d, parts);
     }
     hipLaunchKernelGGL(gate_grad_total_kernel, dim3(static_cast<unsigned>((d + 255) / 256)), dim3(256), 0, stream,
                        parts, nchunks, d, grad_Wg_out);

@@ -260,7 +260,12 @@ int ngram_select_hot_rows(const int32_t* counts, int64_t R, int64_t C, int32_t* 
  * every result is reproducible bit for bit, with no floating-point atomics:
  * the ids are grouped by a stable radix sort that keeps positions ascending.
  * Workspace: ngram_grad_workspace_bytes(n, d) bytes of device memory,
- * 256-byte aligned, shared by the three calls.  n <= 2^20 (ERANGE). */
+ * 256-byte aligned; calls in order on one stream may share one workspace,
+ * calls that can run at the same time (on different streams) need one each.
+ * The table gradient is bound by HBM bandwidth, the e1 and gate gradients by
+ * their in-order chains, so running ngram_grad_e1 and ngram_grad_gate on a
+ * second stream beside ngram_grad_table hides most of them.  n <= 2^20
+ * (ERANGE). */
 int64_t ngram_grad_workspace_bytes(int64_t n, int32_t d);
 
 /* Table gradient, sparse: for each distinct valid row id r in ascending order

@@ -79,7 +79,7 @@ def test_e1_grad(lengths, V, d, bad):
     assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
 
 
-@pytest.mark.parametrize("n,d", [(1, 8), (255, 64), (257, 64), (1000, 2560)])
+@pytest.mark.parametrize("n,d", [(1, 8), (255, 64), (257, 64), (263, 520), (1000, 2560), (515, 1032)])
 def test_gate_grad(n, d):
     say(f"grad gate n={n} d={d}")
     toks, rows, g, W = _inputs((n,), 4096, 1024, d, seed=9)
@@ -91,6 +91,35 @@ def test_gate_grad(n, d):
     torch.cuda.synchronize()
     want = oracle.grad_gate(rows, g, eN)
     assert np.array_equal(gw.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_grads_on_two_streams_equal_one_stream():
+    """The e1 and gate gradients on a side stream with their own workspace,
+    beside the table gradient on the main stream, give the same bits as the
+    three calls in order on one stream."""
+    say("grads on two streams")
+    n, d, R, V = 3000, 520, 50_003, 151936
+    toks, rows, g, W = _inputs((1000, 2000), R, V, d, seed=21)
+    eN = (synth.as_f32(synth.tensor(synth.KIND_F32_UNIT, 22, synth.TAG_TABLE, n * d)).reshape(n, d) - 0.5)
+    t, r, gg, w, e = (_dev(toks, np.int32), _dev(rows, np.int32), _dev(g.view(np.int16), np.int16),
+                      _dev(W, np.float32), _dev(eN.astype(np.float32), np.float32))
+    ws1, ws2 = ng.grad_workspace(n, d), ng.grad_workspace(n, d)
+    serial = (ng.ngram_grad_table(r, w, gg, R, workspace=ws1), ng.ngram_grad_e1(t, r, gg, V, workspace=ws1),
+              ng.ngram_grad_gate(r, gg, e, workspace=ws1))
+    torch.cuda.synchronize()
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ev.record(main)
+    side.wait_event(ev)
+    e1g = ng.ngram_grad_e1(t, r, gg, V, workspace=ws2, stream=side)
+    gate = ng.ngram_grad_gate(r, gg, e, workspace=ws2, stream=side)
+    tab = ng.ngram_grad_table(r, w, gg, R, workspace=ws1, stream=main)
+    torch.cuda.synchronize()
+    for a, b in ((serial[0], tab), (serial[1], e1g)):
+        U = int(a[2].item())
+        assert U == int(b[2].item())
+        assert torch.equal(a[0][:U], b[0][:U]) and torch.equal(a[1][:U].view(torch.int32), b[1][:U].view(torch.int32))
+    assert torch.equal(serial[2].view(torch.int32), gate.view(torch.int32))
 
 
 def test_empty_grads():
