@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 
 import hashed_gram_embedding_ngram_amd as ng  # noqa: E402
 import oracle  # noqa: E402
-from synth.workloads import CONFIGS, DeviceInputs, HostInputs, fill_host_table  # noqa: E402
+from synth.workloads import CONFIGS, DeviceInputs, HostInputs, Spec, fill_host_table  # noqa: E402
 from tests.oracle_ref import expected, sample_tokens  # noqa: E402
 from tests.test_gpu_parity import assert_bf16_equal, bits16, say  # noqa: E402
 
@@ -111,3 +111,27 @@ def test_host_table_full_size():
         _free()
     finally:
         hb.free()
+
+
+@pytest.mark.parametrize("table,kind,d", [("bf16", 2, 8), ("int8", 4, 8), ("mxfp4", 7, 128)])
+def test_forward_at_the_largest_row_count(table, kind, d):
+    """R = 2^31 - 1 rows (the largest the ABI takes): row byte offsets pass
+    2^32 (bf16: 32 GiB table; int8: 16 GiB + 8 GiB of scales; MXFP4 at 68 B
+    per row: 136 GiB).  Every row id and every output equals the oracle."""
+    sp = Spec(f"maxR_{table}", (300, 17, 1), 151936, 2**31 - 1, d, table=table, table_kind=kind,
+              residual=True, config_id=31)
+    say(f"largest R: {table} d={d}")
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    out, rows = torch.empty(sp.n * d, dtype=torch.int16, device="cuda:0"), \
+        torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+    ng.ngram_forward(di.tokens, di.offsets, di.table_obj(), di.W_g, out, e1=di.e1, residual=di.residual,
+                     rows_out=rows)
+    torch.cuda.synchronize()
+    want_rows, _, want = expected(h)
+    got_rows = rows.cpu().numpy()
+    assert np.array_equal(got_rows, want_rows)
+    assert got_rows.max() > 2**31 - 2**28                  # rows near the end of the table are read
+    assert_bf16_equal(bits16(out).reshape(sp.n, d), want, sp.name)
+    del di, out, rows
+    _free()
