@@ -444,3 +444,25 @@ def test_mxfp4_host_table_paths(d, monkeypatch):
             assert np.array_equal(e.cpu().numpy().view(np.uint32), want.view(np.uint32))
     finally:
         hb.free()
+
+
+def test_unpinned_host_table_is_rejected_and_leaves_no_error_behind():
+    """A host table in ordinary (not pinned, not device-mapped) memory: the
+    host-side pointer lookup fails, the call returns NGRAM_EHIP without a
+    launch, and the next call runs normally."""
+    import ctypes
+    sp = Spec("unpinned", (40,), 1000, 64, 64, table_kind=synth.KIND_BF16_WIDE, config_id=26)
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+    plain = np.ascontiguousarray(h.full_table())                    # pageable host memory
+    t = ng._Table(plain.ctypes.data, None, sp.R, sp.d, ng.TABLE_BF16, ng.IN_HOST, 0)
+    eN = torch.empty((sp.n, sp.d), dtype=torch.float32, device="cuda:0")
+    say("unpinned host table")
+    rc = ng.lib().ngram_embed_bag(ctypes.byref(t), rows.data_ptr(), sp.n, eN.data_ptr(), None)
+    assert rc == -4, rc                                                # NGRAM_EHIP
+    assert b"pinned" in ng.lib().ngram_last_error()
+    eN2 = ng.ngram_embed_bag(di.table_obj(), rows)                   # a valid call still succeeds
+    torch.cuda.synchronize()
+    _, want_eN, _ = expected(h)
+    assert np.array_equal(eN2.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
