@@ -63,7 +63,7 @@ typedef enum {
     NGRAM_EALIGN = -2,   /* a pointer is not aligned as documented */
     NGRAM_ERANGE = -3,   /* R, d or V outside the supported range */
     NGRAM_EHIP = -4,     /* the HIP runtime reported an error */
-    NGRAM_ENOTSUP = -5   /* a combination this build does not support */
+    NGRAM_ENOTSUP = -5   /* a combination the library does not support */
 } ngram_status;
 
 typedef enum { NGRAM_TABLE_BF16 = 0, NGRAM_TABLE_INT8_ROWSCALE = 1, NGRAM_TABLE_MXFP4 = 2 } ngram_dtype;
