@@ -94,14 +94,23 @@ struct Ctx {
     bool ok;
 };
 
-__device__ inline Ctx token_context(const int32_t* __restrict__ tok, int64_t i,
-                                    const int32_t* __restrict__ so, int S,
-                                    const int32_t* __restrict__ hist, uint32_t c0_limit) {
-    // The three token loads do not depend on the sequence, so they are issued
-    // before the search and overlap its loads.
-    const uint32_t t0 = static_cast<uint32_t>(tok[i]);
-    const uint32_t t1 = i >= 1 ? static_cast<uint32_t>(tok[i - 1]) : kPad;
-    const uint32_t t2 = i >= 2 ? static_cast<uint32_t>(tok[i - 2]) : kPad;
+// The ids of tokens i, i-1, i-2 (pad before the batch start).  They do not
+// depend on the sequence, so they are loaded before the sequence lookup.
+struct TokIds {
+    uint32_t t0, t1, t2;
+};
+
+__device__ inline TokIds token_ids(const int32_t* __restrict__ tok, int64_t i) {
+    TokIds q;
+    q.t0 = static_cast<uint32_t>(tok[i]);
+    q.t1 = i >= 1 ? static_cast<uint32_t>(tok[i - 1]) : kPad;
+    q.t2 = i >= 2 ? static_cast<uint32_t>(tok[i - 2]) : kPad;
+    return q;
+}
+
+// so / hist point to global memory or to their copies in LDS.
+__device__ inline Ctx context_of(const TokIds& q, int64_t i, const int32_t* so, int S, const int32_t* hist,
+                                 uint32_t c0_limit) {
     int lo = 0, hi = S - 1;     // the last sequence s with so[s] <= i
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -111,11 +120,34 @@ __device__ inline Ctx token_context(const int32_t* __restrict__ tok, int64_t i,
     const uint32_t h0 = hist ? static_cast<uint32_t>(hist[2 * lo]) : kPad;
     const uint32_t h1 = hist ? static_cast<uint32_t>(hist[2 * lo + 1]) : kPad;
     Ctx c;
-    c.c0 = t0;
-    c.c1 = p >= 1 ? t1 : h1;
-    c.c2 = p >= 2 ? t2 : (p == 1 ? h1 : h0);
+    c.c0 = q.t0;
+    c.c1 = p >= 1 ? q.t1 : h1;
+    c.c2 = p >= 2 ? q.t2 : (p == 1 ? h1 : h0);
     c.ok = c.c0 < c0_limit && c.c1 <= kPad && c.c2 <= kPad;
     return c;
+}
+
+// Up to this many sequences, a workgroup copies seq_offsets (and the
+// history) into LDS in one round of loads, overlapped with its token loads,
+// and searches there: the global binary search is a chain of dependent loads
+// at the start of every workgroup (measured on MI355X at the prefill shape:
+// 521-523 us with 8 sequences against 484 us for the same tokens as one).
+constexpr int kStageSeqs = 255;
+constexpr int kSeqLds = (kStageSeqs + 1) + 2 * kStageSeqs;   // int32 words
+// Staging costs a barrier: it pays in batches of many tokens, not in small
+// decode steps (B = 2 and 4 measured 3% slower with it), and with one
+// sequence there is no search to replace.
+constexpr int64_t kStageMinTokens = 1024;
+
+__host__ __device__ inline int32_t stage_for(int64_t n, int S) {
+    return S >= 2 && S <= kStageSeqs && n >= kStageMinTokens ? 1 : 0;
+}
+
+__device__ inline void stage_seqs(const int32_t* __restrict__ so, const int32_t* __restrict__ hist, int S,
+                                  int32_t* lseq) {
+    for (int t = threadIdx.x; t <= S; t += blockDim.x) lseq[t] = so[t];
+    if (hist)
+        for (int t = threadIdx.x; t < 2 * S; t += blockDim.x) lseq[kStageSeqs + 1 + t] = hist[t];
 }
 
 __device__ inline int32_t hashed_row(const Ctx& c, int k, const Seeds& sd, uint64_t R) {
@@ -390,26 +422,53 @@ struct FwdArgs {
     int32_t d;
     int32_t tpw;        // tokens per workgroup
     uint32_t c0_limit;  // token ids must be below this (V, capped at the pad id)
+    int32_t stage;      // copy seq_offsets / history into LDS (see stage_for)
     Seeds sd;
 };
 
 // A tile's hash phase: one thread per (token, k) writes the row id into LDS
 // (and rows_out), and w_t per token; -1 marks an invalid token.
-__device__ inline void hash_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok) {
-    for (int t = threadIdx.x; t < a.tpw * kK; t += blockDim.x) {
-        const int tl = t >> 4, k = t & (kK - 1);
-        const int64_t i = tile0 + tl;
-        int32_t row = -1, c0 = -1;
-        if (i < a.n) {
-            const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
-            if (c.ok) {
-                row = hashed_row(c, k, a.sd, a.R);
-                c0 = static_cast<int32_t>(c.c0);
+__device__ inline void hash_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok, int32_t* lseq) {
+    const int nt = a.tpw * kK;
+    if (a.stage) {
+        // the thread's first (token, k): its ids are loaded ahead of the staging
+        TokIds first = {kPad, kPad, kPad};
+        if (static_cast<int>(threadIdx.x) < nt && tile0 + (threadIdx.x >> 4) < a.n)
+            first = token_ids(a.tok, tile0 + (threadIdx.x >> 4));
+        stage_seqs(a.so, a.hist, a.S, lseq);
+        __syncthreads();
+        for (int t = threadIdx.x; t < nt; t += blockDim.x) {
+            const int tl = t >> 4, k = t & (kK - 1);
+            const int64_t i = tile0 + tl;
+            int32_t row = -1, c0 = -1;
+            if (i < a.n) {
+                const TokIds q = t == static_cast<int>(threadIdx.x) ? first : token_ids(a.tok, i);
+                const Ctx c = context_of(q, i, lseq, a.S, a.hist ? lseq + kStageSeqs + 1 : nullptr, a.c0_limit);
+                if (c.ok) {
+                    row = hashed_row(c, k, a.sd, a.R);
+                    c0 = static_cast<int32_t>(c.c0);
+                }
+                if (a.rows_out) a.rows_out[i * kK + k] = row;
             }
-            if (a.rows_out) a.rows_out[i * kK + k] = row;
+            lrows[t] = row;
+            if (k == 0) ltok[tl] = c0;
         }
-        lrows[t] = row;
-        if (k == 0) ltok[tl] = c0;
+    } else {
+        for (int t = threadIdx.x; t < nt; t += blockDim.x) {
+            const int tl = t >> 4, k = t & (kK - 1);
+            const int64_t i = tile0 + tl;
+            int32_t row = -1, c0 = -1;
+            if (i < a.n) {
+                const Ctx c = context_of(token_ids(a.tok, i), i, a.so, a.S, a.hist, a.c0_limit);
+                if (c.ok) {
+                    row = hashed_row(c, k, a.sd, a.R);
+                    c0 = static_cast<int32_t>(c.c0);
+                }
+                if (a.rows_out) a.rows_out[i * kK + k] = row;
+            }
+            lrows[t] = row;
+            if (k == 0) ltok[tl] = c0;
+        }
     }
     __syncthreads();
 }
@@ -422,7 +481,7 @@ __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows,
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const int nslices = (a.d + kSlice - 1) / kSlice;
-    hash_tile(a, tile0, lrows, ltok);
+    hash_tile(a, tile0, lrows, ltok, lrows + a.tpw * (kK + 1));
 
     const int64_t rem = a.n - tile0;
     const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
@@ -518,7 +577,7 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
     const int64_t d = a.d;
     const uint32_t jl = static_cast<uint32_t>(wave * kSlice + lane * kVec);   // the lane's first column
     const bool col = FULL || jl < static_cast<uint32_t>(d);  // FULL: d a multiple of 512, all lanes have columns
-    hash_tile(a, tile0, lrows, ltok);
+    hash_tile(a, tile0, lrows, ltok, reinterpret_cast<int32_t*>(lred + a.tpw * 2 * nwaves));
 
     const int64_t rem = a.n - tile0;
     const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
@@ -659,15 +718,24 @@ struct HashArgs {
     uint64_t R;
     int32_t S;
     uint32_t c0_limit;
+    int32_t stage;
     Seeds sd;
 };
 
 __global__ void __launch_bounds__(256) ngram_hash_kernel(const HashArgs a) {
+    __shared__ int32_t lseq[kSeqLds];
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= a.n * kK) return;
+    const bool live = t < a.n * kK;
     const int64_t i = t >> 4;
     const int k = static_cast<int>(t & (kK - 1));
-    const Ctx c = token_context(a.tok, i, a.so, a.S, a.hist, a.c0_limit);
+    TokIds q = {kPad, kPad, kPad};
+    if (live) q = token_ids(a.tok, i);
+    const bool staged = a.stage != 0;
+    if (staged) stage_seqs(a.so, a.hist, a.S, lseq);
+    if (staged) __syncthreads();
+    if (!live) return;
+    const Ctx c = staged ? context_of(q, i, lseq, a.S, a.hist ? lseq + kStageSeqs + 1 : nullptr, a.c0_limit)
+                         : context_of(q, i, a.so, a.S, a.hist, a.c0_limit);
     a.rows_out[t] = c.ok ? hashed_row(c, k, a.sd, a.R) : -1;
 }
 
@@ -1570,7 +1638,8 @@ template <int DT, bool E1, bool RES>
 void launch_fwd(const FwdArgs& a, const Shape& sh, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(sh.grid));
     const dim3 block(64 * sh.waves);
-    const size_t lds = static_cast<size_t>(sh.tpw) * (kK + 1) * sizeof(int32_t);
+    const size_t lds = static_cast<size_t>(sh.tpw) * (kK + 1) * sizeof(int32_t) +
+                       (a.stage ? kSeqLds * sizeof(int32_t) : 0);
     if (sh.persist) hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, true>), grid, block, lds, st, a);
     else hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, false>), grid, block, lds, st, a);
 }
@@ -1589,7 +1658,8 @@ template <int DT>
 void launch_gated_dt(const GatedArgs& g, const Shape& sh, hipStream_t st) {
     const int nb = (g.f.d + kSlice - 1) / kSlice;
     const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * nb);
-    const size_t lds = static_cast<size_t>(sh.tpw) * ((kK + 1) * sizeof(int32_t) + 2 * nb * sizeof(float));
+    const size_t lds = static_cast<size_t>(sh.tpw) * ((kK + 1) * sizeof(int32_t) + 2 * nb * sizeof(float)) +
+                       (g.f.stage ? kSeqLds * sizeof(int32_t) : 0);
     const bool res = g.f.res != nullptr, full = g.f.d % kSlice == 0;
     if (sh.persist) {
         if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, false, true>), grid, block, lds, st, g);
@@ -1641,7 +1711,7 @@ int ngram_hash(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int
     if (n == 0) return NGRAM_OK;
     HashArgs a;
     a.tok = tokens; a.so = seq_offsets; a.hist = history; a.rows_out = rows_out;
-    a.n = n; a.R = static_cast<uint64_t>(R); a.S = S; a.c0_limit = kPad;
+    a.n = n; a.R = static_cast<uint64_t>(R); a.S = S; a.c0_limit = kPad; a.stage = stage_for(n, S);
     a.sd = make_seeds(seeds);
     const int64_t total = n * kK;
     hipLaunchKernelGGL(ngram_hash_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
@@ -1734,6 +1804,7 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
     a.e1 = e1; a.wg = W_g; a.res = residual; a.out = out; a.rows_out = rows_out;
     a.n = n; a.R = static_cast<uint64_t>(T->R); a.S = S; a.d = T->d;
     a.c0_limit = c0_limit_for(e1, V);
+    a.stage = stage_for(n, S);
     a.sd = make_seeds(seeds);
     Shape sh = slice_shape(n, T->d, T->dtype);
     cap_for_host(sh, T);
@@ -1773,6 +1844,7 @@ int ngram_forward_gated(const int32_t* tokens, int64_t n, const int32_t* seq_off
     a.e1 = e1; a.wg = W_g; a.res = residual; a.out = out; a.rows_out = rows_out;
     a.n = n; a.R = static_cast<uint64_t>(T->R); a.S = S; a.d = T->d;
     a.c0_limit = c0_limit_for(e1, V);
+    a.stage = stage_for(n, S);
     a.sd = make_seeds(seeds);
     g.gamma = gamma; g.u = u; g.v = v; g.stats = stats_out; g.b = b; g.eps = eps;
     Shape sh = slice_shape(n, T->d, T->dtype);

@@ -466,3 +466,22 @@ def test_unpinned_host_table_is_rejected_and_leaves_no_error_behind():
     torch.cuda.synchronize()
     _, want_eN, _ = expected(h)
     assert np.array_equal(eN2.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+
+
+@pytest.mark.parametrize("lengths,history", [
+    ((600, 0, 1, 2, 450, 3), False),          # 1056 tokens, 6 sequences: offsets staged in LDS
+    ((6,) * 200, True),                       # 1200 tokens, 200 sequences with history: both staged
+    ((4,) * 300, True),                       # 300 sequences: above the staging limit, global search
+    ((1023, 1), False),                       # 1024 tokens exactly, 2 sequences
+])
+def test_sequence_lookup_staged_and_global(lengths, history):
+    """Batches of at least 1024 tokens with 2..255 sequences look their
+    sequence up in LDS copies of seq_offsets (and the history); more
+    sequences, or smaller batches, search in global memory.  Both give the
+    oracle's rows and outputs, through the fused and the unfused hash."""
+    sp = Spec(f"seqs{len(lengths)}", lengths, 151936, 100_003, 64, table_kind=synth.KIND_BF16_WIDE,
+              residual=True, history=history, config_id=27)
+    h, di = check_spec(sp)
+    rows = ng.ngram_hash(di.tokens, di.offsets, sp.R, history=di.history)
+    torch.cuda.synchronize()
+    assert np.array_equal(rows.cpu().numpy(), oracle.hash_rows(h.tokens, h.offsets, sp.R, h.history))
