@@ -135,3 +135,26 @@ def test_forward_at_the_largest_row_count(table, kind, d):
     assert_bf16_equal(bits16(out).reshape(sp.n, d), want, sp.name)
     del di, out, rows
     _free()
+
+
+def test_forward_output_beyond_2_31_elements():
+    """2^22 tokens x d = 1024: the output holds 2^32 elements (8 GiB), so the
+    output offsets pass 2^31; sampled tokens, including the last ones, equal
+    the oracle, and every row id is checked."""
+    n = 1 << 22
+    sp = Spec("big_n", (n // 2, n // 2), 151936, 100_003, 1024, residual=True, config_id=32)
+    say(f"output beyond 2^31 elements: n={sp.n} d={sp.d}")
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    rows = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+    ng.ngram_forward(di.tokens, di.offsets, di.table_obj(), di.W_g, di.residual, e1=di.e1,
+                     residual=di.residual, rows_out=rows)
+    torch.cuda.synchronize()
+    want_rows = oracle.hash_rows(h.tokens, h.offsets, sp.R)
+    assert np.array_equal(rows.cpu().numpy(), want_rows)
+    idx = np.unique(np.concatenate([sample_tokens(sp, m=64), np.arange(n - 8, n)]))
+    _, _, want = expected(h, idx, rows_all=want_rows)
+    got = bits16(di.residual.view(sp.n, sp.d)[torch.from_numpy(idx).to("cuda:0")])
+    assert_bf16_equal(got, want, sp.name)
+    del di, rows
+    _free()
