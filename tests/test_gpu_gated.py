@@ -164,17 +164,26 @@ def test_gated_invalid_tokens_give_nan():
     assert_gated_equal(out[clean], want, y, mag, "g_bad clean tokens")
 
 
-def test_gated_host_table_equals_device_table():
-    sp = Spec("g_host", (300, 212), 151936, 20_003, 2560, table_kind=synth.KIND_BF16_WIDE,
+@pytest.mark.parametrize("table,kind,d", [("bf16", synth.KIND_BF16_WIDE, 2560), ("int8", synth.KIND_I8_NORMAL, 2560),
+                                          ("mxfp4", synth.KIND_MXFP4_WIDE, 640)])
+def test_gated_host_table_equals_device_table(table, kind, d, monkeypatch):
+    """The same table in pinned host memory (capped persistent grid) and in
+    HBM gives bit-identical gated outputs and statistics."""
+    from synth.workloads import fill_host_table
+    monkeypatch.setenv("NGRAM_HOST_WORKGROUPS", "5")
+    sp = Spec(f"g_host_{table}", (300, 212), 151936, 20_003, d, table=table, table_kind=kind,
               residual=True, config_id=48)
     gp = gate_params(sp)
     h = HostInputs(sp)
     di = DeviceInputs(sp, h)
     out_dev, _, st_dev = run_gated(di, gp, out_of_place=True)
-    hb = ng.HostBuffer(sp.R * sp.d * 2)
+    rb = {"bf16": 2 * d, "int8": d, "mxfp4": synth.mxfp4_row_bytes(d)}[table]
+    hb = ng.HostBuffer(sp.R * rb)
     try:
-        hb.numpy(np.uint16, (sp.R, sp.d))[:] = h.full_table()
-        di.table_obj = lambda: ng.Table(hb, sp.R, sp.d)
+        npdt = {"bf16": np.int16, "int8": np.int8, "mxfp4": np.uint8}[table]
+        fill_host_table(sp, hb.numpy(npdt, (sp.R, rb // np.dtype(npdt).itemsize)))
+        dt = {"bf16": ng.TABLE_BF16, "int8": ng.TABLE_INT8_ROWSCALE, "mxfp4": ng.TABLE_MXFP4}[table]
+        di.table_obj = lambda: ng.Table(hb, sp.R, sp.d, dt, row_scale=di.scale)
         out_host, _, st_host = run_gated(di, gp, out_of_place=True)
     finally:
         hb.free()

@@ -438,10 +438,13 @@ def test_mxfp4_host_table_paths(d, monkeypatch):
         ng.ngram_pool_cache_rows(pool, hot, sel)
         prow = ng.ngram_pool_gather(pool, rows)
         eN3 = ng.ngram_embed_bag(pool.device_table(), prow)
+        out = torch.empty(sp.n * d, dtype=torch.int16, device="cuda:0")
+        ng.ngram_forward(di.tokens, di.offsets, T, di.W_g, out, e1=di.e1)     # fused, persistent grid
         torch.cuda.synchronize()
-        _, want, _ = expected(h)
+        want_rows, want, want_out = expected(h)
         for e in (eN, eN2, eN3):
             assert np.array_equal(e.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        assert_bf16_equal(bits16(out).reshape(sp.n, d), want_out, sp.name)
     finally:
         hb.free()
 
