@@ -88,6 +88,29 @@ MUTATIONS = {
 }
 
 
+ALL_PINS = ["tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py", "tests/test_oracle_grad.py",
+            "tests/test_oracle_mxfp4.py", "tests/test_oracle_norm_gate.py"]
+
+
+def pins_for(name):
+    """The pin file of the function a mutation hits (so each run imports only
+    what it needs); the whole set for anything else."""
+    for prefix, f in (("grad_", "test_oracle_grad.py"), ("mxfp4_", "test_oracle_mxfp4.py"),
+                      ("e2m1_", "test_oracle_mxfp4.py"), ("norm_", "test_oracle_norm_gate.py"),
+                      ("blocked_", "test_oracle_norm_gate.py"), ("dot_", "test_oracle_norm_gate.py"),
+                      ("gate_sign", "test_oracle_norm_gate.py"), ("gate_uv", "test_oracle_norm_gate.py"),
+                      ("gate_no_bias", "test_oracle_norm_gate.py"), ("gate_alpha", "test_oracle_norm_gate.py"),
+                      ("gate_uses_raw", "test_oracle_norm_gate.py"), ("sum_", "test_oracle_sum_gate.py"),
+                      ("int8_", "test_oracle_sum_gate.py"), ("gate_", "test_oracle_sum_gate.py"),
+                      ("round_", "test_oracle_sum_gate.py")):
+        if name.startswith(prefix):
+            return ["tests/" + f]
+    if name in ("no_gamma", "wrong_shift", "wrong_multiplier", "bigram_trigram_swapped", "field_width_20",
+                "trigram_drops_c2", "context_off_by_one", "history_swapped", "seed_index", "mod_low_word"):
+        return ["tests/test_oracle_hash.py"]
+    return ALL_PINS
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_mutation(name, tmp_path):
     before, after = MUTATIONS[name]
@@ -99,9 +122,6 @@ def test_pins_catch_mutation(name, tmp_path):
     subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
                     "-o", str(mlib), str(msrc), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(mlib))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py",
-                        "tests/test_oracle_grad.py", "tests/test_oracle_mxfp4.py",
-                        "tests/test_oracle_norm_gate.py"],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + pins_for(name),
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
