@@ -34,6 +34,7 @@ def _dev(a, dt):
     ((300, 7), 100_003, 520, (3, 17)),      # invalid tokens, ragged slices
     ((2000,), 4001, 2560, ()),              # two-level scans (32000 sort items)
     ((1,), 7, 8, ()),
+    ((50,), 3, 136, ()),                    # groups of hundreds of items (several 64-item blocks)
 ])
 def test_table_grad(lengths, R, d, bad):
     say(f"grad table {lengths} R={R} d={d}")
