@@ -49,12 +49,10 @@ def lib():
         L.oracle_embed_bag_mxfp4.argtypes = [P, I64, I32, P, I64, P]
         L.oracle_grad_table_rows.argtypes = [P, I64, I32, P, P, P, I64, P]
         L.oracle_grad_e1_tokens.argtypes = [P, P, I64, I32, P, P, I64, P]
-        L.oracle_grad_gate.argtypes = [P, P, P, I64, I32, P]
+        L.oracle_grad_gate.argtypes = [P, P, P, I64, I32, P, P]
         F = ctypes.c_float
-        L.oracle_blocked_sumsq.restype = F
-        L.oracle_blocked_sumsq.argtypes = [P, I32]
-        L.oracle_blocked_dot2.restype = F
-        L.oracle_blocked_dot2.argtypes = [P, P, P, P, I32]
+        L.oracle_bf16_rne_f64.restype = ctypes.c_uint16
+        L.oracle_bf16_rne_f64.argtypes = [ctypes.c_double]
         L.oracle_norm_gate_add.argtypes = [P, P, I64, I32, P, P, P, P, P, F, F, P, P, P, P]
         _lib = L
     return _lib
@@ -209,34 +207,35 @@ def grad_e1(tokens, rows, g, query=None):
     return query, out
 
 
-def grad_gate(rows, g, eN):
+def grad_gate(rows, g, eN, with_f64=False):
+    """dW_g fp32 [d] (the float64 sum rounded once); with ``with_f64`` also
+    the float64 sum itself."""
     rows = _c(rows, np.int32)
     g = _c(g, np.uint16)
     eN = _c(eN, np.float32)
     n, d = g.shape
     out = np.zeros(d, dtype=np.float32)
-    lib().oracle_grad_gate(_p(rows), _p(g), _p(eN), n, d, _p(out))
-    return out
+    out64 = np.zeros(d, dtype=np.float64)
+    lib().oracle_grad_gate(_p(rows), _p(g), _p(eN), n, d, _p(out), _p(out64))
+    return (out, out64) if with_f64 else out
 
 
-def blocked_sumsq(x) -> np.float32:
-    x = _c(x, np.float32).reshape(-1)
-    return np.float32(lib().oracle_blocked_sumsq(_p(x), x.size))
-
-
-def blocked_dot2(a, b, c, e) -> np.float32:
-    a, b, c, e = (_c(z, np.float32).reshape(-1) for z in (a, b, c, e))
-    return np.float32(lib().oracle_blocked_dot2(_p(a), _p(b), _p(c), _p(e), a.size))
+def bf16_rne_f64(x) -> np.ndarray:
+    """float64 values rounded once to bf16 (bits), ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    L = lib()
+    return np.array([L.oracle_bf16_rne_f64(float(v)) for v in x.reshape(-1)], dtype=np.uint16).reshape(x.shape)
 
 
 def norm_gate_add(eN, e1_rows, e1, W_g, gamma, u, v, b, eps, residual=None):
-    """Normalised, input-gated fusion of the sums eN [n][d].  Returns (out
-    bf16 bits [n][d], stats fp32 [n][2] = (r, logit), y fp32 [n][d])."""
+    """Normalised, input-gated fusion of the sums eN [n][d], evaluated in
+    float64.  Returns (out bf16 bits [n][d], stats float64 [n][2] = (r,
+    logit), y float64 [n][d], the value rounded to out)."""
     eN = _c(eN, np.float32)
     n, d = eN.shape
     out = np.zeros((n, d), dtype=np.uint16)
-    stats = np.zeros((n, 2), dtype=np.float32)
-    y = np.zeros((n, d), dtype=np.float32)
+    stats = np.zeros((n, 2), dtype=np.float64)
+    y = np.zeros((n, d), dtype=np.float64)
     lib().oracle_norm_gate_add(_p(eN), _p(_c(e1_rows, np.int32)), n, d, _p(_c(e1, np.uint16)),
                                _p(_c(W_g, np.float32)), _p(_c(gamma, np.float32)), _p(_c(u, np.float32)),
                                _p(_c(v, np.float32)), float(np.float32(b)), float(np.float32(eps)),

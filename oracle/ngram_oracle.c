@@ -266,9 +266,11 @@ void oracle_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets
  *           ascending t, of acc = fmaf(W_g[j], g[i][j], acc), from +0;
  *   e1:     de1[v][j] = sum over tokens i with tokens[i] == v, ascending i,
  *           of acc = acc + g[i][j], from +0;
- *   gate:   dW_g[j]   = sum over chunks c = 0, 1, … of 256 tokens, in order,
- *           of part_c, each part_c = fmaf(g[i][j], eN[i][j], part) over the
- *           chunk's tokens in ascending i, from +0.
+ *   gate:   dW_g[j]   = the sum over valid tokens i of g[i][j] * eN[i][j], a
+ *           single sum with no stated order: evaluated here in float64 over
+ *           ascending i (every product of a bf16 and an fp32 value is exact in
+ *           float64) and rounded once to fp32; out64 (may be NULL) receives
+ *           the float64 value before that rounding.
  * The residual's gradient is g itself.
  */
 void oracle_grad_table_rows(const int32_t* rows, int64_t n, int32_t d, const float* W_g,
@@ -305,21 +307,53 @@ void oracle_grad_e1_tokens(const int32_t* tokens, const int32_t* rows, int64_t n
 }
 
 void oracle_grad_gate(const int32_t* rows, const uint16_t* g, const float* eN, int64_t n, int32_t d,
-                      float* out)
+                      float* out, double* out64)
 {
     for (int32_t j = 0; j < d; ++j) {
-        float total = 0.0f;
-        for (int64_t c0 = 0; c0 < n; c0 += 256) {
-            float part = 0.0f;
-            for (int64_t i = c0; i < n && i < c0 + 256; ++i) {
-                if (rows[i * ORACLE_K] < 0)
-                    continue;
-                part = fmaf(oracle_bf16_to_f32(g[i * d + j]), eN[i * d + j], part);
-            }
-            total = total + part;
+        double acc = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            if (rows[i * ORACLE_K] < 0)
+                continue;
+            acc = acc + (double)oracle_bf16_to_f32(g[i * d + j]) * (double)eN[i * d + j];
         }
-        out[j] = total;
+        if (out64)
+            out64[j] = acc;
+        out[j] = (float)acc;
     }
+}
+
+/*
+ * Round a float64 value to the nearest bf16, ties to even; NaN to 0x7FC0.
+ * In the binade [2^(e-1), 2^e) a bf16 value has 8 significant bits, so its
+ * spacing is 2^(e-8) (never below the subnormal spacing 2^-133).  The two
+ * bf16 neighbours of |x| and their midpoint are exact float64 values, so the
+ * choice is made by exact comparisons.
+ */
+uint16_t oracle_bf16_rne_f64(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    const double a = fabs(x);
+    if (isinf(a))
+        return sign | 0x7F80;
+    int e = 0;
+    (void)frexp(a, &e);                          /* 2^(e-1) <= a < 2^e, or a == 0 */
+    int qe = e - 8;
+    if (qe < -133)
+        qe = -133;
+    const double m = floor(ldexp(a, -qe));       /* a = (m + f) * 2^qe, 0 <= f < 1 */
+    const double lo = ldexp(m, qe);
+    const double hi = ldexp(m + 1.0, qe);
+    const double mid = ldexp(m + 0.5, qe);
+    const int odd = fmod(m, 2.0) != 0.0;
+    const double r = (a > mid || (a == mid && odd)) ? hi : lo;
+    if (r >= 0x1p128)
+        return sign | 0x7F80;                    /* beyond the largest bf16: infinity */
+    const float f = (float)r;                    /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)(u >> 16);
 }
 
 /*
@@ -327,97 +361,43 @@ void oracle_grad_gate(const int32_t* rows, const uint16_t* g, const float* eN, i
  * "Projection / Normalization" stage between the table lookup and the trunk,
  * and the summary of "Qwen3.8-Flash-Next: …" fuses the n-gram vector with the
  * 1-gram embedding "via a gating network".  Neither page defines the two.
- * Form taken (every step one IEEE fp32 operation):
- *   S      = the blocked sum over j of eN[j] * eN[j];
+ * Form taken, per token, from its fp32 sum x = eN (d columns):
+ *   S      = sum over j of x[j]^2;
  *   r      = 1 / sqrt(S / d + eps);
- *   n[j]   = (eN[j] * r) * gamma[j];                  RMS normalisation
- *   Z      = the blocked sum over j of u[j] e1[j] + v[j] n[j];
- *   logit  = Z + b;   alpha = 1 / (1 + exp(-logit));   sigmoid gate unit
- *   h[j]   = fmaf(alpha * W_g[j], n[j], e1[j]);  y = residual + h (or h);
- *   out[j] = bf16 round-to-nearest-even of y.
- * The blocked sum fixes the order (d a multiple of 8):
- *   - group g = columns 8g .. 8g+7: a chain of fmaf over its columns in
- *     order, from +0 (for Z each column adds u e1, then v n);
- *   - block c = groups 64c .. 64c+63 (512 columns; groups past the end are
- *     +0): a pairwise tree, p[l] = p[l] + p[l + w] for w = 1, 2, 4, …, 32 and
- *     l a multiple of 2w, the block's sum being p[0];
- *   - the block sums added in block order, starting from block 0's.
+ *   n[j]   = x[j] * r * gamma[j];                          RMS normalisation
+ *   logit  = sum over j of (u[j] e1[j] + v[j] n[j]) + b;
+ *   alpha  = 1 / (1 + exp(-logit));                        sigmoid gate unit
+ *   y[j]   = residual[j] + e1[j] + alpha W_g[j] n[j];
+ *   out[j] = y[j] rounded once to bf16, ties to even.
+ * The pages fix no precision for any of this, so it is evaluated here in
+ * float64, each sum over ascending j, and rounded to bf16 only at the end.
+ * stats_out (may be NULL) gets {r, logit} per token, y_out (may be NULL) y.
  */
-static float oracle_blocked_total(const float* group_sums, int32_t ngroups)
-{
-    float total = 0.0f;
-    for (int32_t c = 0; c * 64 < ngroups; ++c) {
-        float p[64];
-        for (int l = 0; l < 64; ++l)
-            p[l] = c * 64 + l < ngroups ? group_sums[c * 64 + l] : 0.0f;
-        for (int w = 1; w < 64; w *= 2)
-            for (int l = 0; l < 64; l += 2 * w)
-                p[l] = p[l] + p[l + w];
-        total = c == 0 ? p[0] : total + p[0];
-    }
-    return total;
-}
-
-/* Sum of squares of x[0..d) in the blocked order. */
-float oracle_blocked_sumsq(const float* x, int32_t d)
-{
-    const int32_t ng = d / 8;
-    float* gs = (float*)malloc(sizeof(float) * (size_t)(ng > 0 ? ng : 1));
-    for (int32_t g = 0; g < ng; ++g) {
-        float s = 0.0f;
-        for (int e = 0; e < 8; ++e)
-            s = fmaf(x[8 * g + e], x[8 * g + e], s);
-        gs[g] = s;
-    }
-    float total = oracle_blocked_total(gs, ng);
-    free(gs);
-    return total;
-}
-
-/* sum over j of a[j] b[j] + c[j] e[j] in the blocked order. */
-float oracle_blocked_dot2(const float* a, const float* b, const float* c, const float* e, int32_t d)
-{
-    const int32_t ng = d / 8;
-    float* gs = (float*)malloc(sizeof(float) * (size_t)(ng > 0 ? ng : 1));
-    for (int32_t g = 0; g < ng; ++g) {
-        float z = 0.0f;
-        for (int q = 0; q < 8; ++q) {
-            int32_t j = 8 * g + q;
-            z = fmaf(a[j], b[j], z);
-            z = fmaf(c[j], e[j], z);
-        }
-        gs[g] = z;
-    }
-    float total = oracle_blocked_total(gs, ng);
-    free(gs);
-    return total;
-}
-
-/* out[i][j] as above from the sums eN[n][d]; e1_rows[i] = w_t.  stats_out
- * (may be NULL) gets {r, logit} per token, y_out (may be NULL) the fp32 y. */
 void oracle_norm_gate_add(const float* eN, const int32_t* e1_rows, int64_t n, int32_t d,
                           const uint16_t* e1, const float* W_g, const float* gamma, const float* u,
                           const float* v, float b, float eps, const uint16_t* residual,
-                          uint16_t* out, float* stats_out, float* y_out)
+                          uint16_t* out, double* stats_out, double* y_out)
 {
-    float* nv = (float*)malloc(sizeof(float) * (size_t)d);
-    float* ev = (float*)malloc(sizeof(float) * (size_t)d);
+    double* nv = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
     for (int64_t i = 0; i < n; ++i) {
         const float* x = eN + i * d;
-        float S = oracle_blocked_sumsq(x, d);
-        float r = 1.0f / sqrtf(S / (float)d + eps);
         const uint16_t* e1_token = e1 + (int64_t)e1_rows[i] * d;
         const uint16_t* res_token = residual ? residual + i * d : NULL;
+        double S = 0.0;
+        for (int32_t j = 0; j < d; ++j)
+            S = S + (double)x[j] * (double)x[j];
+        const double r = 1.0 / sqrt(S / (double)d + (double)eps);
+        for (int32_t j = 0; j < d; ++j)
+            nv[j] = (double)x[j] * r * (double)gamma[j];
+        double Z = 0.0;
+        for (int32_t j = 0; j < d; ++j)
+            Z = Z + ((double)u[j] * (double)oracle_bf16_to_f32(e1_token[j]) + (double)v[j] * nv[j]);
+        const double logit = Z + (double)b;
+        const double alpha = 1.0 / (1.0 + exp(-logit));
         for (int32_t j = 0; j < d; ++j) {
-            nv[j] = (x[j] * r) * gamma[j];
-            ev[j] = oracle_bf16_to_f32(e1_token[j]);
-        }
-        float logit = oracle_blocked_dot2(u, ev, v, nv, d) + b;
-        float alpha = 1.0f / (1.0f + expf(-logit));
-        for (int32_t j = 0; j < d; ++j) {
-            float h = fmaf(alpha * W_g[j], nv[j], ev[j]);
-            float y = res_token ? oracle_bf16_to_f32(res_token[j]) + h : h;
-            out[i * d + j] = oracle_bf16_rne(y);
+            const double h = (double)oracle_bf16_to_f32(e1_token[j]) + alpha * (double)W_g[j] * nv[j];
+            const double y = res_token ? (double)oracle_bf16_to_f32(res_token[j]) + h : h;
+            out[i * d + j] = oracle_bf16_rne_f64(y);
             if (y_out)
                 y_out[i * d + j] = y;
         }
@@ -427,5 +407,4 @@ void oracle_norm_gate_add(const float* eN, const int32_t* e1_rows, int64_t n, in
         }
     }
     free(nv);
-    free(ev);
 }

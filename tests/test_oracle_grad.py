@@ -3,8 +3,10 @@
 The reference is torch autograd in float64 on the forward written with torch
 ops (embedding_bag sum, gate, residual) - a library derivative, independent
 of the oracle's C code - exact where every value is a small dyadic number,
-and within an fp32 rounding bound otherwise; plus exact-rational replays of
-the specified fp32 summation order on sampled elements.
+and within a rounding bound otherwise; plus exact-rational replays of the
+specified fp32 summation order of the table and e1 gradients on sampled
+elements, and exact rational sums for the gate gradient (a plain sum, defined
+with no order, rounded once to fp32).
 """
 from fractions import Fraction
 
@@ -81,8 +83,11 @@ def test_grads_within_fp32_rounding_of_autograd_on_general_values():
     assert np.all(np.abs(got - dT[q]) <= (cnt[q] + 1) * 2.0 ** -23 * mags[q] + 1e-30)
     qt, got_e1 = oracle.grad_e1(toks, rows, g)
     assert np.allclose(got_e1, de1[qt], rtol=0, atol=1e-4)
-    got_w = oracle.grad_gate(rows, g, eN32)
-    assert np.allclose(got_w, dW_ref, rtol=1e-5, atol=1e-4)
+    got_w, got_w64 = oracle.grad_gate(rows, g, eN32, with_f64=True)
+    mag_w = (np.abs(bf16_bits_to_f32(g).astype(np.float64)) * np.abs(eN32.astype(np.float64))).sum(axis=0)
+    n = toks.size
+    assert np.all(np.abs(got_w64 - dW_ref) <= 2 * n * 2.0 ** -53 * mag_w)    # two float64 sums of the same terms
+    assert np.array_equal(got_w, got_w64.astype(np.float32))                   # rounded once to fp32
 
 
 def test_table_grad_is_the_specified_fp32_fma_chain():
@@ -99,7 +104,7 @@ def test_table_grad_is_the_specified_fp32_fma_chain():
             assert acc.view(np.uint32) == got[qi, j].view(np.uint32)
 
 
-def test_e1_and_gate_grads_follow_the_specified_order():
+def test_e1_grad_follows_the_specified_order():
     toks, rows, g, W, T, e1 = _case(n=600, R=97, V=11, d=8, seed=6, dyadic=False)
     gf = bf16_bits_to_f32(g)
     qt, got = oracle.grad_e1(toks, rows, g)
@@ -109,16 +114,46 @@ def test_e1_and_gate_grads_follow_the_specified_order():
             for i in np.nonzero(toks == qt[qi])[0]:
                 acc = round_to_f32(f(acc) + f(gf[i, j]))
             assert acc.view(np.uint32) == got[qi, j].view(np.uint32)
-    eN = np.random.default_rng(7).standard_normal((600, 8)).astype(np.float32)
-    gw = oracle.grad_gate(rows, g, eN)
-    for j in range(8):
-        total = np.float32(0.0)
-        for c0 in range(0, 600, 256):                          # chunks of 256 tokens
-            part = np.float32(0.0)
-            for i in range(c0, min(600, c0 + 256)):
-                part = round_to_f32(f(gf[i, j]) * f(eN[i, j]) + f(part))
-            total = round_to_f32(f(total) + f(part))
-        assert total.view(np.uint32) == gw[j].view(np.uint32)
+
+
+def test_gate_grad_is_the_exact_sum_rounded_once():
+    """On values whose float64 partial sums are exact (bf16 integers times
+    fp32 values with few significant bits), dW_g is the exact rational sum
+    rounded once to fp32, whatever order a fp32 chain would have taken."""
+    rng = np.random.default_rng(9)
+    n, d = 700, 12
+    rows = np.zeros((n, K), np.int32)
+    g = _bf16(rng.integers(-7, 8, size=(n, d)).astype(np.float32))
+    eN = (rng.integers(1, 1 << 10, size=(n, d)) * np.exp2(rng.integers(-18, 10, size=(n, d)))).astype(np.float32)
+    eN *= rng.choice([-1.0, 1.0], size=(n, d)).astype(np.float32)
+    gf = bf16_bits_to_f32(g)
+    got = oracle.grad_gate(rows, g, eN)
+    seq_differs = 0
+    for j in range(d):
+        want = round_to_f32(sum((f(gf[i, j]) * f(eN[i, j]) for i in range(n)), Fraction(0)))
+        assert got[j].view(np.uint32) == want.view(np.uint32)
+        acc = np.float32(0.0)
+        for i in range(n):
+            acc = np.float32(acc + np.float32(gf[i, j] * eN[i, j]))
+        seq_differs += acc != want
+    assert seq_differs >= d // 2          # a sequential fp32 sum would not pass
+
+
+def test_gate_grad_float64_sum_within_its_bound_of_the_exact_sum():
+    """General values: the float64 sum lies within (n - 1) 2^-53 sum |g eN|
+    of the exact rational sum, and the fp32 result is it rounded once."""
+    rng = np.random.default_rng(10)
+    n, d = 513, 6
+    rows = np.zeros((n, K), np.int32)
+    g = _bf16(rng.standard_normal((n, d)).astype(np.float32))
+    eN = rng.standard_normal((n, d)).astype(np.float32)
+    gf = bf16_bits_to_f32(g)
+    got, got64 = oracle.grad_gate(rows, g, eN, with_f64=True)
+    for j in range(d):
+        exact = sum((f(gf[i, j]) * f(eN[i, j]) for i in range(n)), Fraction(0))
+        mag = float(sum(abs(f(gf[i, j]) * f(eN[i, j])) for i in range(n)))
+        assert abs(f(got64[j]) - exact) <= Fraction((n - 1) * 2.0 ** -53 * mag)
+        assert got[j] == np.float32(got64[j])
 
 
 def test_invalid_tokens_contribute_nothing():
@@ -152,7 +187,7 @@ def test_a_row_used_twice_by_one_token_counts_twice():
 
 
 @pytest.mark.parametrize("n", [1, 255, 256, 257, 513])
-def test_gate_grad_chunk_edges(n):
+def test_gate_grad_any_batch_size(n):
     rng = np.random.default_rng(n)
     rows = np.zeros((n, K), np.int32)
     g = _bf16(rng.integers(-3, 4, size=(n, 4)).astype(np.float32))

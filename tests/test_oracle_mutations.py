@@ -51,40 +51,43 @@ MUTATIONS = {
                            "acc[j] = W_g[j] * oracle_bf16_to_f32(g[i * d + j]) + acc[j];"),
     "grad_e1_keeps_invalid": ("if (tokens[i] != query[q] || rows[i * ORACLE_K] < 0)",
                               "if (tokens[i] != query[q])"),
-    "grad_gate_chunk_128": ("for (int64_t c0 = 0; c0 < n; c0 += 256) {\n            float part = 0.0f;\n"
-                            "            for (int64_t i = c0; i < n && i < c0 + 256; ++i) {",
-                            "for (int64_t c0 = 0; c0 < n; c0 += 128) {\n            float part = 0.0f;\n"
-                            "            for (int64_t i = c0; i < n && i < c0 + 128; ++i) {"),
-    "grad_gate_unfused": ("part = fmaf(oracle_bf16_to_f32(g[i * d + j]), eN[i * d + j], part);",
-                          "part = oracle_bf16_to_f32(g[i * d + j]) * eN[i * d + j] + part;"),
+    "grad_gate_float_accumulator": ("acc = acc + (double)oracle_bf16_to_f32(g[i * d + j]) * (double)eN[i * d + j];",
+                                    "acc = (float)(acc + (double)oracle_bf16_to_f32(g[i * d + j]) * (double)eN[i * d + j]);"),
+    "grad_gate_skips_first_token": ("for (int64_t i = 0; i < n; ++i) {\n            if (rows[i * ORACLE_K] < 0)",
+                                    "for (int64_t i = 1; i < n; ++i) {\n            if (rows[i * ORACLE_K] < 0)"),
+    "grad_gate_wrong_operand": ("* (double)eN[i * d + j];", "* (double)eN[i * d + (j + 1) % d];"),
     "mxfp4_nibbles_swapped": ("int code = (j % 2 == 0) ? (byte & 15) : (byte >> 4);",
                               "int code = (j % 2 == 0) ? (byte >> 4) : (byte & 15);"),
     "mxfp4_scale_group_16": ("int E = row[d / 2 + j / 32];", "int E = row[d / 2 + j / 16];"),
     "mxfp4_scale_bias_128": ("return ldexpf(oracle_e2m1(code), E - 127);", "return ldexpf(oracle_e2m1(code), E - 128);"),
     "e2m1_exponent_bias_0": ("ldexpf(1.0f + 0.5f * (float)m, e - 1);", "ldexpf(1.0f + 0.5f * (float)m, e);"),
     "mxfp4_nan_scale_ignored": ("    if (E == 255)\n        return NAN;\n", ""),
-    "grad_gate_keeps_invalid": ("if (rows[i * ORACLE_K] < 0)\n                    continue;\n                part",
-                                "part"),
-    "norm_drops_eps": ("sqrtf(S / (float)d + eps)", "sqrtf(S / (float)d)"),
-    "norm_mean_over_d_minus_1": ("sqrtf(S / (float)d + eps)", "sqrtf(S / (float)(d - 1) + eps)"),
-    "norm_no_gamma": ("nv[j] = (x[j] * r) * gamma[j];", "nv[j] = x[j] * r;"),
-    "norm_rsqrt_unfused_order": ("nv[j] = (x[j] * r) * gamma[j];", "nv[j] = x[j] * (r * gamma[j]);"),
-    "gate_sign_flipped": ("expf(-logit)", "expf(logit)"),
-    "gate_uv_swapped": ("oracle_blocked_dot2(u, ev, v, nv, d)", "oracle_blocked_dot2(v, ev, u, nv, d)"),
-    "gate_no_bias": ("oracle_blocked_dot2(u, ev, v, nv, d) + b;", "oracle_blocked_dot2(u, ev, v, nv, d);"),
-    "gate_alpha_not_applied": ("fmaf(alpha * W_g[j], nv[j], ev[j])", "fmaf(W_g[j], nv[j], ev[j])"),
-    "gate_uses_raw_sum": ("fmaf(alpha * W_g[j], nv[j], ev[j])", "fmaf(alpha * W_g[j], x[j], ev[j])"),
-    "blocked_tree_sequential": ("for (int w = 1; w < 64; w *= 2)\n            for (int l = 0; l < 64; l += 2 * w)\n"
-                                "                p[l] = p[l] + p[l + w];",
-                                "for (int l = 1; l < 64; ++l)\n            p[0] = p[0] + p[l];"),
-    "blocked_group_unfused": ("s = fmaf(x[8 * g + e], x[8 * g + e], s);", "s = x[8 * g + e] * x[8 * g + e] + s;"),
-    "blocked_skips_last_group": ("for (int32_t g = 0; g < ng; ++g) {\n        float s", "for (int32_t g = 0; g + 1 < ng; ++g) {\n        float s"),
+    "grad_gate_keeps_invalid": ("if (rows[i * ORACLE_K] < 0)\n                continue;\n            acc = acc +",
+                                "acc = acc +"),
+    "norm_drops_eps": ("sqrt(S / (double)d + (double)eps)", "sqrt(S / (double)d)"),
+    "norm_mean_over_d_minus_1": ("sqrt(S / (double)d + (double)eps)", "sqrt(S / (double)(d - 1) + (double)eps)"),
+    "norm_no_gamma": ("nv[j] = (double)x[j] * r * (double)gamma[j];", "nv[j] = (double)x[j] * r;"),
+    "norm_sum_in_float": ("S = S + (double)x[j] * (double)x[j];", "S = (float)(S + (double)x[j] * (double)x[j]);"),
+    "norm_skips_last_square": ("for (int32_t j = 0; j < d; ++j)\n            S = S +",
+                               "for (int32_t j = 0; j + 1 < d; ++j)\n            S = S +"),
+    "gate_sign_flipped": ("const double alpha = 1.0 / (1.0 + exp(-logit));",
+                          "const double alpha = 1.0 / (1.0 + exp(logit));"),
+    "gate_uv_swapped": ("Z = Z + ((double)u[j] * (double)oracle_bf16_to_f32(e1_token[j]) + (double)v[j] * nv[j]);",
+                        "Z = Z + ((double)v[j] * (double)oracle_bf16_to_f32(e1_token[j]) + (double)u[j] * nv[j]);"),
+    "gate_z_in_float": ("Z = Z + ((double)u[j] * (double)oracle_bf16_to_f32(e1_token[j]) + (double)v[j] * nv[j]);",
+                        "Z = (float)(Z + ((double)u[j] * (double)oracle_bf16_to_f32(e1_token[j]) + (double)v[j] * nv[j]));"),
+    "gate_no_bias": ("const double logit = Z + (double)b;", "const double logit = Z;"),
+    "gate_alpha_not_applied": ("alpha * (double)W_g[j] * nv[j]", "(double)W_g[j] * nv[j]"),
+    "gate_uses_raw_sum": ("alpha * (double)W_g[j] * nv[j]", "alpha * (double)W_g[j] * (double)x[j]"),
     "norm_gate_wrong_e1_row": ("const uint16_t* e1_token = e1 + (int64_t)e1_rows[i] * d;",
                                "const uint16_t* e1_token = e1 + (int64_t)(e1_rows[i] + 1) * d;"),
     "norm_gate_drops_residual": ("const uint16_t* res_token = residual ? residual + i * d : NULL;",
                                  "const uint16_t* res_token = NULL;"),
-    "dot_terms_reordered": ("            z = fmaf(a[j], b[j], z);\n            z = fmaf(c[j], e[j], z);",
-                            "            z = fmaf(c[j], e[j], z);\n            z = fmaf(a[j], b[j], z);"),
+    "norm_gate_rounds_through_fp32": ("out[i * d + j] = oracle_bf16_rne_f64(y);",
+                                      "out[i * d + j] = oracle_bf16_rne((float)y);"),
+    "bf16f64_ties_away": ("(a > mid || (a == mid && odd))", "(a >= mid)"),
+    "bf16f64_truncates": ("const double r = (a > mid || (a == mid && odd)) ? hi : lo;", "const double r = lo;"),
+    "bf16f64_spacing_off_by_one": ("int qe = e - 8;", "int qe = e - 9;"),
 }
 
 
@@ -97,7 +100,7 @@ def pins_for(name):
     what it needs); the whole set for anything else."""
     for prefix, f in (("grad_", "test_oracle_grad.py"), ("mxfp4_", "test_oracle_mxfp4.py"),
                       ("e2m1_", "test_oracle_mxfp4.py"), ("norm_", "test_oracle_norm_gate.py"),
-                      ("blocked_", "test_oracle_norm_gate.py"), ("dot_", "test_oracle_norm_gate.py"),
+                      ("bf16f64_", "test_oracle_norm_gate.py"), ("gate_z_", "test_oracle_norm_gate.py"),
                       ("gate_sign", "test_oracle_norm_gate.py"), ("gate_uv", "test_oracle_norm_gate.py"),
                       ("gate_no_bias", "test_oracle_norm_gate.py"), ("gate_alpha", "test_oracle_norm_gate.py"),
                       ("gate_uses_raw", "test_oracle_norm_gate.py"), ("sum_", "test_oracle_sum_gate.py"),
