@@ -36,6 +36,10 @@ class _Table(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class _Launch(ctypes.Structure):
+    _fields_ = [("tokens_per_workgroup", ctypes.c_int32), ("host_workgroups", ctypes.c_int32)]
+
+
 class _Pool(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("row_scale", ctypes.c_void_p), ("slot_of_row", ctypes.c_void_p),
                 ("pool_rows", ctypes.c_int64), ("cached", ctypes.c_int64)]
@@ -51,11 +55,17 @@ _SIGNATURES = {
     "ngram_default_seeds": (None, [_P]),
     "ngram_hash": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I64, _P, _P]),
     "ngram_embed_bag": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, _P]),
+    "ngram_embed_bag_ex": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, ctypes.POINTER(_Launch), _P]),
     "ngram_gate_add": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P]),
     "ngram_forward": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, ctypes.POINTER(_Table), _P, _I64,
                                      _P, _P, _P, _P, _P]),
+    "ngram_forward_ex": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, ctypes.POINTER(_Table), _P, _I64,
+                                        _P, _P, _P, _P, ctypes.POINTER(_Launch), _P]),
     "ngram_forward_gated": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, ctypes.POINTER(_Table), _P, _I64,
                                            _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _P]),
+    "ngram_forward_gated_ex": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, ctypes.POINTER(_Table), _P, _I64,
+                                              _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P,
+                                              ctypes.POINTER(_Launch), _P]),
     "ngram_host_alloc": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
     "ngram_host_free": (ctypes.c_int, [_P]),
     "ngram_gather_host": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, _P, _P, _P]),
@@ -135,6 +145,15 @@ def default_seeds():
     s = (ctypes.c_uint64 * K)()
     lib().ngram_default_seeds(s)
     return [int(x) for x in s]
+
+
+def _launch_arg(launch):
+    """``launch``: None, or (tokens_per_workgroup, host_workgroups), 0 for the
+    library's choice of either."""
+    if launch is None:
+        return None
+    tpw, hw = launch
+    return ctypes.byref(_Launch(int(tpw), int(hw)))
 
 
 def _seeds_arg(seeds):
@@ -237,7 +256,7 @@ def ngram_hash(tokens, seq_offsets, R, rows_out=None, history=None, seeds=None, 
     return rows_out
 
 
-def ngram_embed_bag(table: Table, rows, eN_out=None, stream=None):
+def ngram_embed_bag(table: Table, rows, eN_out=None, launch=None, stream=None):
     _dev(rows, _I32T, "rows")
     n = rows.shape[0] if rows.dim() == 2 else rows.numel() // K
     if eN_out is None:
@@ -245,8 +264,11 @@ def ngram_embed_bag(table: Table, rows, eN_out=None, stream=None):
     _dev(eN_out, _F32, "eN_out")
     _need(rows, n * K, "rows")
     _need(eN_out, n * table.d, "eN_out")
-    _check(lib().ngram_embed_bag(table.c, _ptr(rows), n, _ptr(eN_out), _stream(stream)),
-           "ngram_embed_bag")
+    if launch is None:
+        rc = lib().ngram_embed_bag(table.c, _ptr(rows), n, _ptr(eN_out), _stream(stream))
+    else:
+        rc = lib().ngram_embed_bag_ex(table.c, _ptr(rows), n, _ptr(eN_out), _launch_arg(launch), _stream(stream))
+    _check(rc, "ngram_embed_bag")
     return eN_out
 
 
@@ -269,7 +291,7 @@ def ngram_gate_add(eN, tokens, W_g, out, e1=None, residual=None, stream=None):
 
 
 def ngram_forward(tokens, seq_offsets, table: Table, W_g, out, e1=None, residual=None,
-                  history=None, seeds=None, rows_out=None, stream=None):
+                  history=None, seeds=None, rows_out=None, launch=None, stream=None):
     _dev(tokens, _I32T, "tokens")
     _dev(seq_offsets, _I32T, "seq_offsets")
     _dev(history, _I32T, "history", allow_none=True)
@@ -285,17 +307,21 @@ def ngram_forward(tokens, seq_offsets, table: Table, W_g, out, e1=None, residual
     _need(residual, n * d, "residual")
     _need(rows_out, n * K, "rows_out")
     _need(history, 2 * (seq_offsets.numel() - 1), "history")
-    _check(lib().ngram_forward(_ptr(tokens), tokens.numel(), _ptr(seq_offsets), seq_offsets.numel() - 1,
-                               _ptr(history), _seeds_arg(seeds), table.c, _ptr(e1), V, _ptr(W_g),
-                               _ptr(residual), _ptr(out), _ptr(rows_out), _stream(stream)),
-           "ngram_forward")
+    args = (_ptr(tokens), tokens.numel(), _ptr(seq_offsets), seq_offsets.numel() - 1, _ptr(history),
+            _seeds_arg(seeds), table.c, _ptr(e1), V, _ptr(W_g), _ptr(residual), _ptr(out), _ptr(rows_out))
+    if launch is None:
+        rc = lib().ngram_forward(*args, _stream(stream))
+    else:
+        rc = lib().ngram_forward_ex(*args, _launch_arg(launch), _stream(stream))
+    _check(rc, "ngram_forward")
     return out
 
 
 def ngram_forward_gated(tokens, seq_offsets, table: Table, W_g, gamma, u, v, b, eps, out, e1,
-                        residual=None, history=None, seeds=None, rows_out=None, stats_out=None, stream=None):
+                        residual=None, history=None, seeds=None, rows_out=None, stats_out=None, launch=None,
+                        stream=None):
     """Normalised, input-gated forward (see ngram_forward_gated in ngram.h);
-    ``stats_out`` [n][2] fp32 receives (r, logit) per token."""
+    ``stats_out`` [n][2] float64 receives (r, logit) per token."""
     _dev(tokens, _I32T, "tokens")
     _dev(seq_offsets, _I32T, "seq_offsets")
     _dev(history, _I32T, "history", allow_none=True)
@@ -305,7 +331,7 @@ def ngram_forward_gated(tokens, seq_offsets, table: Table, W_g, gamma, u, v, b, 
     _dev(e1, _BF16, "e1")
     _dev(residual, _BF16, "residual", allow_none=True)
     _dev(rows_out, _I32T, "rows_out", allow_none=True)
-    _dev(stats_out, _F32, "stats_out", allow_none=True)
+    _dev(stats_out, (torch.float64,), "stats_out", allow_none=True)
     V = _vocab(e1, table.d)
     n, d = tokens.numel(), table.d
     for t, name in ((W_g, "W_g"), (gamma, "gamma"), (u, "u"), (v, "v")):
@@ -315,11 +341,14 @@ def ngram_forward_gated(tokens, seq_offsets, table: Table, W_g, gamma, u, v, b, 
     _need(rows_out, n * K, "rows_out")
     _need(stats_out, 2 * n, "stats_out")
     _need(history, 2 * (seq_offsets.numel() - 1), "history")
-    _check(lib().ngram_forward_gated(_ptr(tokens), n, _ptr(seq_offsets), seq_offsets.numel() - 1,
-                                     _ptr(history), _seeds_arg(seeds), table.c, _ptr(e1), V, _ptr(W_g),
-                                     _ptr(gamma), _ptr(u), _ptr(v), float(b), float(eps), _ptr(residual),
-                                     _ptr(out), _ptr(rows_out), _ptr(stats_out), _stream(stream)),
-           "ngram_forward_gated")
+    args = (_ptr(tokens), n, _ptr(seq_offsets), seq_offsets.numel() - 1, _ptr(history), _seeds_arg(seeds),
+            table.c, _ptr(e1), V, _ptr(W_g), _ptr(gamma), _ptr(u), _ptr(v), float(b), float(eps), _ptr(residual),
+            _ptr(out), _ptr(rows_out), _ptr(stats_out))
+    if launch is None:
+        rc = lib().ngram_forward_gated(*args, _stream(stream))
+    else:
+        rc = lib().ngram_forward_gated_ex(*args, _launch_arg(launch), _stream(stream))
+    _check(rc, "ngram_forward_gated")
     return out
 
 

@@ -17,7 +17,7 @@
 // 16 rows, so one load instruction reads 1 KiB contiguous of one row.  The
 // compiler keeps about ten of the 16 loads of a slice in flight before the
 // first add at 76 VGPRs (six wavefronts per SIMD); forcing all 16 ahead
-// (NGRAM_SCHED_BARRIER=1) costs 122 VGPRs and measured 2% slower.  The row ids
+// costs 122 VGPRs and measured 2% slower.  The row ids
 // are wave-uniform (read from LDS, moved to scalar registers), so each row
 // address is a scalar base plus a per-lane offset.  The sum runs in fp32 in
 // k order, the gate is one fused multiply-add, the residual one add, and the
@@ -34,20 +34,6 @@
 #include <string.h>
 
 #include "ngram.h"
-
-// Compile-time cache-policy and scheduling choices of the slice loads.
-#ifndef NGRAM_SCHED_BARRIER
-#define NGRAM_SCHED_BARRIER 0      // 1: force all 16 row loads before the first add
-#endif
-#ifndef NGRAM_SADDR
-#define NGRAM_SADDR 1              // row loads as scalar row base + 32-bit lane offset
-#endif
-#ifndef NGRAM_NT_TABLE
-#define NGRAM_NT_TABLE 0           // nontemporal table-row loads
-#endif
-#ifndef NGRAM_NT_OUT
-#define NGRAM_NT_OUT 0             // nontemporal output stores
-#endif
 
 namespace {
 
@@ -199,13 +185,7 @@ template <> struct Row8<NGRAM_TABLE_BF16> {
     __device__ static uint32_t lane_off(int64_t j0) { return static_cast<uint32_t>(j0) * 2u; }
     __device__ static Raw load(gbytes row, uint32_t off, uint32_t aux) {
         (void)aux;
-        const __attribute__((address_space(1))) u32x4* p =
-            reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(row + off);
-#if NGRAM_NT_TABLE
-        const u32x4 v = __builtin_nontemporal_load(p);
-#else
-        const u32x4 v = *p;
-#endif
+        const u32x4 v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(row + off);
         return make_uint4(v.x, v.y, v.z, v.w);
     }
 };
@@ -215,13 +195,7 @@ template <> struct Row8<NGRAM_TABLE_INT8_ROWSCALE> {
     __device__ static uint32_t lane_off(int64_t j0) { return static_cast<uint32_t>(j0); }
     __device__ static Raw load(gbytes row, uint32_t off, uint32_t aux) {
         (void)aux;
-        const __attribute__((address_space(1))) u32x2* p =
-            reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(row + off);
-#if NGRAM_NT_TABLE
-        const u32x2 v = __builtin_nontemporal_load(p);
-#else
-        const u32x2 v = *p;
-#endif
+        const u32x2 v = *reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(row + off);
         return make_uint2(v.x, v.y);
     }
 };
@@ -242,11 +216,7 @@ template <> struct Row8<NGRAM_TABLE_MXFP4> {
 __device__ inline void store_out(uint16_t* o, const uint4& v) {
     u32x4 w;
     w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
-#if NGRAM_NT_OUT
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o));
-#else
     *reinterpret_cast<u32x4*>(o) = w;
-#endif
 }
 
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -297,13 +267,11 @@ __device__ inline void gather_load(typename Row8<DT>::Raw v[kK], const void* __r
                                    int64_t d, int64_t j0) {
     uint32_t off = Row8<DT>::lane_off(j0);
     uint32_t aux = static_cast<uint32_t>(d >> 1) + (static_cast<uint32_t>(j0) >> 5);
-#if NGRAM_SADDR
     // Materialise the lane offsets here as 32-bit registers: each row load is
     // then the row's scalar base plus this offset, with no 64-bit address
     // computed per lane and row.
     if constexpr (DT == NGRAM_TABLE_MXFP4) __asm__ volatile("" : "+v"(off), "+v"(aux));
     else __asm__ volatile("" : "+v"(off));
-#endif
     const int64_t rb = Row8<DT>::row_bytes(d);
 #pragma unroll
     for (int k = 0; k < kK; ++k) v[k] = Row8<DT>::load(uniform_row(tab, r[k], rb), off, aux);
@@ -343,16 +311,10 @@ __device__ inline void gather_sum(float acc[8], const void* __restrict__ tab,
                                   int64_t d, int64_t j0) {
     typename Row8<DT>::Raw v[kK];
     gather_load<DT>(v, tab, r, d, j0);
-#if NGRAM_SCHED_BARRIER
-    // Keep the scheduler from sinking loads below the adds: all 16 row
-    // loads of the slice are in flight before the first one is consumed.
-    __builtin_amdgcn_sched_barrier(0);
-#else
     // MXFP4 rows take 2 registers per row slice, so all 32 loads fit in
     // flight before the first add (measured 3% faster; for int8 the same
-    // costs 101 VGPRs and 20%)
+    // costs 101 VGPRs and 20%, for bf16 122 VGPRs and 2%)
     if constexpr (DT == NGRAM_TABLE_MXFP4) __builtin_amdgcn_sched_barrier(0);
-#endif
     gather_reduce<DT>(acc, v, scale, r);
 }
 
@@ -529,30 +491,29 @@ __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows,
 // Normalised, input-gated fusion ("Qwen 3.8 Flash-Next Deep Dive…": a
 // "Projection / Normalization" stage after the lookup; "Qwen3.8-Flash-Next:
 // …", summary: fusion "via a gating network"; the pages define neither, the
-// form taken is):
-//   r = 1 / sqrt(S / d + eps),  S = blocked sum of eN[j]^2,
-//   n[j] = (eN[j] * r) * gamma[j],
-//   logit = Z + b,  Z = blocked sum of u[j] e1[j] + v[j] n[j],
+// form taken is), per token from its fp32 sum eN:
+//   r = 1 / sqrt(S / d + eps),  S = sum over j of eN[j]^2,
+//   n[j] = eN[j] r gamma[j],
+//   logit = sum over j of (u[j] e1[j] + v[j] n[j]) + b,
 //   alpha = 1 / (1 + exp(-logit)),
-//   out[j] = bf16(residual[j] + fmaf(alpha * W_g[j], n[j], e1[j])).
-// The blocked order maps onto the workgroup: a lane's 8 columns are one group
-// (an fma chain), a wavefront's 64 groups one block (a pairwise tree, which
-// the xor butterfly below computes in every lane), and the block sums are
-// added in block order from LDS.
+//   out[j] = bf16(residual[j] + e1[j] + alpha W_g[j] n[j]).
+// All of it is evaluated in float64 (the squares and the u e1 products of
+// fp32 and bf16 values are exact there) and rounded to bf16 once, from the
+// float64 value.  The sums have no stated order; on CDNA4 a lane adds its 8
+// columns, a 64-lane xor butterfly adds the wavefront's lanes, and the
+// wavefronts' sums meet in LDS.
 struct GatedArgs {
     FwdArgs f;
     const float* gamma;
     const float* u;
     const float* v;
-    float* stats;       // [n][2] = (r, logit), or null
+    double* stats;      // [n][2] = (r, logit), or null
     float b;
     float eps;
 };
 
-// The pairwise tree over the wavefront's 64 lanes in lane order: at width w
-// lane l adds lane l ^ w, i.e. left + right in the tree's left lanes and the
-// same sum (commuted, hence bit-identical) in its right lanes.
-__device__ inline float wave_tree_sum(float x) {
+// The sum of x over the wavefront's 64 lanes, in every lane.
+__device__ inline double wave_sum(double x) {
 #pragma unroll
     for (int w = 1; w < 64; w <<= 1) x = x + __shfl_xor(x, w, 64);
     return x;
@@ -565,19 +526,33 @@ __device__ inline void load_f8(float w[8], const float* __restrict__ p, int64_t 
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
+// float64 to bf16, rounded once to nearest, ties to even; NaN to 0x7FC0.
+// Rounding to fp32 toward zero and setting the last bit when that dropped
+// anything ("round to odd") keeps the information a second rounding needs:
+// fp32 carries 16 more significant bits than bf16 over the same exponent
+// range, so the fp32-to-bf16 rounding to nearest even that follows decides
+// exactly as a direct rounding of x would.
+__device__ inline uint32_t bf16_rne_f64(double x) {
+    if (x != x) return kNaNbf16;
+    const float t = __double2float_rz(x);
+    uint32_t u = __float_as_uint(t);
+    if (static_cast<double>(t) != x) u |= 1u;
+    return bf16_rne(__uint_as_float(u));
+}
+
 // One tile: wavefront w owns columns 512w .. 512w+511 (one block; the launch
 // has one wavefront per block).  Each token takes two workgroup barriers, one
-// per blocked sum; a token's validity is uniform over the workgroup, so every
-// wavefront reaches the same barriers.
+// per sum over its columns; a token's validity is uniform over the workgroup,
+// so every wavefront reaches the same barriers.
 template <int DT, bool RES, bool FULL>
-__device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lrows, int32_t* ltok, float* lred) {
+__device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lrows, int32_t* ltok, double* lred) {
     const FwdArgs& a = g.f;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const uint32_t jl = static_cast<uint32_t>(wave * kSlice + lane * kVec);   // the lane's first column
     const bool col = FULL || jl < static_cast<uint32_t>(d);  // FULL: d a multiple of 512, all lanes have columns
-    hash_tile(a, tile0, lrows, ltok, reinterpret_cast<int32_t*>(lred + a.tpw * 2 * nwaves));
+    hash_tile(a, tile0, lrows, ltok, lrows + a.tpw * (kK + 1));
 
     const int64_t rem = a.n - tile0;
     const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
@@ -590,12 +565,12 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
                 *reinterpret_cast<uint4*>(a.out + i * d + jl) = make_uint4(nn, nn, nn, nn);
             }
             if (g.stats && threadIdx.x == 0) {
-                g.stats[2 * i] = __uint_as_float(kNaNf32);
-                g.stats[2 * i + 1] = __uint_as_float(kNaNf32);
+                g.stats[2 * i] = __longlong_as_double(0x7FF8000000000000ll);
+                g.stats[2 * i + 1] = __longlong_as_double(0x7FF8000000000000ll);
             }
             continue;
         }
-        float* red = lred + tl * 2 * nwaves;         // [2][nwaves], one slot set per token
+        double* red = lred + tl * 2 * nwaves;        // [2][nwaves], one slot set per token
         float acc[8];
         if (col) {
             int32_t r[kK];
@@ -606,19 +581,21 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
         }
-        float s = 0.0f;
+        double s = 0.0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = __builtin_fmaf(acc[e], acc[e], s);
-        s = wave_tree_sum(s);
+        for (int e = 0; e < 8; ++e) s = s + static_cast<double>(acc[e]) * static_cast<double>(acc[e]);
+        s = wave_sum(s);
         if (lane == 0) red[wave] = s;
         __syncthreads();
-        float S = red[0];
+        double S = red[0];
         for (int w = 1; w < nwaves; ++w) S = S + red[w];
-        const float rn = 1.0f / sqrtf(S / static_cast<float>(d) + g.eps);
+        const double rn = 1.0 / sqrt(S / static_cast<double>(d) + static_cast<double>(g.eps));
 
-        // n overwrites acc; the e1 slice stays packed until the output.
+        // n = eN r gamma is formed again after the second barrier (the same
+        // operations give the same bits), so only the fp32 sums, r and the
+        // packed e1 slice stay live across it.
         uint4 e1v = make_uint4(0u, 0u, 0u, 0u);
-        float z = 0.0f;
+        double z = 0.0;
         if (col) {
             const gbytes e1row = uniform_row(a.e1, c0, 2 * d);
             const u32x4 e1w = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(e1row + 2u * jl);
@@ -631,38 +608,42 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
             load_f8(vv, g.v, jl);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                acc[e] = (acc[e] * rn) * gm[e];
-                z = __builtin_fmaf(uu[e], ev[e], z);
-                z = __builtin_fmaf(vv[e], acc[e], z);
+                const double nv = static_cast<double>(acc[e]) * rn * static_cast<double>(gm[e]);
+                z = z + (static_cast<double>(uu[e]) * static_cast<double>(ev[e]) + static_cast<double>(vv[e]) * nv);
             }
         }
-        z = wave_tree_sum(z);
+        z = wave_sum(z);
         if (lane == 0) red[nwaves + wave] = z;
         __syncthreads();
-        float Z = red[nwaves];
+        double Z = red[nwaves];
         for (int w = 1; w < nwaves; ++w) Z = Z + red[nwaves + w];
-        const float logit = Z + g.b;
-        const float alpha = 1.0f / (1.0f + expf(-logit));
+        const double logit = Z + static_cast<double>(g.b);
+        const double alpha = 1.0 / (1.0 + exp(-logit));
         if (col) {
             const float ev[8] = {bf16lo(e1v.x), bf16hi(e1v.x), bf16lo(e1v.y), bf16hi(e1v.y),
                                  bf16lo(e1v.z), bf16hi(e1v.z), bf16lo(e1v.w), bf16hi(e1v.w)};
-            float w8[8];
+            float gm[8], w8[8];
+            load_f8(gm, g.gamma, jl);
             load_w8(w8, a.wg, jl);
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = __builtin_fmaf(alpha * w8[e], acc[e], ev[e]);
+            float rf[8];
             if constexpr (RES) {
                 const uint4 rv = *reinterpret_cast<const uint4*>(a.res + i * d + jl);
-                y[0] = bf16lo(rv.x) + y[0]; y[1] = bf16hi(rv.x) + y[1];
-                y[2] = bf16lo(rv.y) + y[2]; y[3] = bf16hi(rv.y) + y[3];
-                y[4] = bf16lo(rv.z) + y[4]; y[5] = bf16hi(rv.z) + y[5];
-                y[6] = bf16lo(rv.w) + y[6]; y[7] = bf16hi(rv.w) + y[7];
+                rf[0] = bf16lo(rv.x); rf[1] = bf16hi(rv.x); rf[2] = bf16lo(rv.y); rf[3] = bf16hi(rv.y);
+                rf[4] = bf16lo(rv.z); rf[5] = bf16hi(rv.z); rf[6] = bf16lo(rv.w); rf[7] = bf16hi(rv.w);
+            }
+            uint32_t ob[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double nv = static_cast<double>(acc[e]) * rn * static_cast<double>(gm[e]);
+                double y = static_cast<double>(ev[e]) + alpha * static_cast<double>(w8[e]) * nv;
+                if constexpr (RES) y = static_cast<double>(rf[e]) + y;
+                ob[e] = bf16_rne_f64(y);
             }
             uint4 ov;
-            ov.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
-            ov.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
-            ov.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
-            ov.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
+            ov.x = ob[0] | (ob[1] << 16);
+            ov.y = ob[2] | (ob[3] << 16);
+            ov.z = ob[4] | (ob[5] << 16);
+            ov.w = ob[6] | (ob[7] << 16);
             store_out(a.out + i * d + jl, ov);
         }
         if (g.stats && threadIdx.x == 0) {
@@ -675,9 +656,12 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
 template <int DT, bool RES, bool FULL, bool PERSIST>
 __global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
     extern __shared__ int32_t lds[];
-    int32_t* lrows = lds;                                            // [tpw][16]
-    int32_t* ltok = lds + g.f.tpw * kK;                              // [tpw]
-    float* lred = reinterpret_cast<float*>(lds + g.f.tpw * (kK + 1));  // [tpw][2][nwaves]
+    // [tpw][2][nwaves] float64 sums first (8-byte aligned), then the row
+    // lists [tpw][16], w_t [tpw] and the staged sequence table
+    const int nwaves = blockDim.x >> 6;
+    double* lred = reinterpret_cast<double*>(lds);
+    int32_t* lrows = lds + 2 * (g.f.tpw * 2 * nwaves);
+    int32_t* ltok = lrows + g.f.tpw * kK;
     if constexpr (!PERSIST) {
         gated_tile<DT, RES, FULL>(g, static_cast<int64_t>(blockIdx.x) * g.f.tpw, lrows, ltok, lred);
     } else {
@@ -1324,64 +1308,90 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
     }
 }
 
-// dW_g: per chunk of 256 tokens, part = fmaf(g, eN, part) in ascending token
-// order (skipping invalid tokens); then the chunk parts summed in order.
-constexpr int kGateChunk = 256;
+// dW_g[j] = the sum over valid tokens i of g[i][j] eN[i][j], accumulated in
+// float64 (each product of a bf16 and an fp32 value is exact there) and
+// rounded once to fp32.  The sum has no stated order; here: per chunk of
+// kGateChunk tokens, each of a workgroup's 4 wavefronts sums a quarter of the
+// chunk, the quarters are added in LDS, and the chunk partials are then added
+// per column.  The order is fixed, so the bits are reproducible.
+constexpr int kGateChunk = 128;
+constexpr int kGateWaves = 4;
+constexpr int kGateCols = 4;       // columns per lane: 256 per wavefront
+constexpr int kGateUnroll = 8;     // tokens whose loads are issued together
 
-// One wavefront per (chunk, 256 columns): 4 columns per lane, 8 tokens'
-// loads issued before their fmas, which still run in token order.
-constexpr int kGateCols = 4;
-constexpr int kGateUnroll = 8;
-
-__global__ void __launch_bounds__(64) gate_grad_partial_kernel(const int32_t* __restrict__ rows,
-                                                               const uint16_t* __restrict__ g,
-                                                               const float* __restrict__ eN, int64_t n, int32_t d,
-                                                               float* __restrict__ partials) {
+__global__ void __launch_bounds__(256) gate_grad_partial_kernel(const int32_t* __restrict__ rows,
+                                                                const uint16_t* __restrict__ g,
+                                                                const float* __restrict__ eN, int64_t n, int32_t d,
+                                                                double* __restrict__ partials) {
+    __shared__ double lp[kGateWaves][64 * kGateCols];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t c = blockIdx.x;
-    const int64_t j0 = (static_cast<int64_t>(blockIdx.y) * 64 + threadIdx.x) * kGateCols;
-    if (j0 >= d) return;                      // no cross-lane operations below
-    const int64_t i0 = c * kGateChunk;
-    const int64_t i1 = i0 + kGateChunk < n ? i0 + kGateChunk : n;
-    float part[kGateCols] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t ib = i0; ib < i1; ib += kGateUnroll) {
-        uint2 gv[kGateUnroll];
-        float4 ev[kGateUnroll];
-        bool ok[kGateUnroll];
+    const int64_t j0 = (static_cast<int64_t>(blockIdx.y) * 64 + lane) * kGateCols;
+    const bool col = j0 < d;           // d % 8 == 0, so the lane's 4 columns are all in range
+    constexpr int kPerWave = kGateChunk / kGateWaves;
+    const int64_t i0 = c * kGateChunk + wave * kPerWave;
+    const int64_t i1 = i0 + kPerWave < n ? i0 + kPerWave : n;
+    double part[kGateCols] = {0.0, 0.0, 0.0, 0.0};
+    if (col) {
+        for (int64_t ib = i0; ib < i1; ib += kGateUnroll) {
+            uint2 gv[kGateUnroll];
+            float4 ev[kGateUnroll];
+            bool ok[kGateUnroll];
 #pragma unroll
-        for (int u = 0; u < kGateUnroll; ++u) {
-            const int64_t i = ib + u < i1 ? ib + u : ib;
-            ok[u] = ib + u < i1 && rows[i * kK] >= 0;
-            gv[u] = *reinterpret_cast<const uint2*>(g + i * d + j0);
-            ev[u] = *reinterpret_cast<const float4*>(eN + i * d + j0);
-        }
+            for (int q = 0; q < kGateUnroll; ++q) {
+                const int64_t i = ib + q < i1 ? ib + q : ib;
+                ok[q] = ib + q < i1 && rows[i * kK] >= 0;
+                gv[q] = *reinterpret_cast<const uint2*>(g + i * d + j0);
+                ev[q] = *reinterpret_cast<const float4*>(eN + i * d + j0);
+            }
 #pragma unroll
-        for (int u = 0; u < kGateUnroll; ++u) {
-            if (!ok[u]) continue;
-            part[0] = __builtin_fmaf(bf16lo(gv[u].x), ev[u].x, part[0]);
-            part[1] = __builtin_fmaf(bf16hi(gv[u].x), ev[u].y, part[1]);
-            part[2] = __builtin_fmaf(bf16lo(gv[u].y), ev[u].z, part[2]);
-            part[3] = __builtin_fmaf(bf16hi(gv[u].y), ev[u].w, part[3]);
+            for (int q = 0; q < kGateUnroll; ++q) {
+                if (!ok[q]) continue;
+                part[0] = part[0] + static_cast<double>(bf16lo(gv[q].x)) * static_cast<double>(ev[q].x);
+                part[1] = part[1] + static_cast<double>(bf16hi(gv[q].x)) * static_cast<double>(ev[q].y);
+                part[2] = part[2] + static_cast<double>(bf16lo(gv[q].y)) * static_cast<double>(ev[q].z);
+                part[3] = part[3] + static_cast<double>(bf16hi(gv[q].y)) * static_cast<double>(ev[q].w);
+            }
         }
     }
-    *reinterpret_cast<float4*>(partials + c * d + j0) = make_float4(part[0], part[1], part[2], part[3]);
+#pragma unroll
+    for (int e = 0; e < kGateCols; ++e) lp[wave][lane * kGateCols + e] = part[e];
+    __syncthreads();
+    if (wave == 0 && col) {
+#pragma unroll
+        for (int e = 0; e < kGateCols; ++e) {
+            double t = lp[0][lane * kGateCols + e];
+            for (int w = 1; w < kGateWaves; ++w) t = t + lp[w][lane * kGateCols + e];
+            partials[c * d + j0 + e] = t;
+        }
+    }
 }
 
-__global__ void __launch_bounds__(256) gate_grad_total_kernel(const float* __restrict__ partials, int64_t nchunks,
-                                                              int32_t d, float* __restrict__ out) {
-    const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (j >= d) return;
-    float total = 0.0f;
-    for (int64_t c = 0; c < nchunks; ++c) total = total + partials[c * d + j];
-    out[j] = total;
+// Per column: the chunk partials, 16 wavefronts each adding every 16th chunk,
+// then the 16 sums in wavefront order, rounded once to fp32.
+constexpr int kGateTotalWaves = 16;
+
+__global__ void __launch_bounds__(1024) gate_grad_total_kernel(const double* __restrict__ partials, int64_t nchunks,
+                                                               int32_t d, float* __restrict__ out) {
+    __shared__ double red[kGateTotalWaves][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+    double t = 0.0;
+    if (j < d) {
+#pragma unroll 8
+        for (int64_t c = wave; c < nchunks; c += kGateTotalWaves) t = t + partials[c * d + j];
+    }
+    red[wave][lane] = t;
+    __syncthreads();
+    if (wave == 0 && j < d) {
+        double s = red[0][lane];
+        for (int w = 1; w < kGateTotalWaves; ++w) s = s + red[w][lane];
+        out[j] = static_cast<float>(s);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Host side.
-int env_int(const char* name, int dflt) {
-    const char* v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
-}
-
 int hip_status(const char* what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(NGRAM_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -1460,12 +1470,11 @@ struct Shape {
 // slices leave the per-workgroup hash phase and barrier a larger share of the
 // time (measured on MI355X at 2560 columns: int8 5.3 TB/s at 1 token per
 // workgroup, 6.6 TB/s at 4; bf16 best at 1).
-Shape slice_shape(int64_t n, int32_t d, int32_t dtype) {
-    (void)n;
+Shape slice_shape(int64_t n, int32_t d, int32_t dtype, const ngram_launch* L) {
     const int nslices = (d + kSlice - 1) / kSlice;
     Shape s;
     s.waves = nslices < 16 ? nslices : 16;
-    int tpw = env_int("NGRAM_TOKENS_PER_WG", 0);
+    int tpw = L ? L->tokens_per_workgroup : 0;
     if (tpw <= 0) tpw = dtype == NGRAM_TABLE_BF16 ? 1 : 4;     // int8, MXFP4: 4
     if (tpw > 64) tpw = 64;
     s.tpw = tpw;
@@ -1480,9 +1489,10 @@ Shape slice_shape(int64_t n, int32_t d, int32_t dtype) {
 // 5M x 2560 bf16 host table, against a bf16 GEMM loop on another stream):
 // 8 workgroups read at 58 GB/s and leave 4.3 ms of an 11.6 ms gather
 // exposed; 64 leave 9.5 ms, 256 leave 12.5 ms.
-int host_workgroups() {
-    const int v = env_int("NGRAM_HOST_WORKGROUPS", 0);
-    return v > 0 ? v : 8;
+constexpr int kHostWorkgroups = 8;
+
+int host_workgroups(const ngram_launch* L) {
+    return L && L->host_workgroups > 0 ? L->host_workgroups : kHostWorkgroups;
 }
 
 int64_t table_row_bytes(const ngram_table* T) {
@@ -1552,7 +1562,7 @@ GradLayout grad_layout(int64_t n, int32_t d) {
     L.segs = o; o = up(o + 4 * (L.N + 1));
     L.hist = o; o = up(o + 4 * 256 * (L.nblocks > 0 ? L.nblocks : 1));
     L.tiles = o; o = up(o + 4 * 2 * kScanTile);
-    L.parts = o; o = up(o + 4 * ((n + kGateChunk - 1) / kGateChunk) * static_cast<int64_t>(d > 0 ? d : 1));
+    L.parts = o; o = up(o + 8 * ((n + kGateChunk - 1) / kGateChunk) * static_cast<int64_t>(d > 0 ? d : 1));
     L.total = o;
     return L;
 }
@@ -1627,11 +1637,18 @@ int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* val
     return hip_status("gradient launch");
 }
 
-void cap_for_host(Shape& sh, const ngram_table* T) {
-    if (T->location == NGRAM_IN_HOST && sh.grid > host_workgroups()) {
-        sh.grid = host_workgroups();
+void cap_for_host(Shape& sh, const ngram_table* T, const ngram_launch* L) {
+    if (T->location == NGRAM_IN_HOST && sh.grid > host_workgroups(L)) {
+        sh.grid = host_workgroups(L);
         sh.persist = true;
     }
+}
+
+int check_launch(const ngram_launch* L) {
+    if (L && (L->tokens_per_workgroup < 0 || L->tokens_per_workgroup > 64 || L->host_workgroups < 0 ||
+              L->host_workgroups > 65536))
+        return fail(NGRAM_EINVAL, "launch: tokens_per_workgroup must be in [0, 64], host_workgroups in [0, 65536]");
+    return NGRAM_OK;
 }
 
 template <int DT, bool E1, bool RES>
@@ -1658,7 +1675,7 @@ template <int DT>
 void launch_gated_dt(const GatedArgs& g, const Shape& sh, hipStream_t st) {
     const int nb = (g.f.d + kSlice - 1) / kSlice;
     const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * nb);
-    const size_t lds = static_cast<size_t>(sh.tpw) * ((kK + 1) * sizeof(int32_t) + 2 * nb * sizeof(float)) +
+    const size_t lds = static_cast<size_t>(sh.tpw) * ((kK + 1) * sizeof(int32_t) + 2 * nb * sizeof(double)) +
                        (g.f.stage ? kSeqLds * sizeof(int32_t) : 0);
     const bool res = g.f.res != nullptr, full = g.f.d % kSlice == 0;
     if (sh.persist) {
@@ -1721,8 +1738,15 @@ int ngram_hash(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int
 
 int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
                     ngram_stream_t stream) {
+    return ngram_embed_bag_ex(T, rows, n, eN_out, nullptr, stream);
+}
+
+int ngram_embed_bag_ex(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
+                       const ngram_launch* launch, ngram_stream_t stream) {
     g_err[0] = 0;
     int rc = check_table(T);
+    if (rc) return rc;
+    rc = check_launch(launch);
     if (rc) return rc;
     if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
     if (n > INT32_MAX) return fail(NGRAM_ERANGE, "n=%lld above 2^31-1", (long long)n);
@@ -1735,8 +1759,8 @@ int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float*
     BagArgs a;
     a.tab = tab; a.scale = T->row_scale; a.rows = rows; a.eN = eN_out;
     a.n = n; a.R = T->R; a.d = T->d;
-    Shape sh = slice_shape(n, T->d, T->dtype);
-    cap_for_host(sh, T);
+    Shape sh = slice_shape(n, T->d, T->dtype, launch);
+    cap_for_host(sh, T, launch);
     a.tpw = sh.tpw;
     const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
@@ -1784,8 +1808,18 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
                   const int32_t* history, const uint64_t* seeds, const ngram_table* T,
                   const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
                   uint16_t* out, int32_t* rows_out, ngram_stream_t stream) {
+    return ngram_forward_ex(tokens, n, seq_offsets, S, history, seeds, T, e1, V, W_g, residual, out, rows_out,
+                            nullptr, stream);
+}
+
+int ngram_forward_ex(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                     const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                     const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
+                     uint16_t* out, int32_t* rows_out, const ngram_launch* launch, ngram_stream_t stream) {
     g_err[0] = 0;
     int rc = check_tokens(tokens, n, seq_offsets, S);
+    if (rc) return rc;
+    rc = check_launch(launch);
     if (rc) return rc;
     rc = check_table(T);
     if (rc) return rc;
@@ -1806,8 +1840,8 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
     a.c0_limit = c0_limit_for(e1, V);
     a.stage = stage_for(n, S);
     a.sd = make_seeds(seeds);
-    Shape sh = slice_shape(n, T->d, T->dtype);
-    cap_for_host(sh, T);
+    Shape sh = slice_shape(n, T->d, T->dtype, launch);
+    cap_for_host(sh, T, launch);
     a.tpw = sh.tpw;
     if (T->dtype == NGRAM_TABLE_BF16) launch_fwd_dt<NGRAM_TABLE_BF16>(a, sh, stream);
     else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) launch_fwd_dt<NGRAM_TABLE_INT8_ROWSCALE>(a, sh, stream);
@@ -1819,9 +1853,21 @@ int ngram_forward_gated(const int32_t* tokens, int64_t n, const int32_t* seq_off
                         const int32_t* history, const uint64_t* seeds, const ngram_table* T,
                         const uint16_t* e1, int64_t V, const float* W_g, const float* gamma, const float* u,
                         const float* v, float b, float eps, const uint16_t* residual, uint16_t* out,
-                        int32_t* rows_out, float* stats_out, ngram_stream_t stream) {
+                        int32_t* rows_out, double* stats_out, ngram_stream_t stream) {
+    return ngram_forward_gated_ex(tokens, n, seq_offsets, S, history, seeds, T, e1, V, W_g, gamma, u, v, b, eps,
+                                  residual, out, rows_out, stats_out, nullptr, stream);
+}
+
+int ngram_forward_gated_ex(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                           const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                           const uint16_t* e1, int64_t V, const float* W_g, const float* gamma, const float* u,
+                           const float* v, float b, float eps, const uint16_t* residual, uint16_t* out,
+                           int32_t* rows_out, double* stats_out, const ngram_launch* launch,
+                           ngram_stream_t stream) {
     g_err[0] = 0;
     int rc = check_tokens(tokens, n, seq_offsets, S);
+    if (rc) return rc;
+    rc = check_launch(launch);
     if (rc) return rc;
     rc = check_table(T);
     if (rc) return rc;
@@ -1847,15 +1893,15 @@ int ngram_forward_gated(const int32_t* tokens, int64_t n, const int32_t* seq_off
     a.stage = stage_for(n, S);
     a.sd = make_seeds(seeds);
     g.gamma = gamma; g.u = u; g.v = v; g.stats = stats_out; g.b = b; g.eps = eps;
-    Shape sh = slice_shape(n, T->d, T->dtype);
-    if (T->dtype == NGRAM_TABLE_BF16 && env_int("NGRAM_TOKENS_PER_WG", 0) <= 0) {
+    Shape sh = slice_shape(n, T->d, T->dtype, launch);
+    if (T->dtype == NGRAM_TABLE_BF16 && !(launch && launch->tokens_per_workgroup > 0)) {
         // Two tokens per workgroup measured best for the gated bf16 path on
         // MI355X at the prefill shape: 1 token 526 us, 2 tokens 514 us,
         // 4 tokens 521 us per launch.
         sh.tpw = 2;
         sh.grid = (n + 1) / 2;
     }
-    cap_for_host(sh, T);
+    cap_for_host(sh, T, launch);
     a.tpw = sh.tpw;
     if (T->dtype == NGRAM_TABLE_BF16) launch_gated_dt<NGRAM_TABLE_BF16>(g, sh, stream);
     else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) launch_gated_dt<NGRAM_TABLE_INT8_ROWSCALE>(g, sh, stream);
@@ -1912,7 +1958,7 @@ int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
     a.remap = remap_out; a.nrows = n * kK; a.R = T_host->R;
     a.row_bytes = table_row_bytes(T_host);
     int64_t blocks = (a.nrows + 15) / 16;
-    if (blocks > host_workgroups()) blocks = host_workgroups();
+    if (blocks > kHostWorkgroups) blocks = kHostWorkgroups;
     const dim3 grid(static_cast<unsigned>(blocks)), block(1024);
     if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x4>, grid, block, 0, stream, a);
     else if (a.row_bytes % 8 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x2>, grid, block, 0, stream, a);
@@ -1950,7 +1996,7 @@ int ngram_pool_cache_rows(const ngram_table* T_host, ngram_row_pool* P, const in
     if (C > 0) {
         const int64_t row_bytes = table_row_bytes(T_host);
         int64_t blocks = (C + 15) / 16;
-        if (blocks > host_workgroups()) blocks = host_workgroups();
+        if (blocks > kHostWorkgroups) blocks = kHostWorkgroups;
         float* pscale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? P->row_scale : nullptr;
         if (row_bytes % 16 == 0)
             hipLaunchKernelGGL(pool_cache_kernel<u32x4>, dim3(blocks), dim3(1024), 0, stream, tab, T_host->row_scale,
@@ -2005,7 +2051,7 @@ int ngram_pool_gather(const ngram_table* T_host, const ngram_row_pool* P, const 
     hipLaunchKernelGGL(pool_insert_kernel, g, b, 0, stream, a);
     hipLaunchKernelGGL(pool_resolve_kernel, g, b, 0, stream, a);
     int64_t blocks = (a.nrows + 15) / 16;
-    if (blocks > host_workgroups()) blocks = host_workgroups();
+    if (blocks > kHostWorkgroups) blocks = kHostWorkgroups;
     if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(pool_fetch_kernel<u32x4>, dim3(blocks), dim3(1024), 0, stream, a);
     else if (a.row_bytes % 8 == 0) hipLaunchKernelGGL(pool_fetch_kernel<u32x2>, dim3(blocks), dim3(1024), 0, stream, a);
     else hipLaunchKernelGGL(pool_fetch_kernel<uint32_t>, dim3(blocks), dim3(1024), 0, stream, a);
@@ -2125,15 +2171,15 @@ int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, 
     if (!grad_Wg_out) return fail(NGRAM_EINVAL, "grad_Wg_out is NULL");
     if (n > 0 && (!rows || !eN || !aligned(eN, 16))) return fail(NGRAM_EINVAL, "rows or eN is NULL/misaligned");
     const GradLayout L = grad_layout(n, d);
-    float* parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.parts);
+    double* parts = reinterpret_cast<double*>(static_cast<char*>(workspace) + L.parts);
     const int64_t nchunks = (n + kGateChunk - 1) / kGateChunk;
     if (nchunks > 0) {
         const unsigned colblocks = static_cast<unsigned>((d / kGateCols + 63) / 64);
-        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks), colblocks), dim3(64), 0,
-                           stream, rows, dout, eN, n, d, parts);
+        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks), colblocks),
+                           dim3(64 * kGateWaves), 0, stream, rows, dout, eN, n, d, parts);
     }
-    hipLaunchKernelGGL(gate_grad_total_kernel, dim3(static_cast<unsigned>((d + 255) / 256)), dim3(256), 0, stream,
-                       parts, nchunks, d, grad_Wg_out);
+    hipLaunchKernelGGL(gate_grad_total_kernel, dim3(static_cast<unsigned>((d + 63) / 64)), dim3(64 * kGateTotalWaves),
+                       0, stream, parts, nchunks, d, grad_Wg_out);
     return hip_status("ngram_grad_gate launch");
 }
 

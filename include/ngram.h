@@ -89,6 +89,19 @@ typedef struct {
     int32_t reserved;
 } ngram_table;
 
+/* Launch-shape overrides, for tuning and for tests that cover several tile
+ * shapes; the plain entry points use the library's own choice.  Results are
+ * bit-identical for every value: only the speed changes.
+ *   tokens_per_workgroup: tokens a gather workgroup hashes into LDS and then
+ *     gathers (0: the library's choice, 1 for bf16 tables, 4 for int8 and
+ *     MXFP4 tables, 2 on the gated path over bf16 tables; at most 64);
+ *   host_workgroups: the grid cap for a table in pinned host memory, whose
+ *     workgroups then loop over the tiles (0: the library's choice, 8). */
+typedef struct {
+    int32_t tokens_per_workgroup;
+    int32_t host_workgroups;
+} ngram_launch;
+
 const char* ngram_status_string(int status);
 const char* ngram_last_error(void);
 int ngram_version(void);
@@ -113,6 +126,10 @@ int ngram_hash(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int
  * Errors: EINVAL, EALIGN, ERANGE (see ngram_table). */
 int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
                     ngram_stream_t stream);
+/* The same with launch-shape overrides (NULL: none); EINVAL for values out of
+ * range. */
+int ngram_embed_bag_ex(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
+                       const ngram_launch* launch, ngram_stream_t stream);
 
 /* Gate and residual: "Qwen3.8-Flash-Next: …", Key point 1, and the
  * residual add of "N-grams, of all things": out[i][j] = bf16(residual[i][j] +
@@ -133,32 +150,41 @@ int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, 
                   const int32_t* history, const uint64_t* seeds, const ngram_table* T,
                   const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
                   uint16_t* out, int32_t* rows_out, ngram_stream_t stream);
+int ngram_forward_ex(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                     const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                     const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
+                     uint16_t* out, int32_t* rows_out, const ngram_launch* launch, ngram_stream_t stream);
 
 /* Normalised, input-gated variant of ngram_forward.  "Qwen 3.8 Flash-Next
  * Deep Dive…" draws a "Projection / Normalization" stage after the lookup and
  * "Qwen3.8-Flash-Next: …" (summary) fuses the n-gram and 1-gram vectors "via a
  * gating network"; neither is defined there.  Form taken, per token, from its
  * fp32 sum eN:
- *   r      = 1 / sqrt(S / d + eps),   S = blocked sum over j of eN[j]^2;
- *   n[j]   = (eN[j] * r) * gamma[j];
- *   logit  = Z + b,   Z = blocked sum over j of u[j] e1[j] + v[j] n[j];
+ *   r      = 1 / sqrt(S / d + eps),   S = sum over j of eN[j]^2;
+ *   n[j]   = eN[j] r gamma[j];
+ *   logit  = sum over j of (u[j] e1[j] + v[j] n[j]) + b;
  *   alpha  = 1 / (1 + exp(-logit));
- *   out[j] = bf16(residual[j] + fmaf(alpha * W_g[j], n[j], e1[w_t][j])).
- * Blocked sum: groups of 8 columns (an fmaf chain in column order; for Z each
- * column adds u e1 then v n), blocks of 64 groups (a pairwise tree in group
- * order, missing groups +0), block sums added in block order.  Every step is
- * one IEEE fp32 operation except exp, so r and logit are reproducible bit for
- * bit; alpha may differ from another libm's by an ulp or so.
+ *   out[j] = bf16(residual[j] + e1[w_t][j] + alpha W_g[j] n[j]).
+ * Everything after eN is evaluated in float64 and the output is rounded once
+ * to bf16 from the float64 value (ties to even).  The sums have no stated
+ * order, so r and the logit can differ from another float64 evaluation by a
+ * few units in the last place (a relative error of order d 2^-53).
  * e1 [V][d] bf16 is required; gamma, u, v [d] fp32 (device, 16-byte aligned);
- * eps finite >= 0, b finite; d <= 8192 (ERANGE).  stats_out [n][2] fp32
- * (device, may be NULL) receives (r, logit) per token, NaN for an invalid
- * token.  Other arguments and rules as ngram_forward. */
+ * eps finite >= 0, b finite; d <= 8192 (ERANGE).  stats_out [n][2] float64
+ * (device, 8-byte aligned, may be NULL) receives (r, logit) per token, NaN
+ * for an invalid token.  Other arguments and rules as ngram_forward. */
 int ngram_forward_gated(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
                         const int32_t* history, const uint64_t* seeds, const ngram_table* T,
                         const uint16_t* e1, int64_t V, const float* W_g, const float* gamma,
                         const float* u, const float* v, float b, float eps,
                         const uint16_t* residual, uint16_t* out, int32_t* rows_out,
-                        float* stats_out, ngram_stream_t stream);
+                        double* stats_out, ngram_stream_t stream);
+int ngram_forward_gated_ex(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
+                           const int32_t* history, const uint64_t* seeds, const ngram_table* T,
+                           const uint16_t* e1, int64_t V, const float* W_g, const float* gamma,
+                           const float* u, const float* v, float b, float eps,
+                           const uint16_t* residual, uint16_t* out, int32_t* rows_out,
+                           double* stats_out, const ngram_launch* launch, ngram_stream_t stream);
 
 /* Pinned-host-table path, "N-grams, of all things" / "Which is why the
  * offload matters more than the parameter count": the table shard sits in
@@ -288,10 +314,11 @@ int ngram_grad_e1(const int32_t* tokens, const int32_t* rows, int64_t n, int32_t
                   int64_t* n_unique_out, void* workspace, int64_t workspace_bytes,
                   ngram_stream_t stream);
 
-/* Gate gradient: grad_Wg_out[j] = sum over chunks of 256 tokens, in order, of
- * the chunk's acc = fmaf(dout[i][j], eN[i][j], acc) over its valid tokens in
- * ascending i, from +0.  eN [n][d] fp32 is the forward's sum (ngram_embed_bag);
- * grad_Wg_out [d] fp32. */
+/* Gate gradient: grad_Wg_out[j] = the sum over valid tokens i of
+ * dout[i][j] eN[i][j], accumulated in float64 (every product is exact there)
+ * and rounded once to fp32; the sum has no stated order, but the library's
+ * is fixed, so the bits are reproducible.  eN [n][d] fp32 is the forward's
+ * sum (ngram_embed_bag); grad_Wg_out [d] fp32. */
 int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, int64_t n, int32_t d,
                     float* grad_Wg_out, void* workspace, int64_t workspace_bytes,
                     ngram_stream_t stream);

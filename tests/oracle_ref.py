@@ -47,16 +47,16 @@ def expected(h, sample=None, rows_all=None):
 
 def expected_gated(h, gp, sample=None, rows_all=None):
     """The normalised, gated fusion with parameters ``gp``: (rows [n][16],
-    out [m][d] bf16 bits, stats [m][2] = (r, logit), y [m][d] fp32, mag
-    [m][d] = |residual| + |e1| + |y - residual - e1| in float64, the size of
-    the terms y is made of)."""
+    out [m][d] bf16 bits, stats [m][2] float64 = (r, logit), y [m][d]
+    float64, bounds = (r [m], logit [m], y [m][d]): how far another float64
+    evaluation may lie from the oracle's, see tests.tolerance)."""
+    from tests.tolerance import gated_bounds
     rows_all, eN, ids, e1c, res = _sampled(h, sample, rows_all)
     out, stats, y = oracle.norm_gate_add(eN, ids, e1c, h.W_g, gp.gamma, gp.u, gp.v, gp.b, gp.eps, res)
     f = lambda b: (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
-    e1v = f(e1c[ids])
-    rv = f(res) if res is not None else np.zeros_like(e1v)
-    mag = np.abs(rv) + np.abs(e1v) + np.abs(y.astype(np.float64) - rv - e1v)
-    return rows_all, out, stats, y, mag
+    bounds = gated_bounds(eN, f(e1c[ids]), f(res) if res is not None else None, h.W_g, gp.gamma, gp.u, gp.v,
+                          stats)
+    return rows_all, out, stats, y, bounds
 
 
 def sample_tokens(spec, m=64, seed=0):

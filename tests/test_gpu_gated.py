@@ -1,16 +1,19 @@
 """GPU parity of the normalised, input-gated forward (ngram_forward_gated)
 against the oracle, through the C ABI.
 
-Bar: row ids bit-exact; the normalisation factor r and the gate's logit
-bit-exact (every step to them is one IEEE fp32 operation in a stated order);
-bf16 outputs bit-exact except where the two sides' exp differ by an ulp and
-the oracle's fp32 value y lies that close to a bf16 rounding midpoint.  Then
-the two bf16 values are neighbours and y sits within 2^-20 of the size of its
-terms (|residual| + |e1| + |alpha W_g n|) from their midpoint: one ulp of
-alpha moves alpha W_g n by 2^-23 of itself, and the fma and the residual add
-each round once.  With the gate closed, half open or fully open (alpha exactly
-0, 1/2 or 1) every output is bit-exact.
+The oracle evaluates the fusion in float64 with each sum over ascending
+columns; the kernel evaluates it in float64 with its own order of the sums.
+Bar: row ids bit-exact; r and the logit within the bound two float64
+evaluations of those sums can differ by (tests.tolerance.gated_bounds, each
+step's error derived from the arithmetic, times a safety factor); bf16
+outputs equal to the oracle's except where the oracle's float64 y lies
+within its bound of a bf16 rounding midpoint, and then only the neighbour on
+the other side.  The number of such outputs is printed (it is expected to be
+0: the bounds are about 1e-12 of the values, against a bf16 spacing of about
+4e-3).
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -21,6 +24,8 @@ import synth  # noqa: E402
 from synth.workloads import CONFIGS, DeviceInputs, GateParams, HostInputs, Spec, gate_params  # noqa: E402
 from tests.oracle_ref import expected_gated, sample_tokens  # noqa: E402
 from tests.test_gpu_parity import bits16, say  # noqa: E402
+from tests.exact import round_to_bf16  # noqa: E402
+from tests.tolerance import assert_bf16_rounded_once, assert_f64_close  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -30,56 +35,42 @@ def _f32(b):
     return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def assert_gated_equal(got, want, y, mag, what, max_frac=1e-3):
-    got = np.asarray(got, np.uint16).reshape(want.shape)
-    diff = got != want
-    nan_w = np.isnan(_f32(want))
-    assert np.array_equal(np.isnan(_f32(got)), nan_w), f"{what}: NaN pattern differs"
-    diff &= ~nan_w
-    nd = int(diff.sum())
-    assert nd <= max(2, max_frac * want.size), f"{what}: {nd} of {want.size} bf16 values differ"
-    if nd:
-        gi, wi = got[diff].astype(np.int32), want[diff].astype(np.int32)
-        assert np.all((gi >> 15) == (wi >> 15)) and np.all(np.abs(gi - wi) == 1), \
-            f"{what}: differing values are not bf16 neighbours"
-        mid = (_f32(got[diff]) + _f32(want[diff])) / 2
-        dist = np.abs(y[diff].astype(np.float64) - mid) / mag[diff]
-        assert np.all(dist <= 2.0 ** -20), \
-            f"{what}: {nd} differ, max distance from the midpoint {dist.max():.3g} of the terms' size"
-
-
-def run_gated(di: DeviceInputs, gp: GateParams, out_of_place=False):
+def run_gated(di: DeviceInputs, gp: GateParams, out_of_place=False, launch=None):
     sp = di.spec
     dev = di.tokens.device
     out = di.residual if (di.residual is not None and not out_of_place) else \
         torch.empty(sp.n * sp.d, dtype=torch.int16, device=dev)
     rows = torch.empty((sp.n, 16), dtype=torch.int32, device=dev)
-    stats = torch.empty((sp.n, 2), dtype=torch.float32, device=dev)
+    stats = torch.empty((sp.n, 2), dtype=torch.float64, device=dev)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     ng.ngram_forward_gated(di.tokens, di.offsets, di.table_obj(), di.W_g, t(gp.gamma), t(gp.u), t(gp.v),
                            gp.b, gp.eps, out, di.e1, residual=di.residual, history=di.history,
-                           rows_out=rows, stats_out=stats)
+                           rows_out=rows, stats_out=stats, launch=launch)
     torch.cuda.synchronize()
     return bits16(out).reshape(sp.n, sp.d), rows.cpu().numpy(), stats.cpu().numpy()
 
 
-def check(sp: Spec, gp=None, sample=None, exact=False, **kw):
+def compare(out, stats, want, want_stats, y, bounds, what):
+    b_r, b_logit, b_y = bounds
+    assert_f64_close(stats[:, 0], want_stats[:, 0], b_r, f"{what} r")
+    assert_f64_close(stats[:, 1], want_stats[:, 1], b_logit, f"{what} logit")
+    near = assert_bf16_rounded_once(out, want, y, b_y, what)
+    say(f"{what}: {out.size} outputs, {near} at a bf16 midpoint within the bound")
+    return near
+
+
+def check(sp: Spec, gp=None, sample=None, **kw):
     gp = gp or gate_params(sp)
     say(f"gated {sp.name} n={sp.n} R={sp.R} d={sp.d} table={sp.table} res={sp.residual} hist={sp.history} "
         f"b={gp.b} {kw}")
     h = HostInputs(sp)
     di = DeviceInputs(sp, h)
     out, rows, stats = run_gated(di, gp, **kw)
-    want_rows, want, want_stats, y, mag = expected_gated(h, gp, sample=sample)
+    want_rows, want, want_stats, y, bounds = expected_gated(h, gp, sample=sample)
     assert np.array_equal(rows, want_rows), "row ids differ"
     if sample is not None:
         out, stats = out[sample], stats[sample]
-    assert np.array_equal(stats.view(np.uint32), want_stats.view(np.uint32)), \
-        f"r or logit differ: {np.argwhere(stats.view(np.uint32) != want_stats.view(np.uint32))[:5]}"
-    if exact:
-        assert np.array_equal(out, want), f"{int((out != want).sum())} outputs differ"
-    else:
-        assert_gated_equal(out, want, y, mag, sp.name)
+    compare(out, stats, want, want_stats, y, bounds, sp.name)
     return h, di, out
 
 
@@ -87,15 +78,23 @@ RAGGED = Spec("g_ragged", (1, 2, 3, 5, 0, 250, 33), 151936, 1_000_003, 2560,
               table_kind=synth.KIND_BF16_WIDE, residual=True, config_id=41)
 
 
-@pytest.mark.parametrize("b", [200.0, -200.0, 0.0])
-def test_gated_open_closed_and_half_gate_bit_exact(b):
-    """u = v = 0: logit = b exactly; alpha = 1 (b = 200), 0 (b = -200) or 1/2
-    (b = 0) on both sides, so every output is bit-exact."""
+@pytest.mark.parametrize("b", [200.0, -800.0, 0.0])
+def test_gated_open_closed_and_half_gate(b):
+    """u = v = 0: logit = b exactly on both sides, and alpha = 1 (b = 200),
+    0 (b = -800) or 1/2 (b = 0) exactly."""
     sp = Spec(f"g_open{b}", (200, 56), 151936, 100_003, 2560, table_kind=synth.KIND_BF16_WIDE,
               residual=True, config_id=46)
     gp0 = gate_params(sp)
     z = np.zeros(sp.d, np.float32)
-    check(sp, gp=GateParams(gp0.gamma, z, z, b, gp0.eps), exact=True)
+    h, di, _ = check(sp, gp=GateParams(gp0.gamma, z, z, b, gp0.eps))
+    if b == -800.0:
+        # a closed gate leaves residual + e1 rounded once to bf16, exactly
+        out, _, stats = run_gated(DeviceInputs(sp, h), GateParams(gp0.gamma, z, z, b, gp0.eps), out_of_place=True)
+        assert np.all(stats[:, 1] == b)
+        e1v, res = _f32(h.e1_rows(h.tokens)), _f32(h.full_residual())
+        for i in (0, 1, 100, sp.n - 1):
+            for j in (0, 1, sp.d - 1):
+                assert out[i, j] == round_to_bf16(Fraction(float(res[i, j])) + Fraction(float(e1v[i, j])))
 
 
 def test_gated_tiny():
@@ -124,11 +123,10 @@ def test_gated_quantised_tables(table, kind, d):
                residual=True, config_id=43))
 
 
-@pytest.mark.parametrize("tpw", ["1", "3", "64"])
-def test_gated_tokens_per_workgroup(tpw, monkeypatch):
-    monkeypatch.setenv("NGRAM_TOKENS_PER_WG", tpw)
+@pytest.mark.parametrize("tpw", [1, 3, 64])
+def test_gated_tokens_per_workgroup(tpw):
     check(Spec(f"gtpw{tpw}", (300, 7), 151936, 100_003, 2560, table_kind=synth.KIND_BF16_WIDE,
-               residual=True, config_id=44))
+               residual=True, config_id=44), launch=(tpw, 0))
 
 
 def test_gated_decode_with_history_no_residual():
@@ -159,18 +157,16 @@ def test_gated_invalid_tokens_give_nan():
     clean = [i for i in range(sp.n) if not any(i - k in changed and not any(s in range(i - k + 1, i + 1)
                                                                             for s in starts) for k in (0, 1, 2))]
     assert len(clean) > 40
-    _, want, want_stats, y, mag = expected_gated(h, gp, sample=np.array(clean))
-    assert np.array_equal(stats[clean].view(np.uint32), want_stats.view(np.uint32))
-    assert_gated_equal(out[clean], want, y, mag, "g_bad clean tokens")
+    _, want, want_stats, y, bounds = expected_gated(h, gp, sample=np.array(clean))
+    compare(out[clean], stats[clean], want, want_stats, y, bounds, "g_bad clean tokens")
 
 
 @pytest.mark.parametrize("table,kind,d", [("bf16", synth.KIND_BF16_WIDE, 2560), ("int8", synth.KIND_I8_NORMAL, 2560),
                                           ("mxfp4", synth.KIND_MXFP4_WIDE, 640)])
-def test_gated_host_table_equals_device_table(table, kind, d, monkeypatch):
+def test_gated_host_table_equals_device_table(table, kind, d):
     """The same table in pinned host memory (capped persistent grid) and in
     HBM gives bit-identical gated outputs and statistics."""
     from synth.workloads import fill_host_table
-    monkeypatch.setenv("NGRAM_HOST_WORKGROUPS", "5")
     sp = Spec(f"g_host_{table}", (300, 212), 151936, 20_003, d, table=table, table_kind=kind,
               residual=True, config_id=48)
     gp = gate_params(sp)
@@ -184,10 +180,10 @@ def test_gated_host_table_equals_device_table(table, kind, d, monkeypatch):
         fill_host_table(sp, hb.numpy(npdt, (sp.R, rb // np.dtype(npdt).itemsize)))
         dt = {"bf16": ng.TABLE_BF16, "int8": ng.TABLE_INT8_ROWSCALE, "mxfp4": ng.TABLE_MXFP4}[table]
         di.table_obj = lambda: ng.Table(hb, sp.R, sp.d, dt, row_scale=di.scale)
-        out_host, _, st_host = run_gated(di, gp, out_of_place=True)
+        out_host, _, st_host = run_gated(di, gp, out_of_place=True, launch=(0, 5))
     finally:
         hb.free()
-    assert np.array_equal(out_dev, out_host) and np.array_equal(st_dev.view(np.uint32), st_host.view(np.uint32))
+    assert np.array_equal(out_dev, out_host) and np.array_equal(st_dev.view(np.uint64), st_host.view(np.uint64))
 
 
 def test_gated_empty_batch():

@@ -1,5 +1,9 @@
-"""GPU gradients against the oracle, bit for bit: the distinct row and token
-lists (ascending) and every fp32 gradient value."""
+"""GPU gradients against the oracle: the distinct row and token lists
+(ascending) and every fp32 table and e1 gradient value bit for bit (both sides
+run the same stated fp32 order); the gate gradient, a plain sum accumulated in
+float64 and rounded once, equal to the oracle's rounding except where an fp32
+midpoint lies within the bound two float64 sums of the same terms can differ
+by (tests.tolerance)."""
 import numpy as np
 import pytest
 
@@ -9,6 +13,7 @@ import hashed_gram_embedding_ngram_amd as ng  # noqa: E402
 import oracle  # noqa: E402
 import synth  # noqa: E402
 from tests.test_gpu_parity import say  # noqa: E402
+from tests.tolerance import assert_f32_rounded_once, sum_bound  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -90,8 +95,16 @@ def test_gate_grad(n, d):
     eN[n // 2] = np.nan                      # an invalid token's sum is never read
     gw = ng.ngram_grad_gate(_dev(rows, np.int32), _dev(g.view(np.int16), np.int16), _dev(eN, np.float32))
     torch.cuda.synchronize()
-    want = oracle.grad_gate(rows, g, eN)
-    assert np.array_equal(gw.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    check_gate(gw.cpu().numpy(), rows, g, eN, f"dW_g n={n} d={d}")
+
+
+def check_gate(got, rows, g, eN, what):
+    _, want64 = oracle.grad_gate(rows, g, eN, with_f64=True)
+    valid = rows.reshape(-1, 16)[:, 0] >= 0
+    gf = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    mag = (np.abs(gf[valid]) * np.abs(eN[valid].astype(np.float64))).sum(axis=0)
+    near = assert_f32_rounded_once(got, want64, sum_bound(int(valid.sum()), mag), what)
+    say(f"{what}: {got.size} values, {near} at an fp32 midpoint within the bound")
 
 
 def test_grads_on_two_streams_equal_one_stream():
@@ -161,4 +174,4 @@ def test_full_prefill_backward_sampled():
     tp = np.unique(np.concatenate([[0, 1, 2], rng.integers(0, ut.size, 8)]))
     _, want_e = oracle.grad_e1(h.tokens, rows, g, query=ut[tp])
     assert np.array_equal(ge[torch.from_numpy(tp).cuda()].cpu().numpy().view(np.uint32), want_e.view(np.uint32))
-    assert np.array_equal(gw.cpu().numpy().view(np.uint32), oracle.grad_gate(rows, g, eN).view(np.uint32))
+    check_gate(gw.cpu().numpy(), rows, g, eN, "dW_g prefill")

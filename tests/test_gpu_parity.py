@@ -5,7 +5,6 @@ Bar: row ids bit-exact, fp32 sums bit-exact, bf16 outputs bit-exact (the
 relative-error bound of 1e-3 is below one bf16 ulp, so only identical bits
 meet it; the observed maximum relative error is asserted too).
 """
-import os
 
 import numpy as np
 import pytest
@@ -42,7 +41,7 @@ def assert_bf16_equal(got, want, what):
     assert rel.size == 0 or rel.max() <= REL_TOL
 
 
-def run_forward(di: DeviceInputs, out_of_place=False, seeds=None):
+def run_forward(di: DeviceInputs, out_of_place=False, seeds=None, launch=None):
     sp = di.spec
     if di.residual is not None and not out_of_place:
         out = di.residual
@@ -50,7 +49,7 @@ def run_forward(di: DeviceInputs, out_of_place=False, seeds=None):
         out = torch.empty(sp.n * sp.d, dtype=torch.int16, device=di.tokens.device)
     rows = torch.empty((sp.n, 16), dtype=torch.int32, device=di.tokens.device)
     ng.ngram_forward(di.tokens, di.offsets, di.table_obj(), di.W_g, out, e1=di.e1,
-                     residual=di.residual, history=di.history, rows_out=rows, seeds=seeds)
+                     residual=di.residual, history=di.history, rows_out=rows, seeds=seeds, launch=launch)
     torch.cuda.synchronize()
     return bits16(out).reshape(sp.n, sp.d), rows.cpu().numpy()
 
@@ -96,11 +95,18 @@ def test_optional_e1_and_residual(e1, res):
                     table_kind=synth.KIND_BF16_WIDE, e1=e1, residual=res, config_id=13))
 
 
-@pytest.mark.parametrize("tpw", ["1", "3", "64"])
-def test_tokens_per_workgroup(tpw, monkeypatch):
-    monkeypatch.setenv("NGRAM_TOKENS_PER_WG", tpw)
+@pytest.mark.parametrize("tpw", [1, 3, 64])
+def test_tokens_per_workgroup(tpw):
     check_spec(Spec(f"tpw{tpw}", (300, 7), 151936, 100_003, 2560,
-                    table_kind=synth.KIND_BF16_WIDE, residual=True, config_id=14))
+                    table_kind=synth.KIND_BF16_WIDE, residual=True, config_id=14), launch=(tpw, 0))
+
+
+def test_launch_override_out_of_range_is_refused():
+    sp = Spec("launch_bad", (8,), 100, 101, 64, config_id=14)
+    di = DeviceInputs(sp, HostInputs(sp))
+    for bad in ((65, 0), (-1, 0), (0, -2)):
+        with pytest.raises(ng.NgramError, match="EINVAL"):
+            run_forward(di, launch=bad)
 
 
 def test_decode_with_history():
@@ -256,15 +262,12 @@ def test_repeated_calls_are_deterministic():
     assert np.array_equal(a, b) and np.array_equal(ra, rb)
 
 
-@pytest.mark.parametrize("wgs,tpw,table", [("3", "1", "bf16"), ("5", "3", "bf16"), ("64", "4", "bf16"),
-                                           ("7", "2", "int8")])
-def test_host_table_paths(wgs, tpw, table, monkeypatch):
+@pytest.mark.parametrize("wgs,tpw,table", [(3, 1, "bf16"), (5, 3, "bf16"), (64, 4, "bf16"), (7, 2, "int8")])
+def test_host_table_paths(wgs, tpw, table):
     """Pinned-host table with a capped, persistent grid (several ragged tiles
     per workgroup): fused forward, zero-copy sum and staged gather all equal
     the oracle."""
     from synth.workloads import fill_host_table
-    monkeypatch.setenv("NGRAM_HOST_WORKGROUPS", wgs)
-    monkeypatch.setenv("NGRAM_TOKENS_PER_WG", tpw)
     kw = dict(table="int8", table_kind=synth.KIND_I8_NORMAL) if table == "int8" else \
         dict(table_kind=synth.KIND_BF16_WIDE)
     sp = Spec(f"host_{table}_{wgs}_{tpw}", (1, 40, 0, 300, 2), 151936, 20_011, 2560, residual=True,
@@ -285,8 +288,9 @@ def test_host_table_paths(wgs, tpw, table, monkeypatch):
         want_rows, want_eN, want_out = expected(h)
         out = torch.empty(sp.n * sp.d, dtype=torch.int16, device="cuda:0")
         rows = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
-        ng.ngram_forward(di.tokens, di.offsets, T, di.W_g, out, e1=di.e1, residual=di.residual, rows_out=rows)
-        eN = ng.ngram_embed_bag(T, rows)
+        ng.ngram_forward(di.tokens, di.offsets, T, di.W_g, out, e1=di.e1, residual=di.residual, rows_out=rows,
+                         launch=(tpw, wgs))
+        eN = ng.ngram_embed_bag(T, rows, launch=(tpw, wgs))
         stage = torch.empty(sp.n * 16 * sp.d * esize, dtype=torch.int8, device="cuda:0")
         remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
         sscale = torch.empty(sp.n * 16, dtype=torch.float32, device="cuda:0") if table == "int8" else None
@@ -413,9 +417,8 @@ def test_mxfp4_special_scales():
 
 
 @pytest.mark.parametrize("d", [128, 2560])
-def test_mxfp4_host_table_paths(d, monkeypatch):
+def test_mxfp4_host_table_paths(d):
     from synth.workloads import fill_host_table
-    monkeypatch.setenv("NGRAM_HOST_WORKGROUPS", "3")
     sp = Spec(f"mxfp4_host_d{d}", (40, 0, 90), 151936, 20_011, d, table="mxfp4",
               table_kind=synth.KIND_MXFP4_WIDE, config_id=30)
     say(sp.name)
@@ -427,7 +430,7 @@ def test_mxfp4_host_table_paths(d, monkeypatch):
         T = ng.Table(hb, sp.R, d, ng.TABLE_MXFP4)
         di = DeviceInputs(sp, h, table=False)
         rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
-        eN = ng.ngram_embed_bag(T, rows)
+        eN = ng.ngram_embed_bag(T, rows, launch=(0, 3))
         stage = torch.empty(sp.n * 16 * rb, dtype=torch.uint8, device="cuda:0")
         remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
         ng.ngram_gather_host(T, rows, stage, remap)
