@@ -79,6 +79,8 @@ _SIGNATURES = {
     "ngram_grad_table": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
     "ngram_grad_e1": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _P, _P, _P, _P, _I64, _P]),
     "ngram_grad_gate": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _P, _P, _I64, _P]),
+    "ngram_grad_gate_noalloc_max_elements": (ctypes.c_int64, []),
+    "ngram_grad_gate_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _P, _P]),
     "ngram_select_hot_rows": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.POINTER(ctypes.c_int64), _P, _I64, _P]),
 }
 
@@ -542,4 +544,21 @@ def ngram_grad_gate(rows, dout, eN, grad_Wg_out=None, workspace=None, stream=Non
     workspace = grad_workspace(n, d, eN.device) if workspace is None else workspace
     _check(lib().ngram_grad_gate(_ptr(rows), _ptr(dout), _ptr(eN), n, d, _ptr(grad_Wg_out), *_ws_args(workspace),
                                  _stream(stream)), "ngram_grad_gate")
+    return grad_Wg_out
+
+
+def ngram_grad_gate_noalloc(rows, dout, eN, grad_Wg_out=None, stream=None):
+    """The gate gradient without a workspace (the library's static scratch;
+    calls that overlap on one GPU race)."""
+    _dev(rows, _I32T, "rows")
+    _dev(dout, _BF16, "dout")
+    _dev(eN, _F32, "eN")
+    n, d = eN.shape
+    _need(rows, n * K, "rows")
+    _need(dout, n * d, "dout")
+    grad_Wg_out = torch.empty(d, dtype=torch.float32, device=eN.device) if grad_Wg_out is None else grad_Wg_out
+    _dev(grad_Wg_out, _F32, "grad_Wg_out")
+    _need(grad_Wg_out, d, "grad_Wg_out")
+    _check(lib().ngram_grad_gate_noalloc(_ptr(rows), _ptr(dout), _ptr(eN), n, d, _ptr(grad_Wg_out), _stream(stream)),
+           "ngram_grad_gate_noalloc")
     return grad_Wg_out

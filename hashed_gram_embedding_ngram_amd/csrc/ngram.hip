@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include <stdarg.h>
 #include <stdint.h>
@@ -1691,6 +1692,56 @@ void launch_gated_dt(const GatedArgs& g, const Shape& sh, hipStream_t st) {
 }
 
 
+// The gate gradient's two launches, given the float64 partials buffer
+// (nchunks x d doubles).
+void launch_gate_grad(const int32_t* rows, const uint16_t* dout, const float* eN, int64_t n, int32_t d,
+                      float* grad_Wg_out, double* parts, hipStream_t stream) {
+    const int64_t nchunks = (n + kGateChunk - 1) / kGateChunk;
+    if (nchunks > 0) {
+        const unsigned colblocks = static_cast<unsigned>((d / kGateCols + 63) / 64);
+        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks), colblocks),
+                           dim3(64 * kGateWaves), 0, stream, rows, dout, eN, n, d, parts);
+    }
+    hipLaunchKernelGGL(gate_grad_total_kernel, dim3(static_cast<unsigned>((d + 63) / 64)), dim3(64 * kGateTotalWaves),
+                       0, stream, parts, nchunks, d, grad_Wg_out);
+}
+
+// Scratch of the allocation-free gate gradient: the float64 chunk partials
+// live in this file-scope device array, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it only stands for the symbol): it passes the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr int64_t kNoAllocScratchBytes = int64_t{16} << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// each device, with that device current).
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NGRAM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(NGRAM_ENOTSUP, "device %d above the supported %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(NGRAM_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NGRAM_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -2172,15 +2223,31 @@ int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, 
     if (n > 0 && (!rows || !eN || !aligned(eN, 16))) return fail(NGRAM_EINVAL, "rows or eN is NULL/misaligned");
     const GradLayout L = grad_layout(n, d);
     double* parts = reinterpret_cast<double*>(static_cast<char*>(workspace) + L.parts);
-    const int64_t nchunks = (n + kGateChunk - 1) / kGateChunk;
-    if (nchunks > 0) {
-        const unsigned colblocks = static_cast<unsigned>((d / kGateCols + 63) / 64);
-        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks), colblocks),
-                           dim3(64 * kGateWaves), 0, stream, rows, dout, eN, n, d, parts);
-    }
-    hipLaunchKernelGGL(gate_grad_total_kernel, dim3(static_cast<unsigned>((d + 63) / 64)), dim3(64 * kGateTotalWaves),
-                       0, stream, parts, nchunks, d, grad_Wg_out);
+    launch_gate_grad(rows, dout, eN, n, d, grad_Wg_out, parts, stream);
     return hip_status("ngram_grad_gate launch");
+}
+
+int64_t ngram_grad_gate_noalloc_max_elements(void) { return kNoAllocScratchBytes / 8; }
+
+int ngram_grad_gate_noalloc(const int32_t* rows, const uint16_t* dout, const float* eN, int64_t n, int32_t d,
+                            float* grad_Wg_out, ngram_stream_t stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > (1 << 20)) return fail(NGRAM_ERANGE, "n=%lld above 2^20", (long long)n);
+    if (d <= 0 || d % kVec != 0) return fail(NGRAM_EINVAL, "d=%d must be a positive multiple of 8", d);
+    if (d > NGRAM_MAX_D) return fail(NGRAM_ERANGE, "d=%d above %d", d, NGRAM_MAX_D);
+    if (!grad_Wg_out) return fail(NGRAM_EINVAL, "grad_Wg_out is NULL");
+    if (n > 0 && (!rows || !dout || !aligned(dout, 16) || !eN || !aligned(eN, 16)))
+        return fail(NGRAM_EINVAL, "rows, dout or eN is NULL or dout / eN not 16-byte aligned");
+    const int64_t nchunks = (n + kGateChunk - 1) / kGateChunk;
+    if (nchunks * static_cast<int64_t>(d) > kNoAllocScratchBytes / 8)
+        return fail(NGRAM_ERANGE, "ceil(n/%d) * d = %lld partials exceed the %lld-double static scratch", kGateChunk,
+                    (long long)(nchunks * d), (long long)(kNoAllocScratchBytes / 8));
+    void* p = nullptr;
+    int rc = scratch_address(&p);
+    if (rc) return rc;
+    launch_gate_grad(rows, dout, eN, n, d, grad_Wg_out, static_cast<double*>(p), stream);
+    return hip_status("ngram_grad_gate_noalloc launch");
 }
 
 }  // extern "C"

@@ -323,6 +323,21 @@ int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, 
                     float* grad_Wg_out, void* workspace, int64_t workspace_bytes,
                     ngram_stream_t stream);
 
+/* The gate gradient with no workspace argument and no allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid it).  Same result, bit for bit,
+ * as ngram_grad_gate.  Its float64 chunk partials (ceil(n / 128) x d of them)
+ * live in a static device array of 16 MiB that the library holds on each GPU
+ * it runs on until the process ends: ceil(n / 128) * d must not exceed
+ * ngram_grad_gate_noalloc_max_elements() (2^21), else ERANGE and nothing is
+ * launched.  Calls on one GPU share that array, so calls that can overlap on
+ * one GPU (different streams, or other threads) race: serialise them.  The
+ * calling thread's current device must be the stream's device.  Other
+ * arguments, rules and errors as ngram_grad_gate. */
+int64_t ngram_grad_gate_noalloc_max_elements(void);
+int ngram_grad_gate_noalloc(const int32_t* rows, const uint16_t* dout, const float* eN, int64_t n, int32_t d,
+                            float* grad_Wg_out, ngram_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
