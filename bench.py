@@ -99,6 +99,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture one launch per batch in a HIP graph and time graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tpw", type=int, default=0,
+                    help="tokens per workgroup of the gather kernels (0: the library's choice)")
     ap.add_argument("--serial", action="store_true",
                     help="backward: the three gradient calls in order on one stream")
     ap.add_argument("--cpu-rows", type=int, default=1_000_000,
@@ -266,12 +268,15 @@ def main():
         gp = gate_params(spec)
         g_gamma, g_u, g_v = (torch.from_numpy(a).to(dev) for a in (gp.gamma, gp.u, gp.v))
 
+    shape = (args.tpw, 0) if args.tpw else None
+
     def launch(tok, off, hist, res, out, stream=None):
         if gated:
             ng.ngram_forward_gated(tok, off, T, W_g, g_gamma, g_u, g_v, gp.b, gp.eps, out, e1,
-                                   residual=res, history=hist, stream=stream)
+                                   residual=res, history=hist, launch=shape, stream=stream)
         else:
-            ng.ngram_forward(tok, off, T, W_g, out, e1=e1, residual=res, history=hist, stream=stream)
+            ng.ngram_forward(tok, off, T, W_g, out, e1=e1, residual=res, history=hist, launch=shape,
+                             stream=stream)
 
     def step(i):
         tok, off, hist, res, out = batches[i % nb]

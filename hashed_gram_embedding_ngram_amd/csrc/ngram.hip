@@ -513,11 +513,37 @@ struct GatedArgs {
     float eps;
 };
 
-// The sum of x over the wavefront's 64 lanes, in every lane.
+// x from another lane of the same 16-lane row, chosen by a DPP control word
+// (both 32-bit halves moved with the same pattern).
+template <int CTRL>
+__device__ inline double dpp_f64(double x) {
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, false));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ inline double readlane_f64(double x, int lane) {
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), lane));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), lane));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// The sum of x over the wavefront's 64 lanes, the same value in every lane.
+// Within each 16-lane row, lanes exchange by DPP: neighbours (xor 1), pairs
+// (xor 2), the two halves of 8 (half mirror), the two halves of 16 (mirror);
+// each step adds two values whose sum is the same whichever lane forms it,
+// so all 16 lanes of a row hold the same row sum.  The four row sums are then
+// added in row order.
 __device__ inline double wave_sum(double x) {
-#pragma unroll
-    for (int w = 1; w < 64; w <<= 1) x = x + __shfl_xor(x, w, 64);
-    return x;
+    x = x + dpp_f64<0xB1>(x);     // quad_perm [1,0,3,2]
+    x = x + dpp_f64<0x4E>(x);     // quad_perm [2,3,0,1]
+    x = x + dpp_f64<0x141>(x);    // row_half_mirror
+    x = x + dpp_f64<0x140>(x);    // row_mirror
+    return ((readlane_f64(x, 0) + readlane_f64(x, 16)) + readlane_f64(x, 32)) + readlane_f64(x, 48);
 }
 
 __device__ inline void load_f8(float w[8], const float* __restrict__ p, int64_t j0) {
@@ -544,8 +570,10 @@ __device__ inline uint32_t bf16_rne_f64(double x) {
 // One tile: wavefront w owns columns 512w .. 512w+511 (one block; the launch
 // has one wavefront per block).  Each token takes two workgroup barriers, one
 // per sum over its columns; a token's validity is uniform over the workgroup,
-// so every wavefront reaches the same barriers.
-template <int DT, bool RES, bool FULL>
+// so every wavefront reaches the same barriers.  ONE: the tile is one token,
+// so there is no token loop (a loop lets the compiler keep loop-invariant
+// float64 constants of exp in registers through the gather).
+template <int DT, bool RES, bool FULL, bool ONE>
 __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lrows, int32_t* ltok, double* lred) {
     const FwdArgs& a = g.f;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -556,7 +584,7 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
     hash_tile(a, tile0, lrows, ltok, lrows + a.tpw * (kK + 1));
 
     const int64_t rem = a.n - tile0;
-    const int tile_n = rem < a.tpw ? static_cast<int>(rem) : a.tpw;
+    const int tile_n = ONE ? 1 : (rem < a.tpw ? static_cast<int>(rem) : a.tpw);
     for (int tl = 0; tl < tile_n; ++tl) {
         const int64_t i = tile0 + tl;
         const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
@@ -654,7 +682,9 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
     }
 }
 
-template <int DT, bool RES, bool FULL, bool PERSIST>
+// MODE 0: one token per workgroup; 1: one tile of tpw tokens per workgroup;
+// 2: a capped grid loops over the tiles (tables in host memory).
+template <int DT, bool RES, bool FULL, int MODE>
 __global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
     extern __shared__ int32_t lds[];
     // [tpw][2][nwaves] float64 sums first (8-byte aligned), then the row
@@ -663,12 +693,14 @@ __global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
     double* lred = reinterpret_cast<double*>(lds);
     int32_t* lrows = lds + 2 * (g.f.tpw * 2 * nwaves);
     int32_t* ltok = lrows + g.f.tpw * kK;
-    if constexpr (!PERSIST) {
-        gated_tile<DT, RES, FULL>(g, static_cast<int64_t>(blockIdx.x) * g.f.tpw, lrows, ltok, lred);
+    if constexpr (MODE == 0) {
+        gated_tile<DT, RES, FULL, true>(g, static_cast<int64_t>(blockIdx.x), lrows, ltok, lred);
+    } else if constexpr (MODE == 1) {
+        gated_tile<DT, RES, FULL, false>(g, static_cast<int64_t>(blockIdx.x) * g.f.tpw, lrows, ltok, lred);
     } else {
         const int64_t ntiles = (g.f.n + g.f.tpw - 1) / g.f.tpw;
         for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-            gated_tile<DT, RES, FULL>(g, tile * g.f.tpw, lrows, ltok, lred);
+            gated_tile<DT, RES, FULL, false>(g, tile * g.f.tpw, lrows, ltok, lred);
             __syncthreads();              // the next tile rewrites the LDS lists
         }
     }
@@ -1672,6 +1704,12 @@ void launch_fwd_dt(const FwdArgs& a, const Shape& sh, hipStream_t st) {
 }
 
 // The gated kernel: one wavefront per 512-column block (d <= 8192).
+template <int DT, bool RES, int MODE>
+void launch_gated_mode(const GatedArgs& g, dim3 grid, dim3 block, size_t lds, bool full, hipStream_t st) {
+    if (full) hipLaunchKernelGGL((ngram_gated_kernel<DT, RES, true, MODE>), grid, block, lds, st, g);
+    else hipLaunchKernelGGL((ngram_gated_kernel<DT, RES, false, MODE>), grid, block, lds, st, g);
+}
+
 template <int DT>
 void launch_gated_dt(const GatedArgs& g, const Shape& sh, hipStream_t st) {
     const int nb = (g.f.d + kSlice - 1) / kSlice;
@@ -1680,14 +1718,14 @@ void launch_gated_dt(const GatedArgs& g, const Shape& sh, hipStream_t st) {
                        (g.f.stage ? kSeqLds * sizeof(int32_t) : 0);
     const bool res = g.f.res != nullptr, full = g.f.d % kSlice == 0;
     if (sh.persist) {
-        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, false, true>), grid, block, lds, st, g);
-        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, false, true>), grid, block, lds, st, g);
-    } else if (full) {
-        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, true, false>), grid, block, lds, st, g);
-        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, true, false>), grid, block, lds, st, g);
+        if (res) launch_gated_mode<DT, true, 2>(g, grid, block, lds, false, st);
+        else launch_gated_mode<DT, false, 2>(g, grid, block, lds, false, st);
+    } else if (sh.tpw == 1) {
+        if (res) launch_gated_mode<DT, true, 0>(g, grid, block, lds, full, st);
+        else launch_gated_mode<DT, false, 0>(g, grid, block, lds, full, st);
     } else {
-        if (res) hipLaunchKernelGGL((ngram_gated_kernel<DT, true, false, false>), grid, block, lds, st, g);
-        else hipLaunchKernelGGL((ngram_gated_kernel<DT, false, false, false>), grid, block, lds, st, g);
+        if (res) launch_gated_mode<DT, true, 1>(g, grid, block, lds, full, st);
+        else launch_gated_mode<DT, false, 1>(g, grid, block, lds, full, st);
     }
 }
 
@@ -1944,13 +1982,12 @@ int ngram_forward_gated_ex(const int32_t* tokens, int64_t n, const int32_t* seq_
     a.stage = stage_for(n, S);
     a.sd = make_seeds(seeds);
     g.gamma = gamma; g.u = u; g.v = v; g.stats = stats_out; g.b = b; g.eps = eps;
+    // One token per workgroup for every table type (the kernel then has no
+    // token loop, which keeps it at 69-78 VGPRs instead of 113-128).
     Shape sh = slice_shape(n, T->d, T->dtype, launch);
-    if (T->dtype == NGRAM_TABLE_BF16 && !(launch && launch->tokens_per_workgroup > 0)) {
-        // Two tokens per workgroup measured best for the gated bf16 path on
-        // MI355X at the prefill shape: 1 token 526 us, 2 tokens 514 us,
-        // 4 tokens 521 us per launch.
-        sh.tpw = 2;
-        sh.grid = (n + 1) / 2;
+    if (!(launch && launch->tokens_per_workgroup > 0)) {
+        sh.tpw = 1;
+        sh.grid = n;
     }
     cap_for_host(sh, T, launch);
     a.tpw = sh.tpw;

@@ -94,7 +94,7 @@ typedef struct {
  * bit-identical for every value: only the speed changes.
  *   tokens_per_workgroup: tokens a gather workgroup hashes into LDS and then
  *     gathers (0: the library's choice, 1 for bf16 tables, 4 for int8 and
- *     MXFP4 tables, 2 on the gated path over bf16 tables; at most 64);
+ *     MXFP4 tables, 1 on the gated path for every table type; at most 64);
  *   host_workgroups: the grid cap for a table in pinned host memory, whose
  *     workgroups then loop over the tiles (0: the library's choice, 8). */
 typedef struct {
