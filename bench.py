@@ -88,9 +88,20 @@ def parse():
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "int8", "fp4", "gated", "decode1", "decode2", "decode4", "host",
                              "backward"])
-    ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged", "pool"],
-                    help="host workload: sum straight from pinned memory, stage rows in HBM first, or go "
-                         "through an HBM row pool (hot-row cache + per-batch dedup)")
+    ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged", "async", "pool"],
+                    help="host workload: sum straight from pinned memory; stage the distinct rows in HBM first, "
+                         "read by GPU workgroups (staged) or copied by the DMA engines (async); or go through an "
+                         "HBM row pool (hot-row cache + per-batch dedup)")
+    ap.add_argument("--host-wgs", type=int, default=0,
+                    help="host workload, zero copy: workgroups of the capped grid that reads the host table "
+                         "(0: the library's choice)")
+    ap.add_argument("--cu-split", type=int, default=0,
+                    help="host workload: run the gather on a stream confined to the first N compute units and "
+                         "the GEMM stand-in on a stream confined to the others (0: no confinement)")
+    ap.add_argument("--interference", action="store_true",
+                    help="host workload: also time the GEMM stand-in beside other PCIe readers (the same gather "
+                         "kernel over consecutive rows, a DMA copy of the same bytes) to separate the causes of "
+                         "its slowdown")
     ap.add_argument("--cache-rows", type=int, default=1 << 20, help="pool mode: rows of the hot-row cache")
     ap.add_argument("--cache-history", type=int, default=8, help="pool mode: earlier batches counted")
     ap.add_argument("--dist", default="zipf", choices=["zipf", "uniform"],
@@ -401,6 +412,31 @@ def backward_bytes_per_token(d: int, rows_per_token_unique: float, tokens_unique
     return 16 * 2 * d + rows_per_token_unique * 4 * d + 2 * d + tokens_unique * 4 * d + 6 * d
 
 
+def cu_masked_streams(n_side: int):
+    """Two streams of default priority on disjoint compute units: the first
+    ``n_side`` CUs for the side stream, the rest for the main stream
+    (hipExtStreamCreateWithCUMask of the HIP runtime torch has loaded)."""
+    import ctypes
+
+    import torch
+
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    total = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (total + 31) // 32
+
+    def make(cus):
+        mask = (ctypes.c_uint32 * words)()
+        for c in cus:
+            mask[c // 32] |= 1 << (c % 32)
+        h = ctypes.c_void_p()
+        rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), mask)
+        if rc != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({rc})")
+        return torch.cuda.ExternalStream(h.value)
+
+    return make(range(n_side)), make(range(n_side, total)), total
+
+
 def run_backward(args):
     """Gradients of one prefill batch (8 x 4096 tokens, R = 20M, d = 2560):
     ngram_grad_table + ngram_grad_e1 + ngram_grad_gate, from the forward's
@@ -515,9 +551,13 @@ def run_host(args):
     rows = torch.empty((n, 16), dtype=torch.int32, device=dev)
     out = torch.empty(n * d, dtype=torch.int16, device=dev)
     stage = remap = pool = None
-    if args.host_mode == "staged":
+    if args.host_mode in ("staged", "async"):
         stage = torch.empty((n * 16, d), dtype=torch.int16, device=dev)
         remap = torch.empty((n, 16), dtype=torch.int32, device=dev)
+        n_staged = torch.zeros(1, dtype=torch.int64, device=dev)
+        gws = ng.gather_host_workspace(n, d, dev)
+        pinned = ng.gather_host_pinned(n) if args.host_mode == "async" else None
+        gmode = ng.GATHER_ASYNC_COPY if args.host_mode == "async" else ng.GATHER_ZERO_COPY
     cache_info = None
     if args.host_mode == "pool":
         # Row frequencies of earlier batches choose the cached rows.
@@ -540,20 +580,27 @@ def run_host(args):
     A = torch.randn((32768, d), dtype=torch.bfloat16, device=dev)
     B = torch.randn((d, d), dtype=torch.bfloat16, device=dev).contiguous()
     C = torch.empty((32768, d), dtype=torch.bfloat16, device=dev)
-    side = torch.cuda.Stream(device=dev)            # default priority
-    main = torch.cuda.current_stream()
+    cu_total = None
+    if args.cu_split > 0:
+        side, main, cu_total = cu_masked_streams(args.cu_split)
+        torch.cuda.set_stream(main)
+    else:
+        side = torch.cuda.Stream(device=dev)        # default priority
+        main = torch.cuda.current_stream()
     setup_s = time.time() - t0
 
     def gather(stream):
         ng.ngram_hash(di.tokens, di.offsets, R, rows_out=rows, stream=stream)
-        if args.host_mode == "staged":
-            ng.ngram_gather_host(T_host, rows, stage, remap, stream=stream)
+        if args.host_mode in ("staged", "async"):
+            ng.ngram_gather_host(T_host, rows, stage, remap, n_staged_out=n_staged, mode=gmode, workspace=gws,
+                                 pinned=pinned, stream=stream)
             ng.ngram_embed_bag(ng.Table(stage, n * 16, d), remap, eN_out=eN, stream=stream)
         elif args.host_mode == "pool":
             ng.ngram_pool_gather(pool, rows, pool_rows_out=prow, fetched_out=fetched, workspace=pws, stream=stream)
             ng.ngram_embed_bag(pool_T, prow, eN_out=eN, stream=stream)
         else:
-            ng.ngram_embed_bag(T_host, rows, eN_out=eN, stream=stream)
+            ng.ngram_embed_bag(T_host, rows, eN_out=eN, stream=stream,
+                               launch=(0, args.host_wgs) if args.host_wgs else None)
 
     def gemms(k):
         for _ in range(k):
@@ -591,20 +638,75 @@ def run_host(args):
     gemm_s = timed(lambda: gemms(k), 3)
 
     def overlapped():
+        # the GEMMs are enqueued first: the async-copy mode waits on the host
+        # for the side stream's dedup before it enqueues its copies
         side.wait_stream(main)
+        gemms(k)
         gather(side)
         ev_done = torch.cuda.Event()
         ev_done.record(side)
-        gemms(k)
         main.wait_event(ev_done)
         ng.ngram_gate_add(eN, di.tokens, di.W_g, out, e1=di.e1, residual=di.residual, stream=main)
     both_s = timed(overlapped, 3)
     gate_s = timed(lambda: ng.ngram_gate_add(eN, di.tokens, di.W_g, out, e1=di.e1,
                                              residual=di.residual, stream=main), 5)
 
-    # The bytes that cross PCIe: all 16 rows per token (zero copy, staged),
-    # or only the distinct uncached rows (pool).
+    interference = None
+    if args.interference:
+        # The GEMM stand-in's time per call beside each reader of pinned host
+        # memory running on the side stream for the whole GEMM loop: the
+        # random-row gather (the path), the same kernel over consecutive rows
+        # (the same bytes and grid, sequential addresses), and a DMA copy of
+        # the same bytes (no compute units, PCIe traffic only).
+        seq_rows = torch.arange(n * 16, dtype=torch.int32, device=dev).reshape(n, 16)
+        eN2 = torch.empty_like(eN)
+        pinned_src = torch.empty(n * 16 * d * 2, dtype=torch.uint8, pin_memory=True)
+        dma_dst = torch.empty(n * 16 * d * 2, dtype=torch.uint8, device=dev)
+        readers = {
+            "random_row_gather": lambda st: ng.ngram_embed_bag(T_host, rows, eN_out=eN, stream=st),
+            "consecutive_row_gather": lambda st: ng.ngram_embed_bag(T_host, seq_rows, eN_out=eN2, stream=st),
+            "dma_copy": lambda st: dma_dst.copy_(pinned_src, non_blocking=True),
+        }
+        ng.ngram_hash(di.tokens, di.offsets, R, rows_out=rows, stream=side)
+        interference = {"gemm_alone_ms_per_call": gemm1 * 1e3, "bytes_per_reader_call": n * 16 * d * 2}
+        for name, fn in readers.items():
+            with torch.cuda.stream(side):
+                fn(side)                                            # warm-up
+            torch.cuda.synchronize()
+            ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev0[0].record(side)
+            with torch.cuda.stream(side):
+                fn(side)
+            ev0[1].record(side)
+            torch.cuda.synchronize()
+            reader_s = ev0[0].elapsed_time(ev0[1]) / 1e3
+            reps = max(1, int(np.ceil(1.5 * k * gemm1 / reader_s)))
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                for _ in range(reps):
+                    fn(side)
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(main)
+            gemms(k)
+            g1.record(main)
+            torch.cuda.synchronize()
+            interference[name] = {"reader_alone_ms": reader_s * 1e3,
+                                  "reader_GBps": n * 16 * d * 2 / reader_s / 1e9,
+                                  "gemm_beside_ms_per_call": g0.elapsed_time(g1) / k}
+        del pinned_src, dma_dst
+
+    # The bytes that cross PCIe: all 16 rows per token (zero copy), the
+    # distinct rows (staged, async), or the distinct uncached rows (pool).
     pcie_bytes = nominal_pcie = n * 16 * d * 2
+    staged_info = None
+    if stage is not None:
+        torch.cuda.synchronize()
+        U = int(n_staged.item())
+        pcie_bytes = U * d * 2
+        staged_info = {"distinct_rows": U, "pcie_bytes_per_batch": pcie_bytes,
+                       "nominal_GBps": nominal_pcie / gather_s / 1e9,
+                       "engine": "DMA (one copy per distinct row)" if args.host_mode == "async"
+                       else "GPU workgroups (zero copy, capped grid)"}
     if cache_info is not None:
         torch.cuda.synchronize()
         cache_info["rows_fetched_per_batch"] = int(fetched.item())
@@ -627,10 +729,13 @@ def run_host(args):
         "data": "synthetic",
         "config": {"workload": "host", "tokens": n, "R": R, "d": d, "K": K_ROWS, "table_dtype": "bf16",
                    "table_location": "pinned host memory", "mode": args.host_mode,
+                   "cu_split": None if not args.cu_split else f"gather {args.cu_split} CUs, GEMM {cu_total - args.cu_split}",
+                   "host_workgroups": args.host_wgs or 8,
                    "token_dist": f"zipf({spec.zipf_s})" if args.dist == "zipf" else "uniform"},
         "roofline": {"bound": "pcie", "achieved": achieved, "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PCIE_PEAK_GBPS, "traffic": None,
-                     "kernel": "ngram_bag_kernel (host table)",
+                     "kernel": {"zero_copy": "ngram_bag_kernel (host table)", "staged": "pool_fetch_kernel (staging)",
+                                "async": "host-to-device copies", "pool": "pool_fetch_kernel"}[args.host_mode],
                      "algorithmic_bytes_per_launch": pcie_bytes,
                      "h2d_copy_GBps": (1 << 30) / h2d_s / 1e9},
         "overlap": {"gemm_stand_in": "[32768 x 2560] @ [2560 x 2560] bf16", "gemm_count": k,
@@ -639,6 +744,8 @@ def run_host(args):
                     "gate_add_ms": gate_s * 1e3,
                     "dma_estimate_ms": dma_time_estimate_us(K_ROWS, d, 2, PCIE_PEAK_GBPS) * n / 1e3},
         "row_pool": cache_info,
+        "staged": staged_info,
+        "interference": interference,
         "setup_s": setup_s,
         "cpu_baseline": None,
     }

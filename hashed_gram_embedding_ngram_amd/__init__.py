@@ -68,7 +68,10 @@ _SIGNATURES = {
                                               ctypes.POINTER(_Launch), _P]),
     "ngram_host_alloc": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
     "ngram_host_free": (ctypes.c_int, [_P]),
-    "ngram_gather_host": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, _P, _P, _P]),
+    "ngram_gather_host_workspace_bytes": (ctypes.c_int64, [_I64, _I32]),
+    "ngram_gather_host_pinned_bytes": (ctypes.c_int64, [_I64]),
+    "ngram_gather_host": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                                         _I32, _P]),
     "ngram_pool_workspace_bytes": (ctypes.c_int64, [_I64]),
     "ngram_pool_reset": (ctypes.c_int, [ctypes.POINTER(_Table), ctypes.POINTER(_Pool), _P]),
     "ngram_pool_cache_rows": (ctypes.c_int, [ctypes.POINTER(_Table), ctypes.POINTER(_Pool), _P, _I64, _P]),
@@ -354,7 +357,24 @@ def ngram_forward_gated(tokens, seq_offsets, table: Table, W_g, gamma, u, v, b, 
     return out
 
 
-def ngram_gather_host(table: Table, rows, stage_out, remap_out, stage_scale_out=None, stream=None):
+GATHER_ZERO_COPY = 0
+GATHER_ASYNC_COPY = 1
+
+
+def gather_host_workspace(n: int, d: int, device="cuda:0"):
+    nbytes = int(lib().ngram_gather_host_workspace_bytes(int(n), int(d)))
+    return torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def gather_host_pinned(n: int) -> "HostBuffer":
+    """Pinned host memory for ngram_gather_host's async-copy mode."""
+    return HostBuffer(max(16, int(lib().ngram_gather_host_pinned_bytes(int(n)))))
+
+
+def ngram_gather_host(table: Table, rows, stage_out, remap_out, stage_scale_out=None, n_staged_out=None,
+                      mode=GATHER_ZERO_COPY, workspace=None, pinned=None, stream=None):
+    """Stage the batch's distinct rows of a pinned-host table in device
+    memory.  Returns (stage_out, remap_out, n_staged_out [1] int64)."""
     _dev(rows, _I32T, "rows")
     _dev(remap_out, _I32T, "remap_out")
     _dev(stage_scale_out, _F32, "stage_scale_out", allow_none=True)
@@ -368,9 +388,25 @@ def ngram_gather_host(table: Table, rows, stage_out, remap_out, stage_scale_out=
         raise NgramError("stage_out is smaller than n * 16 rows")
     if table.dtype == TABLE_INT8_ROWSCALE:
         _need(stage_scale_out, n * K, "stage_scale_out")
-    _check(lib().ngram_gather_host(table.c, _ptr(rows), n, _ptr(stage_out), _ptr(stage_scale_out),
-                                   _ptr(remap_out), _stream(stream)), "ngram_gather_host")
-    return stage_out, remap_out
+    if n_staged_out is None:
+        n_staged_out = torch.empty(1, dtype=torch.int64, device=rows.device)
+    _dev(n_staged_out, (torch.int64,), "n_staged_out")
+    if workspace is None:
+        workspace = gather_host_workspace(n, table.d, rows.device)
+    own_pinned = None
+    if mode == GATHER_ASYNC_COPY and pinned is None:
+        own_pinned = pinned = gather_host_pinned(n)
+    p_ptr = None if pinned is None else ctypes.c_void_p(pinned.ptr)
+    p_bytes = 0 if pinned is None else pinned.nbytes
+    _check(lib().ngram_gather_host(table.c, _ptr(rows), n, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   p_ptr, p_bytes, _ptr(stage_out), _ptr(stage_scale_out), _ptr(remap_out),
+                                   _ptr(n_staged_out), int(mode), _stream(stream)), "ngram_gather_host")
+    if own_pinned is not None:
+        # the copies read only the table, but the row list they were built
+        # from sits in this buffer: let the stream pass them before freeing it
+        (stream or torch.cuda.current_stream()).synchronize()
+        own_pinned.free()
+    return stage_out, remap_out, n_staged_out
 
 
 class RowPool:

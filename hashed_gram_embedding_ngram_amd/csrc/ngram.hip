@@ -963,7 +963,7 @@ __global__ void __launch_bounds__(256) pool_insert_kernel(const PoolArgs a) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (t >= a.nrows) return;
     const int32_t r = a.rows[t];
-    if (r < 0 || r >= a.R || a.slot_of_row[r] >= 0) return;
+    if (r < 0 || r >= a.R || (a.slot_of_row && a.slot_of_row[r] >= 0)) return;
     uint32_t h = set_home(r, a.shift);
     for (uint32_t probe = 0; probe <= a.mask; ++probe) {
         const int32_t prev = atomicCAS(&a.keys[h], -1, r);
@@ -984,7 +984,7 @@ __global__ void __launch_bounds__(256) pool_resolve_kernel(const PoolArgs a) {
     const int32_t r = a.rows[t];
     int32_t out = -1;
     if (r >= 0 && r < a.R) {
-        const int32_t s = a.slot_of_row[r];
+        const int32_t s = a.slot_of_row ? a.slot_of_row[r] : -1;
         if (s >= 0) {
             out = s;
         } else {
@@ -1020,6 +1020,15 @@ __global__ void __launch_bounds__(1024) pool_fetch_kernel(const PoolArgs a) {
         copy_row<U>(reinterpret_cast<const U*>(static_cast<const char*>(a.tab) + static_cast<int64_t>(r) * a.row_bytes),
                     reinterpret_cast<U*>(static_cast<char*>(a.pool) + dst_row * a.row_bytes), nu, lane);
     }
+}
+
+// The distinct-row count and, for int8 tables, the staged rows' scales, when
+// the rows themselves are copied by the DMA engines (ngram_gather_host mode 1).
+__global__ void __launch_bounds__(256) stage_meta_kernel(const PoolArgs a) {
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t nmiss = static_cast<int64_t>(*a.counter);
+    if (u == 0 && a.fetched_out) *a.fetched_out = nmiss;
+    if (u < nmiss && a.pool_scale) a.pool_scale[u] = a.scale[a.miss[u]];
 }
 
 // Cache hot rows: wavefront per pool slot s, claiming slot_of_row[hot[s]].
@@ -2023,35 +2032,98 @@ int ngram_host_free(void* host_ptr) {
     return NGRAM_OK;
 }
 
-int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
-                      void* stage_out, float* stage_scale_out, int32_t* remap_out,
+int64_t ngram_gather_host_workspace_bytes(int64_t n, int32_t d) {
+    if (n < 0 || d <= 0) return -1;
+    return pool_layout(n).total;
+}
+
+int64_t ngram_gather_host_pinned_bytes(int64_t n) {
+    if (n < 0) return -1;
+    return 16 + 4 * kK * n;
+}
+
+int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n, void* workspace,
+                      int64_t workspace_bytes, void* pinned, int64_t pinned_bytes, void* stage_out,
+                      float* stage_scale_out, int32_t* remap_out, int64_t* n_staged_out, int32_t mode,
                       ngram_stream_t stream) {
     g_err[0] = 0;
     int rc = check_table(T_host);
     if (rc) return rc;
     if (T_host->location != NGRAM_IN_HOST) return fail(NGRAM_ENOTSUP, "ngram_gather_host needs a host table");
+    if (mode != 0 && mode != 1) return fail(NGRAM_EINVAL, "mode=%d must be 0 (zero copy) or 1 (async copy)", mode);
     if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
-    if (n > INT32_MAX / kK) return fail(NGRAM_ERANGE, "n=%lld above (2^31-1)/16", (long long)n);
-    if (n > 0 && (!rows || !stage_out || !remap_out)) return fail(NGRAM_EINVAL, "rows, stage_out or remap_out is NULL");
+    if (n > (1 << 26)) return fail(NGRAM_ERANGE, "n=%lld above 2^26", (long long)n);
+    if (n > 0 && (!rows || !stage_out || !remap_out || !n_staged_out))
+        return fail(NGRAM_EINVAL, "rows, stage_out, remap_out or n_staged_out is NULL");
     if (n > 0 && T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE && !stage_scale_out)
         return fail(NGRAM_EINVAL, "int8 table needs stage_scale_out");
     if (n > 0 && !aligned(stage_out, 16)) return fail(NGRAM_EALIGN, "stage_out not 16-byte aligned");
+    const PoolLayout L = pool_layout(n);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < L.total)
+        return fail(NGRAM_EINVAL, "workspace needs %lld bytes, 16-byte aligned", (long long)L.total);
+    const int64_t nrows = kK * n;
+    const int64_t pinned_need = ngram_gather_host_pinned_bytes(n);
+    if (mode == 1 && (!pinned || !aligned(pinned, 16) || pinned_bytes < pinned_need))
+        return fail(NGRAM_EINVAL, "mode 1 needs %lld bytes of pinned host memory, 16-byte aligned",
+                    (long long)pinned_need);
     if (n == 0) return NGRAM_OK;
     const void* tab = nullptr;
     rc = table_device_ptr(T_host, &tab);
     if (rc) return rc;
-    StageArgs a;
-    a.tab = tab; a.scale = T_host->row_scale; a.rows = rows; a.stage = stage_out;
-    a.stage_scale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? stage_scale_out : nullptr;
-    a.remap = remap_out; a.nrows = n * kK; a.R = T_host->R;
-    a.row_bytes = table_row_bytes(T_host);
-    int64_t blocks = (a.nrows + 15) / 16;
-    if (blocks > kHostWorkgroups) blocks = kHostWorkgroups;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(1024);
-    if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x4>, grid, block, 0, stream, a);
-    else if (a.row_bytes % 8 == 0) hipLaunchKernelGGL(ngram_stage_kernel<u32x2>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(ngram_stage_kernel<uint32_t>, grid, block, 0, stream, a);
-    return hip_status("ngram_gather_host launch");
+    char* ws = static_cast<char*>(workspace);
+    PoolArgs a;
+    a.tab = tab; a.scale = T_host->row_scale; a.rows = rows; a.pool = stage_out;
+    a.pool_scale = T_host->dtype == NGRAM_TABLE_INT8_ROWSCALE ? stage_scale_out : nullptr;
+    a.slot_of_row = nullptr; a.pool_rows_out = remap_out;
+    a.keys = reinterpret_cast<int32_t*>(ws + L.keys);
+    a.vals = reinterpret_cast<int32_t*>(ws + L.vals);
+    a.miss = reinterpret_cast<int32_t*>(ws + L.miss);
+    a.counter = reinterpret_cast<uint32_t*>(ws + L.counter);
+    a.fetched_out = n_staged_out;
+    a.nrows = nrows; a.R = T_host->R; a.cached = 0; a.row_bytes = table_row_bytes(T_host);
+    a.mask = static_cast<uint32_t>(L.H - 1);
+    a.shift = 32u - static_cast<uint32_t>(L.log2H);
+    // distinct rows: keys := -1, counter := 0, insert, then resolve to staging indices
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(L.H)), dim3(256), 0, stream, a.keys, L.H, -1);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, stream, reinterpret_cast<int32_t*>(a.counter), 4, 0);
+    const dim3 g(static_cast<unsigned>((nrows + 255) / 256)), b(256);
+    hipLaunchKernelGGL(pool_insert_kernel, g, b, 0, stream, a);
+    hipLaunchKernelGGL(pool_resolve_kernel, g, b, 0, stream, a);
+    if (mode == 0) {
+        int64_t blocks = (nrows + 15) / 16;
+        if (blocks > kHostWorkgroups) blocks = kHostWorkgroups;
+        if (a.row_bytes % 16 == 0) hipLaunchKernelGGL(pool_fetch_kernel<u32x4>, dim3(blocks), dim3(1024), 0, stream, a);
+        else if (a.row_bytes % 8 == 0) hipLaunchKernelGGL(pool_fetch_kernel<u32x2>, dim3(blocks), dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL(pool_fetch_kernel<uint32_t>, dim3(blocks), dim3(1024), 0, stream, a);
+        return hip_status("ngram_gather_host launch");
+    }
+    // mode 1: read the distinct-row list back, then enqueue one host-to-device
+    // copy per row on the stream (the DMA engines; no compute units)
+    hipLaunchKernelGGL(stage_meta_kernel, g, b, 0, stream, a);
+    rc = hip_status("ngram_gather_host launch");
+    if (rc) return rc;
+    char* hp = static_cast<char*>(pinned);
+    uint32_t* h_count = reinterpret_cast<uint32_t*>(hp);
+    int32_t* h_miss = reinterpret_cast<int32_t*>(hp + 16);
+    hipError_t e = hipMemcpyAsync(h_count, a.counter, 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_miss, a.miss, 4 * nrows, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NGRAM_EHIP, "reading the distinct-row list: %s", hipGetErrorString(e));
+    }
+    const int64_t U = *h_count;
+    const char* host_tab = static_cast<const char*>(T_host->data);
+    char* stage = static_cast<char*>(stage_out);
+    for (int64_t u = 0; u < U; ++u) {
+        e = hipMemcpyAsync(stage + u * a.row_bytes, host_tab + static_cast<int64_t>(h_miss[u]) * a.row_bytes,
+                           static_cast<size_t>(a.row_bytes), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NGRAM_EHIP, "copy of row %lld of %lld: %s", (long long)u, (long long)U, hipGetErrorString(e));
+        }
+    }
+    return NGRAM_OK;
 }
 
 int64_t ngram_pool_workspace_bytes(int64_t n) {

@@ -197,18 +197,42 @@ int ngram_forward_gated_ex(const int32_t* tokens, int64_t n, const int32_t* seq_
 int ngram_host_alloc(int64_t bytes, void** host_ptr);
 int ngram_host_free(void* host_ptr);
 
-/* Copy the 16 selected rows of each token from a table in pinned host memory
- * into a device staging table: stage_out row i*16+k = T_host row rows[i][k]
- * (raw element bytes, d elements of the table's dtype; stage_out [n*16][d],
- * 16-byte aligned), stage_scale_out[i*16+k] = its row scale (int8 tables
- * only, else may be NULL), remap_out[i][k] = i*16+k, or -1 where rows[i][k]
- * is outside [0, R) (that stage row is left unwritten).  ngram_embed_bag on
- * the staging table (R' = n*16, in device memory) with remap_out then gives
- * exactly what ngram_embed_bag gives on T_host with rows.  Run it on a side
- * stream and join with an event.  Errors: EINVAL, EALIGN, ERANGE, and
- * ENOTSUP when T_host is not in host memory. */
-int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n,
-                      void* stage_out, float* stage_scale_out, int32_t* remap_out,
+/* Stage the distinct rows a batch selects from a table in pinned host memory
+ * in device memory: "Qwen Brought Back N-Grams…", section "Which is why the
+ * offload matters more than the parameter count" (the selected rows of the
+ * pinned-host shard gathered into a small BF16 GPU buffer on a dedicated
+ * stream), and "Qwen3.8-Flash-Next: A 51B N-gram Embedding Table with
+ * Heterogeneous Memory Prefetch", Key point 3 (a DMA pipeline over PCIe 5.0
+ * that moves the rows while the GPU computes; T_DMA = K d S / BW).
+ *   rows[n][16] int32 (device): the batch's row ids.
+ *   stage_out [16 n][row] (device, 16-byte aligned, room for 16 n rows):
+ *     stage row u = T_host row U_u, for the distinct valid row ids U_0,
+ *     U_1, … (each once, in an unspecified order); stage_scale_out[u] (int8
+ *     tables, device) its row scale, else may be NULL.
+ *   remap_out[n][16] int32 (device): the stage row of rows[i][k], or -1 where
+ *     rows[i][k] is outside [0, R).
+ *   *n_staged_out (device int64): the number of distinct rows staged.
+ * ngram_embed_bag on the stage (as a device table of 16 n rows) with
+ * remap_out then gives exactly what ngram_embed_bag gives on T_host with rows.
+ *   mode 0 (zero copy): a capped grid of GPU workgroups reads each distinct
+ *     row over PCIe through the device mapping and writes it to the stage.
+ *     Only enqueues work on `stream`.
+ *   mode 1 (async copy): the GPU finds the distinct rows, the call reads
+ *     their list back into `pinned` (it waits for `stream` up to that point),
+ *     then enqueues one host-to-device copy per distinct row on `stream` (the
+ *     DMA engines move the bytes, no compute unit is used) and returns.  Not
+ *     capturable in a HIP graph.
+ * workspace: device memory of ngram_gather_host_workspace_bytes(n, d) bytes,
+ * 16-byte aligned; pinned (mode 1 only, else may be NULL): pinned host memory
+ * (ngram_host_alloc) of ngram_gather_host_pinned_bytes(n) bytes, 16-byte
+ * aligned.  Calls that can overlap need a workspace and a pinned buffer each.
+ * Run it on a side stream and join with an event.  Errors: EINVAL, EALIGN,
+ * ERANGE (n > 2^26), ENOTSUP when T_host is not in host memory, EHIP. */
+int64_t ngram_gather_host_workspace_bytes(int64_t n, int32_t d);
+int64_t ngram_gather_host_pinned_bytes(int64_t n);
+int ngram_gather_host(const ngram_table* T_host, const int32_t* rows, int64_t n, void* workspace,
+                      int64_t workspace_bytes, void* pinned, int64_t pinned_bytes, void* stage_out,
+                      float* stage_scale_out, int32_t* remap_out, int64_t* n_staged_out, int32_t mode,
                       ngram_stream_t stream);
 
 /* Row pool in front of a pinned-host table: a hot-row cache in HBM plus a

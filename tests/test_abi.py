@@ -124,14 +124,25 @@ def test_forward_checks():
 def test_gather_host_and_host_alloc_checks():
     L = ng.lib()
     dev_t = ctypes.byref(_table())
-    assert L.ngram_gather_host(dev_t, A, 4, A, None, A, None) == ENOTSUP
+    ws = L.ngram_gather_host_workspace_bytes(4, 64)
+    pb = L.ngram_gather_host_pinned_bytes(4)
+    assert ws > 0 and pb == 16 + 4 * 64
+    assert L.ngram_gather_host_workspace_bytes(-1, 64) == -1 and L.ngram_gather_host_pinned_bytes(-1) == -1
+    G = L.ngram_gather_host
+    assert G(dev_t, A, 4, A, ws, None, 0, A, None, A, A, 0, None) == ENOTSUP
     host_t = ctypes.byref(_table(loc=1))
-    assert L.ngram_gather_host(host_t, None, 4, A, None, A, None) == EINVAL
-    assert L.ngram_gather_host(host_t, A, 4, A + 8, None, A, None) == EALIGN
-    assert L.ngram_gather_host(host_t, A, 2**28, A, None, A, None) == ERANGE
+    assert G(host_t, A, 4, A, ws, None, 0, A, None, A, A, 2, None) == EINVAL       # unknown mode
+    assert G(host_t, None, 4, A, ws, None, 0, A, None, A, A, 0, None) == EINVAL
+    assert G(host_t, A, 4, A, ws, None, 0, A, None, A, None, 0, None) == EINVAL    # n_staged_out
+    assert G(host_t, A, 4, A, ws, None, 0, A + 8, None, A, A, 0, None) == EALIGN
+    assert G(host_t, A, 2**28, A, ws, None, 0, A, None, A, A, 0, None) == ERANGE
+    assert G(host_t, A, 4, None, ws, None, 0, A, None, A, A, 0, None) == EINVAL    # no workspace
+    assert G(host_t, A, 4, A, ws - 1, None, 0, A, None, A, A, 0, None) == EINVAL   # workspace too small
+    assert G(host_t, A, 4, A, ws, None, 0, A, None, A, A, 1, None) == EINVAL       # mode 1 without pinned
+    assert G(host_t, A, 4, A, ws, A, pb - 1, A, None, A, A, 1, None) == EINVAL     # pinned too small
     h8 = ctypes.byref(_table(loc=1, dtype=1, scale=A))
-    assert L.ngram_gather_host(h8, A, 4, A, None, A, None) == EINVAL
-    assert L.ngram_gather_host(host_t, None, 0, None, None, None, None) == OK
+    assert G(h8, A, 4, A, ws, None, 0, A, None, A, A, 0, None) == EINVAL           # int8 without scales
+    assert G(host_t, None, 0, A, ws, None, 0, None, None, None, None, 0, None) == OK
     p = ctypes.c_void_p()
     assert L.ngram_host_alloc(0, ctypes.byref(p)) == EINVAL
     assert L.ngram_host_alloc(16, None) == EINVAL

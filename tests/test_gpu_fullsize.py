@@ -91,16 +91,22 @@ def test_host_table_full_size():
         assert np.array_equal(eN_host[tidx].cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
         assert_bf16_equal(bits16(out.view(sp.n, sp.d)[tidx]), want, "host")
 
-        say("host: staged gather")
-        stage = torch.empty((sp.n * 16, sp.d), dtype=torch.int16, device="cuda:0")
-        remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
-        ng.ngram_gather_host(th, rows, stage, remap)
-        eN_stage = ng.ngram_embed_bag(ng.Table(stage, sp.n * 16, sp.d), remap)
-        torch.cuda.synchronize()
-        assert np.array_equal(remap.cpu().numpy(), np.arange(sp.n * 16, dtype=np.int32).reshape(sp.n, 16))
-        assert torch.equal(eN_stage.view(torch.int32), eN_host.view(torch.int32))
-        del stage, remap, eN_stage
-        _free()
+        for mode in (ng.GATHER_ZERO_COPY, ng.GATHER_ASYNC_COPY):
+            say(f"host: staged gather, mode {mode}")
+            stage = torch.empty((sp.n * 16, sp.d), dtype=torch.int16, device="cuda:0")
+            remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
+            _, _, nst = ng.ngram_gather_host(th, rows, stage, remap, mode=mode)
+            eN_stage = ng.ngram_embed_bag(ng.Table(stage, sp.n * 16, sp.d), remap)
+            torch.cuda.synchronize()
+            U = int(nst.item())
+            assert U == np.unique(want_rows).size
+            rm = remap.cpu().numpy()
+            host = hb.numpy(np.int16, (sp.R, sp.d))
+            pick = np.random.default_rng(mode).integers(0, sp.n * 16, 2000)
+            assert np.array_equal(stage.cpu().numpy()[rm.reshape(-1)[pick]], host[want_rows.reshape(-1)[pick]])
+            assert torch.equal(eN_stage.view(torch.int32), eN_host.view(torch.int32))
+            del stage, remap, eN_stage
+            _free()
 
         say("host: same table in HBM")
         dev_table = torch.from_numpy(hb.numpy(np.int16, (sp.R * sp.d,))).to("cuda:0")

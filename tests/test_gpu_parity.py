@@ -41,6 +41,35 @@ def assert_bf16_equal(got, want, what):
     assert rel.size == 0 or rel.max() <= REL_TOL
 
 
+def check_staged(T, hb, rows, want_rows, want_eN, mode, scale=None):
+    """ngram_gather_host in ``mode`` on the host table T (pinned buffer hb):
+    each distinct valid row staged once, byte for byte, the remap pointing at
+    it, and the sums from the stage equal to the oracle's ``want_eN``."""
+    say(f"staged gather mode {mode}: R={T.R} d={T.d} dtype={T.dtype}")
+    n = rows.shape[0]
+    rb = ng.row_bytes(T.d, T.dtype)
+    stage = torch.empty(n * 16 * rb, dtype=torch.uint8, device="cuda:0")
+    remap = torch.empty((n, 16), dtype=torch.int32, device="cuda:0")
+    sscale = torch.empty(n * 16, dtype=torch.float32, device="cuda:0") if T.dtype == ng.TABLE_INT8_ROWSCALE else None
+    _, _, nst = ng.ngram_gather_host(T, rows, stage, remap, stage_scale_out=sscale, mode=mode)
+    view = {ng.TABLE_BF16: stage.view(torch.int16), ng.TABLE_INT8_ROWSCALE: stage.view(torch.int8)}.get(T.dtype, stage)
+    eN2 = ng.ngram_embed_bag(ng.Table(view, n * 16, T.d, T.dtype, row_scale=sscale), remap)
+    torch.cuda.synchronize()
+    U = int(nst.item())
+    valid = want_rows[(want_rows >= 0) & (want_rows < T.R)]
+    assert U == np.unique(valid).size
+    rm = remap.cpu().numpy()
+    assert np.array_equal(rm < 0, (want_rows < 0) | (want_rows >= T.R))
+    assert rm.max() == U - 1 and np.unique(rm[rm >= 0]).size == U          # stage rows 0..U-1, each used
+    host = hb.numpy(np.uint8, (T.R, rb))
+    st = stage.cpu().numpy().reshape(n * 16, rb)
+    ok = rm >= 0
+    assert np.array_equal(st[rm[ok]], host[want_rows[ok]])                   # staged rows are the table's bytes
+    if sscale is not None:
+        assert np.array_equal(sscale.cpu().numpy()[rm[ok]], scale.cpu().numpy()[want_rows[ok]])
+    assert np.array_equal(eN2.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+
+
 def run_forward(di: DeviceInputs, out_of_place=False, seeds=None, launch=None):
     sp = di.spec
     if di.residual is not None and not out_of_place:
@@ -291,17 +320,12 @@ def test_host_table_paths(wgs, tpw, table):
         ng.ngram_forward(di.tokens, di.offsets, T, di.W_g, out, e1=di.e1, residual=di.residual, rows_out=rows,
                          launch=(tpw, wgs))
         eN = ng.ngram_embed_bag(T, rows, launch=(tpw, wgs))
-        stage = torch.empty(sp.n * 16 * sp.d * esize, dtype=torch.int8, device="cuda:0")
-        remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
-        sscale = torch.empty(sp.n * 16, dtype=torch.float32, device="cuda:0") if table == "int8" else None
-        ng.ngram_gather_host(T, rows, stage, remap, stage_scale_out=sscale)
-        st = stage.view(torch.int16) if table == "bf16" else stage
-        eN2 = ng.ngram_embed_bag(ng.Table(st, sp.n * 16, sp.d, T.dtype, row_scale=sscale), remap)
         torch.cuda.synchronize()
         assert np.array_equal(rows.cpu().numpy(), want_rows)
         assert_bf16_equal(bits16(out).reshape(sp.n, -1), want_out, sp.name)
         assert np.array_equal(eN.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
-        assert np.array_equal(eN2.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+        for mode in (ng.GATHER_ZERO_COPY, ng.GATHER_ASYNC_COPY):
+            check_staged(T, hb, rows, want_rows, want_eN, mode, scale=scale)
     finally:
         hb.free()
 
@@ -431,10 +455,10 @@ def test_mxfp4_host_table_paths(d):
         di = DeviceInputs(sp, h, table=False)
         rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
         eN = ng.ngram_embed_bag(T, rows, launch=(0, 3))
-        stage = torch.empty(sp.n * 16 * rb, dtype=torch.uint8, device="cuda:0")
-        remap = torch.empty((sp.n, 16), dtype=torch.int32, device="cuda:0")
-        ng.ngram_gather_host(T, rows, stage, remap)
-        eN2 = ng.ngram_embed_bag(ng.Table(stage, sp.n * 16, d, ng.TABLE_MXFP4), remap)
+        torch.cuda.synchronize()
+        want_rows, want, want_out = expected(h)
+        for mode in (ng.GATHER_ZERO_COPY, ng.GATHER_ASYNC_COPY):
+            check_staged(T, hb, rows, want_rows, want, mode)
         pool = ng.RowPool(T, 50 + 16 * sp.n)
         counts = ng.ngram_count_rows(rows, sp.R)
         hot, sel = ng.ngram_select_hot_rows(counts, 50)
@@ -444,8 +468,7 @@ def test_mxfp4_host_table_paths(d):
         out = torch.empty(sp.n * d, dtype=torch.int16, device="cuda:0")
         ng.ngram_forward(di.tokens, di.offsets, T, di.W_g, out, e1=di.e1)     # fused, persistent grid
         torch.cuda.synchronize()
-        want_rows, want, want_out = expected(h)
-        for e in (eN, eN2, eN3):
+        for e in (eN, eN3):
             assert np.array_equal(e.cpu().numpy().view(np.uint32), want.view(np.uint32))
         assert_bf16_equal(bits16(out).reshape(sp.n, d), want_out, sp.name)
     finally:
