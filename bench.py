@@ -121,62 +121,80 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, max_seconds=20.0,
-                 mxfp4_d=None, gate=None):
+def cpu_baseline(host_inputs, table_np, scale_np, e1_np, res_np, R_cpu, prep_s, table_note, mxfp4_d=None,
+                 gate=None, repeats=5, chunk=512):
     """The oracle timed on the host cores on a bounded sample of the
-    workload: the whole batch, sequence by sequence, hashed into a host copy
-    of the first ``R_cpu`` table rows (the full table does not fit in host
-    memory; a random-row gather far beyond the last-level cache is
-    DRAM-bound either way), one oracle_forward call per sequence on a pool of
-    threads; repeated until about ``max_seconds`` / 4 of wall time."""
+    workload: the whole batch, hashed into a host copy of the first ``R_cpu``
+    table rows when the full table does not fit in host memory (a random-row
+    gather far beyond the last-level cache is DRAM-bound either way).  The
+    batch is cut into ``chunk``-token pieces, each carrying its 2-token
+    history, so that every core has work and the results are those of the
+    whole batch; one oracle_forward call per piece (or the oracle's hash,
+    sum and normalised gated fusion) on a pool of threads.  Reported: the
+    median of ``repeats`` passes on all cores the process may use (at most
+    16), and the median of ``repeats`` passes over the first sequence on 1
+    core."""
     import concurrent.futures as cf
+    import statistics
 
     import numpy as np
 
     import oracle
 
     toks, offs, hist = host_inputs.tokens, host_inputs.offsets, host_inputs.history
-    nseq = len(offs) - 1
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16, nseq))
+    pieces = []
+    for sq in range(len(offs) - 1):
+        a0, b0 = int(offs[sq]), int(offs[sq + 1])
+        for a in range(a0, b0, chunk):
+            b = min(b0, a + chunk)
+            if a == a0:
+                h = None if hist is None else np.ascontiguousarray(hist[sq:sq + 1])
+            else:
+                h = np.array([[toks[a - 2], toks[a - 1]]], np.int32)
+            pieces.append((sq, a, b, h))
 
-    def one(s):
-        a, b = int(offs[s]), int(offs[s + 1])
+    def one(piece):
+        sq, a, b, h = piece
         so = np.array([0, b - a], np.int32)
         res = None if res_np is None else res_np[a:b]
-        hs = None if hist is None else hist[s:s + 1]
         if gate is None:
             oracle.forward(toks[a:b], so, table_np, host_inputs.W_g, e1=e1_np, residual=res,
-                           history=hs, scale=scale_np, mxfp4_d=mxfp4_d)
+                           history=h, scale=scale_np, mxfp4_d=mxfp4_d)
         else:
-            # the gated path's steps: hash, sum, normalised gated fusion
-            rows = oracle.hash_rows(toks[a:b], so, R_cpu, hs)
+            rows = oracle.hash_rows(toks[a:b], so, R_cpu, h)
             eN = oracle.embed_bag_bf16(table_np, rows)
             oracle.norm_gate_add(eN, toks[a:b], e1_np, host_inputs.W_g, gate.gamma, gate.u, gate.v,
                                  gate.b, gate.eps, res)
         return b - a
 
-    passes = tokens_done = 0
-    t0 = time.time()
-    with cf.ThreadPoolExecutor(threads) as ex:
-        while True:
-            tokens_done += sum(ex.map(one, range(nseq)))
-            passes += 1
-            if time.time() - t0 >= max_seconds / 4 or passes >= 8:
-                break
-    wall = time.time() - t0
+    def timed_pass(work, threads):
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            done = sum(ex.map(one, work))
+        return done, time.perf_counter() - t0
+
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16, len(pieces)))
+    all_passes = [timed_pass(pieces, threads) for _ in range(repeats)]
+    first_seq = [pc for pc in pieces if pc[0] == 0]
+    one_passes = [timed_pass(first_seq, 1) for _ in range(repeats)]
+    n_all, n_one = all_passes[0][0], one_passes[0][0]
+    rate_all = [n_all / w for _, w in all_passes]
+    rate_one = [n_one / w for _, w in one_passes]
+    what = ("the oracle hash, sum and normalised gated fusion" if gate is not None
+            else "one oracle_forward call")
     return {
-        "value": tokens_done / wall,
+        "value": statistics.median(rate_all),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{passes} pass(es) over the {len(toks)}-token batch ({nseq} sequences, "
-                   f"{'the oracle hash, sum and normalised gated fusion' if gate is not None else 'one oracle_forward call'}"
-                   f" per sequence on {threads} threads); rows hashed mod "
-                   f"{R_cpu} into a {table_np.nbytes / 2**30:.2f} GiB host copy of the first "
-                   f"{R_cpu} table rows (the full table does not fit in host memory); "
-                   f"host copy prep {prep_s:.1f} s, not timed"),
+        "sample": (f"the {n_all}-token batch in {len(pieces)} pieces of up to {chunk} tokens ({what} per piece, "
+                   f"each with its 2-token history), median of {repeats} passes on {threads} threads; {table_note}; "
+                   f"prep {prep_s:.1f} s, not timed"),
+        "single_core": {"value": statistics.median(rate_one), "unit": "tokens/s", "cores": 1,
+                        "sample": f"the first sequence ({n_one} tokens), median of {repeats} passes"},
+        "passes_s": [round(w, 4) for _, w in all_passes],
         "cpu_model": _cpu_model(),
-        "wall_s": wall,
+        "wall_s": sum(w for _, w in all_passes) + sum(w for _, w in one_passes),
     }
 
 
@@ -317,7 +335,9 @@ def main():
         wall = time.perf_counter() - t0
         args.steps = reps * nb
         mean_launch_s = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
+        latency_floor = graph_floor(batches, e1, d, nb, reps)
     else:
+        latency_floor = None
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -378,6 +398,8 @@ def main():
         },
         "setup_s": setup_s,
     }
+    if latency_floor is not None:
+        result["latency_floor"] = latency_floor
 
     if not args.no_cpu_baseline:
         R_cpu = min(args.cpu_rows, spec.R)
@@ -394,13 +416,49 @@ def main():
             scale_np = None
         e1_np = None if e1 is None else e1.cpu().numpy().view(np.uint16).reshape(spec.V, d)
         res_np = None if batches[0][3] is None else batches[0][3].cpu().numpy().view(np.uint16).reshape(n, d)
+        note = (f"rows hashed mod {R_cpu} into a {table_np.nbytes / 2**30:.2f} GiB host copy of the first "
+                f"{R_cpu} of the {spec.R} table rows (the full table does not fit in host memory)")
         result["cpu_baseline"] = cpu_baseline(HostInputs(spec.replace(R=R_cpu)), table_np, scale_np,
-                                              e1_np, res_np, R_cpu, time.time() - tp,
+                                              e1_np, res_np, R_cpu, time.time() - tp, note,
                                               mxfp4_d=d if spec.table == "mxfp4" else None,
                                               gate=gp if gated else None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def graph_floor(batches, e1, d, nb, reps):
+    """What a graph-replayed step costs at least, measured the same way as the
+    step (one graph holding nb launches, replayed reps times): an empty
+    kernel (torch.cuda._sleep(0)), and one kernel that loads the batch's
+    token ids and then, dependent on them, their e1 rows (torch.index_select:
+    launch + a dependent pair of memory round trips, which is the shape of a
+    decode step's critical path: token ids, then the rows they select)."""
+    import torch
+
+    def replay_us(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nb):
+                body(i)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        for _ in range(reps):
+            g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        return s_ev.elapsed_time(e_ev) * 1e3 / (reps * nb)
+
+    floor = {"empty_kernel_us": replay_us(lambda i: torch.cuda._sleep(0))}
+    if e1 is not None:
+        table = e1.view(-1, d)
+        outs = [torch.empty((batches[i][0].numel(), d), dtype=table.dtype, device=table.device) for i in range(nb)]
+        floor["token_then_row_load_us"] = replay_us(
+            lambda i: torch.index_select(table, 0, batches[i][0], out=outs[i]))
+    return floor
 
 
 def backward_bytes_per_token(d: int, rows_per_token_unique: float, tokens_unique: float) -> float:
@@ -749,6 +807,12 @@ def run_host(args):
         "setup_s": setup_s,
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        res_np = di.residual.cpu().numpy().view(np.uint16).reshape(n, d)
+        e1_np = di.e1.cpu().numpy().view(np.uint16).reshape(spec.V, d)
+        result["cpu_baseline"] = cpu_baseline(h, hb.numpy(np.uint16, (R, d)), None, e1_np, res_np, R, 0.0,
+                                              f"the full {R * d * 2 / 2**30:.2f} GiB table, read in place in "
+                                              "pinned host memory")
     print(json.dumps(result), flush=True)
     hb.free()
 
