@@ -527,10 +527,9 @@ def run_backward(args):
     ne = torch.empty(1, dtype=torch.int64, device=dev)
     gw = torch.empty(d, dtype=torch.float32, device=dev)
 
-    # The table gradient (HBM-bound) on the main stream; the e1 and gate
-    # gradients (bound by their in-order chains) on a side stream with their
-    # own workspace, joined at the end of the step.  --serial runs all three
-    # in order on one stream.
+    # The table gradient (HBM-bound) on the main stream; the gate and e1
+    # gradients on a side stream with their own workspace, joined at the end
+    # of the step.  --serial runs all three in order on one stream.
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     ws2 = ng.grad_workspace(n, d, dev)
@@ -544,9 +543,11 @@ def run_backward(args):
             return
         ev_in.record(main)
         side.wait_event(ev_in)
+        # the gate gradient (bandwidth-bound) first, while the main stream
+        # sorts the row ids (little traffic); then the e1 gradient
+        ng.ngram_grad_gate(rows, g, eN, grad_Wg_out=gw, workspace=ws2, stream=side)
         ng.ngram_grad_e1(tok, rows, g, spec.V, grad_tokens_out=et, grad_out=ge, n_unique_out=ne, workspace=ws2,
                          stream=side)
-        ng.ngram_grad_gate(rows, g, eN, grad_Wg_out=gw, workspace=ws2, stream=side)
         ng.ngram_grad_table(rows, W, g, R, grad_rows_out=gr, grad_out=gt, n_unique_out=nu, workspace=ws,
                             stream=main)
         ev_side.record(side)

@@ -1088,36 +1088,128 @@ __global__ void __launch_bounds__(256) select_kernel(const int32_t* counts, int6
 // token ids) with their positions still ascending, then a segmented reduce
 // sums each group in that fixed order.  No floating-point atomics, so every
 // result is reproducible bit for bit.
-constexpr int kSortItems = 8;                  // items per thread
-constexpr int kSortTile = 256 * kSortItems;    // 2048 items per 256-thread tile
-constexpr int kScanTile = 4096;                // 1024 threads x 4 items
+constexpr int kSortItems = 8;                      // items per thread
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kSortTile = kSortThreads * kSortItems;   // 8192 items per tile
+constexpr int kRadixBits = 9;
+constexpr int kRadixBins = 1 << kRadixBits;            // 512
+constexpr int kScanTile = 4096;                        // items per tile of the segment scan
 
-__global__ void __launch_bounds__(256) radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t N, int shift,
-                                                         uint32_t* __restrict__ block_hist, int64_t nblocks) {
-    __shared__ uint32_t h[256];
-    h[threadIdx.x] = 0;
+// Per-tile digit counts: block_hist[digit][tile].
+__global__ void __launch_bounds__(kSortThreads) radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t N,
+                                                                  int shift, uint32_t* __restrict__ block_hist,
+                                                                  int64_t nblocks) {
+    __shared__ uint32_t h[kRadixBins];
+    for (int q = threadIdx.x; q < kRadixBins; q += kSortThreads) h[q] = 0;
     __syncthreads();
     const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kSortTile;
     for (int q = 0; q < kSortItems; ++q) {
-        const int64_t idx = tile0 + q * 256 + threadIdx.x;
-        if (idx < N) atomicAdd(&h[(keys[idx] >> shift) & 255u], 1u);
+        const int64_t idx = tile0 + q * kSortThreads + threadIdx.x;
+        if (idx < N) atomicAdd(&h[(keys[idx] >> shift) & (kRadixBins - 1)], 1u);
     }
     __syncthreads();
-    block_hist[static_cast<int64_t>(threadIdx.x) * nblocks + blockIdx.x] = h[threadIdx.x];
+    for (int q = threadIdx.x; q < kRadixBins; q += kSortThreads)
+        block_hist[static_cast<int64_t>(q) * nblocks + blockIdx.x] = h[q];
 }
 
-// Stable scatter of one 8-bit digit.  Tile order is (wavefront, round, lane):
+// Exclusive scan, in place, of M uint32 values by one workgroup: thread t
+// owns a contiguous run of ceil(M / 1024) values.
+__global__ void __launch_bounds__(1024) scan_one_block_kernel(uint32_t* __restrict__ v, int64_t M) {
+    __shared__ uint32_t wsum[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t per = (M + 1023) / 1024;
+    const int64_t b0 = static_cast<int64_t>(threadIdx.x) * per;
+    const int64_t b1 = b0 + per < M ? b0 + per : M;
+    uint32_t s = 0;
+    for (int64_t q0 = b0; q0 < b1; q0 += 8) {        // 8 independent loads in flight
+        uint32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = q0 + u < b1 ? v[q0 + u] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += c[u];
+    }
+    uint32_t x = s;                                  // inclusive scan of the run sums over the wavefront
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t t = lane < 16 ? wsum[lane] : 0u;
+        for (int off = 1; off < 16; off <<= 1) {
+            const uint32_t y = __shfl_up(t, off);
+            if (lane >= off) t += y;
+        }
+        if (lane < 16) wsum[lane] = t;
+    }
+    __syncthreads();
+    uint32_t run = (wave > 0 ? wsum[wave - 1] : 0u) + x - s;
+    for (int64_t q0 = b0; q0 < b1; q0 += 8) {
+        uint32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = q0 + u < b1 ? v[q0 + u] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (q0 + u < b1) v[q0 + u] = run;
+            run += c[u];
+        }
+    }
+}
+
+// Up to this many tiles the scatter computes its digit offsets itself from
+// the per-tile counts (no scan launch between the count and the scatter).
+constexpr int64_t kScatterOwnOffsetsMax = 128;
+
+// Stable scatter of one 9-bit digit.  Tile order is (wavefront, round, lane):
 // an item's rank among equal digits of its tile = equal digits in earlier
 // wavefronts + in earlier rounds of its wavefront + in lower lanes of its
-// round (lanes with an equal digit found by eight ballots).
-__global__ void __launch_bounds__(256) radix_scatter_kernel(const uint32_t* __restrict__ kin,
-                                                            const int32_t* __restrict__ vin, int64_t N, int shift,
-                                                            const uint32_t* __restrict__ offs, int64_t nblocks,
-                                                            uint32_t* __restrict__ kout, int32_t* __restrict__ vout) {
-    __shared__ uint32_t cnt[4][256];
-    __shared__ uint32_t wpre[4][256];
+// round (lanes with an equal digit found by nine ballots).  The tile's base
+// for digit q is offs[q][tile] (the exclusive scan of the counts in digit-major
+// order) or, with OWN, computed here from the counts hist[q][tile].
+template <bool OWN>
+__global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint32_t* __restrict__ kin,
+                                                                     const int32_t* __restrict__ vin, int64_t N,
+                                                                     int shift, const uint32_t* __restrict__ offs,
+                                                                     int64_t nblocks, uint32_t* __restrict__ kout,
+                                                                     int32_t* __restrict__ vout) {
+    __shared__ uint32_t cnt[kSortWaves][kRadixBins];
+    __shared__ uint32_t base[kRadixBins];
+    __shared__ uint32_t wtot[kSortWaves];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int q = threadIdx.x; q < 4 * 256; q += 256) (&cnt[0][0])[q] = 0;
+    for (int q = threadIdx.x; q < kSortWaves * kRadixBins; q += kSortThreads) (&cnt[0][0])[q] = 0;
+    if constexpr (OWN) {
+        // digit q = thread / 2: half h of the tiles; the digit's count over all
+        // tiles and over the tiles before this one
+        const int q = threadIdx.x >> 1, h = threadIdx.x & 1;
+        const int64_t half = (nblocks + 1) / 2;
+        const int64_t c0 = h * half, c1 = c0 + half < nblocks ? c0 + half : nblocks;
+        uint32_t tot = 0, bef = 0;
+        for (int64_t c = c0; c < c1; c += 8) {
+            uint32_t v8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v8[u] = c + u < c1 ? offs[static_cast<int64_t>(q) * nblocks + c + u] : 0u;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                tot += v8[u];
+                if (c + u < static_cast<int64_t>(blockIdx.x)) bef += v8[u];
+            }
+        }
+        tot += __shfl_xor(tot, 1);
+        bef += __shfl_xor(bef, 1);
+        // exclusive scan of the digit totals: lane pairs hold one digit each
+        uint32_t x = h == 0 ? tot : 0u;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wtot[w] = x;
+        __syncthreads();
+        uint32_t earlier = 0;
+        for (int ww = 0; ww < w; ++ww) earlier += wtot[ww];
+        if (h == 0) base[q] = earlier + x - tot + bef;
+    }
     __syncthreads();
     const int64_t base0 = static_cast<int64_t>(blockIdx.x) * kSortTile + w * (64 * kSortItems);
     const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -1129,10 +1221,10 @@ __global__ void __launch_bounds__(256) radix_scatter_kernel(const uint32_t* __re
         const bool active = idx < N;
         key[r] = active ? kin[idx] : 0u;
         val[r] = active ? vin[idx] : 0;
-        const uint32_t dg = (key[r] >> shift) & 255u;
+        const uint32_t dg = (key[r] >> shift) & (kRadixBins - 1);
         uint64_t same = __ballot(active);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < kRadixBits; ++b) {
             const bool bit = (dg >> b) & 1u;
             const uint64_t m = __ballot(active && bit);
             same &= bit ? m : ~m;
@@ -1144,11 +1236,13 @@ __global__ void __launch_bounds__(256) radix_scatter_kernel(const uint32_t* __re
         local[r] = before + rank;
     }
     __syncthreads();
-    {
+    // cnt[w][dg] := equal digits in wavefronts before w (exclusive prefix)
+    for (int dg = threadIdx.x; dg < kRadixBins; dg += kSortThreads) {
         uint32_t acc = 0;
-        for (int ww = 0; ww < 4; ++ww) {
-            wpre[ww][threadIdx.x] = acc;
-            acc += cnt[ww][threadIdx.x];
+        for (int ww = 0; ww < kSortWaves; ++ww) {
+            const uint32_t c = cnt[ww][dg];
+            cnt[ww][dg] = acc;
+            acc += c;
         }
     }
     __syncthreads();
@@ -1156,25 +1250,49 @@ __global__ void __launch_bounds__(256) radix_scatter_kernel(const uint32_t* __re
     for (int r = 0; r < kSortItems; ++r) {
         const int64_t idx = base0 + r * 64 + lane;
         if (idx < N) {
-            const uint32_t dg = (key[r] >> shift) & 255u;
-            const uint32_t pos = offs[static_cast<int64_t>(dg) * nblocks + blockIdx.x] + wpre[w][dg] + local[r];
+            const uint32_t dg = (key[r] >> shift) & (kRadixBins - 1);
+            const uint32_t b0 = OWN ? base[dg] : offs[static_cast<int64_t>(dg) * nblocks + blockIdx.x];
+            const uint32_t pos = b0 + cnt[w][dg] + local[r];
             kout[pos] = key[r];
             vout[pos] = val[r];
         }
     }
 }
 
-// Exclusive scan of M uint32 (tiles of 4096; tile totals to `tile_sums`).
-__global__ void __launch_bounds__(1024) scan_tiles_kernel(const uint32_t* in, uint32_t* out, int64_t M,
-                                                          uint32_t* tile_sums) {
+// Keys and positions to sort: keys[t] = the id (limit for an invalid one),
+// vals[t] = t.  Thread 0 also clears the group count.
+__global__ void __launch_bounds__(256) sort_init_kernel(const int32_t* __restrict__ ids, int64_t N, int stride,
+                                                        const int32_t* __restrict__ valid_rows, uint32_t limit,
+                                                        uint32_t* __restrict__ keys, int32_t* __restrict__ vals,
+                                                        int64_t* __restrict__ n_unique) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t == 0) *n_unique = 0;
+    if (t >= N) return;
+    const int32_t id = ids[t];
+    bool ok = id >= 0 && static_cast<uint32_t>(id) < limit;
+    if (valid_rows) ok = ok && valid_rows[t * stride] >= 0;
+    keys[t] = ok ? static_cast<uint32_t>(id) : limit;
+    vals[t] = static_cast<int32_t>(t);
+}
+
+// Group numbering of the sorted keys, first half: per tile of kScanTile
+// items, the exclusive scan of the group-start flags (a valid key that
+// differs from its predecessor) into seg[], and the tile's count.
+__global__ void __launch_bounds__(1024) seg_scan_kernel(const uint32_t* __restrict__ keys, int64_t N, uint32_t limit,
+                                                        uint32_t* __restrict__ seg, uint32_t* __restrict__ tile_sums) {
     __shared__ uint32_t wsum[16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile + threadIdx.x * 4;
-    uint32_t v[4], s = 0;
+    uint32_t f[4], s = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        v[q] = base + q < M ? in[base + q] : 0u;
-        s += v[q];
+        const int64_t t = base + q;
+        f[q] = 0u;
+        if (t < N) {
+            const uint32_t k = keys[t];
+            f[q] = (k < limit && (t == 0 || keys[t - 1] != k)) ? 1u : 0u;
+        }
+        s += f[q];
     }
     uint32_t x = s;
     for (int off = 1; off < 64; off <<= 1) {
@@ -1195,60 +1313,58 @@ __global__ void __launch_bounds__(1024) scan_tiles_kernel(const uint32_t* in, ui
     uint32_t prefix = (wave > 0 ? wsum[wave - 1] : 0u) + x - s;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (base + q < M) out[base + q] = prefix;
-        prefix += v[q];
+        if (base + q < N) seg[base + q] = prefix;
+        prefix += f[q];
     }
-    if (threadIdx.x == 0 && tile_sums) tile_sums[blockIdx.x] = wsum[15];
+    if (threadIdx.x == 0) tile_sums[blockIdx.x] = wsum[15];
 }
 
-__global__ void __launch_bounds__(256) scan_add_kernel(uint32_t* out, int64_t M, const uint32_t* tile_prefix) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x + kScanTile;
-    if (i < M) out[i] += tile_prefix[i / kScanTile];
-}
-
-__global__ void __launch_bounds__(256) sort_init_kernel(const int32_t* __restrict__ ids, int64_t N, int stride,
-                                                        const int32_t* __restrict__ valid_rows, uint32_t limit,
-                                                        uint32_t* __restrict__ keys, int32_t* __restrict__ vals) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= N) return;
-    const int32_t id = ids[t];
-    bool ok = id >= 0 && static_cast<uint32_t>(id) < limit;
-    if (valid_rows) ok = ok && valid_rows[t * stride] >= 0;
-    keys[t] = ok ? static_cast<uint32_t>(id) : limit;
-    vals[t] = static_cast<int32_t>(t);
-}
-
-__global__ void __launch_bounds__(256) seg_flags_kernel(const uint32_t* keys, int64_t N, uint32_t limit, uint32_t* flags) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= N) return;
-    const uint32_t k = keys[t];
-    flags[t] = (k < limit && (t == 0 || keys[t - 1] != k)) ? 1u : 0u;
-}
-
-// seg[t]: exclusive scan of the flags.  Writes each group's first index, its
-// id, the end sentinel and the group count.
-__global__ void __launch_bounds__(256) seg_bounds_kernel(const uint32_t* keys, const uint32_t* seg, int64_t N,
-                                                         uint32_t limit, int32_t* seg_start, int32_t* ids_out,
-                                                         int64_t* n_unique) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= N) return;
-    const uint32_t k = keys[t];
-    if (k >= limit) return;
-    const bool first = t == 0 || keys[t - 1] != k;
-    if (first) {
-        seg_start[seg[t]] = static_cast<int32_t>(t);
-        ids_out[seg[t]] = static_cast<int32_t>(k);
-    }
-    if (t + 1 == N || keys[t + 1] >= limit) {
-        const uint32_t U = seg[t] + (first ? 1u : 0u);
-        seg_start[U] = static_cast<int32_t>(t + 1);
-        *n_unique = U;
+// Second half: seg[t] += the counts of the earlier tiles (each workgroup adds
+// them up itself), then each group's first index, its id, the end sentinel
+// and the group count.
+__global__ void __launch_bounds__(1024) seg_bounds_kernel(const uint32_t* __restrict__ keys, uint32_t* __restrict__ seg,
+                                                          const uint32_t* __restrict__ tile_sums, int64_t N,
+                                                          uint32_t limit, int32_t* __restrict__ seg_start,
+                                                          int32_t* __restrict__ ids_out, int64_t* __restrict__ n_unique) {
+    __shared__ uint32_t red[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t part = 0;
+    for (int64_t q = threadIdx.x; q < blockIdx.x; q += 1024) part += tile_sums[q];
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    uint32_t earlier = 0;
+    for (int q = 0; q < 16; ++q) earlier += red[q];
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile + threadIdx.x * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t t = base + q;
+        if (t >= N) break;
+        const uint32_t sg = seg[t] + earlier;
+        seg[t] = sg;
+        const uint32_t k = keys[t];
+        if (k >= limit) continue;
+        const bool first = t == 0 || keys[t - 1] != k;
+        if (first) {
+            seg_start[sg] = static_cast<int32_t>(t);
+            ids_out[sg] = static_cast<int32_t>(k);
+        }
+        if (t + 1 == N || keys[t + 1] >= limit) {
+            const uint32_t U = sg + (first ? 1u : 0u);
+            seg_start[U] = static_cast<int32_t>(t + 1);
+            *n_unique = U;
+        }
     }
 }
 
 __global__ void __launch_bounds__(64) set_i64_kernel(int64_t* p, int64_t v) {
     if (threadIdx.x == 0) *p = v;
 }
+
+// Groups longer than this many items are walked by long_walk_kernel, with
+// four times the rows in flight per wavefront (a Zipf-hot token's e1
+// gradient adds thousands of dL/dout rows, one after another per column).
+constexpr int kLongGroup = 512;
 
 // Workgroup c owns the groups that start among sorted items [64 c, 64 c + 64)
 // and walks their items in order (past the chunk's end for the last group),
@@ -1258,7 +1374,53 @@ __global__ void __launch_bounds__(64) set_i64_kernel(int64_t* p, int64_t v) {
 // (groups can be thousands of items long: a Zipf-hot token's e1 gradient).
 constexpr int kWalkChunk = 64;
 
-template <bool WEIGHT, int DEPTH>
+// 16 rows ahead: the deepest prefetch that stays in registers (no scratch).
+constexpr int kWalkDepth = 16;
+
+// Rows of items tb + first .. tb + first + B - 1 (lanes of pl hold the
+// positions of items tb + 0 .. 63); an item past the end loads item tb's row,
+// which is always valid, and is not added.
+template <int B>
+__device__ inline void walk_load(uint4 gv[B], int32_t pl, int first, int64_t tb, int64_t te,
+                                 const uint16_t* __restrict__ g, int32_t d, int64_t jc, int pos_shift) {
+#pragma unroll
+    for (int m = 0; m < B; ++m) {
+        const int src = tb + first + m < te ? first + m : 0;
+        const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readlane(pl, src) >> pos_shift);
+        gv[m] = *reinterpret_cast<const uint4*>(g + i * d + jc);
+    }
+}
+
+// Add the bank's items in order; when the id changes, store the finished
+// group's sum and start the next one.
+template <bool WEIGHT, int B>
+__device__ inline void walk_add(float acc[8], const float w[8], const uint4 gv[B], uint32_t kl, int first,
+                                int64_t tb, int64_t te, uint32_t& prev, int64_t& uo, float* __restrict__ out,
+                                int32_t d, int64_t jc, bool col_ok) {
+#pragma unroll
+    for (int m = 0; m < B; ++m) {
+        if (tb + first + m < te) {          // uniform predicate, so every index stays constant
+            const uint32_t km = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kl), first + m));
+            if (km != prev) {               // a new group: store the finished one
+                float* o = out + uo * d + jc;
+                if (col_ok) {
+                    reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+                ++uo;
+                prev = km;
+            }
+            const float x[8] = {bf16lo(gv[m].x), bf16hi(gv[m].x), bf16lo(gv[m].y), bf16hi(gv[m].y),
+                                bf16lo(gv[m].z), bf16hi(gv[m].z), bf16lo(gv[m].w), bf16hi(gv[m].w)};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = WEIGHT ? __builtin_fmaf(w[q], x[q], acc[q]) : acc[q] + x[q];
+        }
+    }
+}
+
+template <bool WEIGHT>
 __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restrict__ keys,
                                                         const uint32_t* __restrict__ seg,
                                                         const int32_t* __restrict__ seg_start,
@@ -1281,7 +1443,14 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
     const int64_t tl = (t0 + kWalkChunk < nvalid ? t0 + kWalkChunk : nvalid) - 1;
     const bool tl_starts = keys[tl - 1 >= 0 ? tl - 1 : 0] != keys[tl] || tl == 0;
     const int64_t u_last = static_cast<int64_t>(seg[tl]) - (tl_starts ? 0 : 1);
-    const int64_t t_begin = seg_start[u], t_end = seg_start[u_last + 1];
+    const int64_t t_begin = seg_start[u];
+    int64_t t_end = seg_start[u_last + 1];
+    // a group longer than kLongGroup items (only the last one can be) is
+    // walked by long_walk_kernel instead
+    if (t_end - seg_start[u_last] > kLongGroup) {
+        if (u_last == u) return;
+        t_end = seg_start[u_last];
+    }
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
@@ -1308,36 +1477,10 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
             const int64_t tn = tb + 64 + lane;
             const uint32_t kl_next = tn < t_end ? keys[tn] : 0u;
             const int32_t pl_next = tn < t_end ? sorted_pos[tn] : 0;
-            for (int m0 = 0; m0 < 64 && tb + m0 < t_end; m0 += DEPTH) {
-                uint4 gv[DEPTH];
-#pragma unroll
-                for (int m = 0; m < DEPTH; ++m) {
-                    const int src = tb + m0 + m < t_end ? m0 + m : m0;
-                    const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readlane(pl, src) >> pos_shift);
-                    gv[m] = *reinterpret_cast<const uint4*>(g + i * d + jc);
-                }
-#pragma unroll
-                for (int m = 0; m < DEPTH; ++m) {
-                    if (tb + m0 + m < t_end) {      // uniform predicate, so every index stays constant
-                        const uint32_t km = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kl), m0 + m));
-                        if (km != prev) {           // a new group: store the finished one
-                            float* o = out + uo * d + jc;
-                            if (col_ok) {
-                                reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                                reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-                            }
-#pragma unroll
-                            for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-                            ++uo;
-                            prev = km;
-                        }
-                        const float x[8] = {bf16lo(gv[m].x), bf16hi(gv[m].x), bf16lo(gv[m].y), bf16hi(gv[m].y),
-                                            bf16lo(gv[m].z), bf16hi(gv[m].z), bf16lo(gv[m].w), bf16hi(gv[m].w)};
-#pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            acc[q] = WEIGHT ? __builtin_fmaf(w[q], x[q], acc[q]) : acc[q] + x[q];
-                    }
-                }
+            for (int m0 = 0; m0 < 64 && tb + m0 < t_end; m0 += kWalkDepth) {
+                uint4 gv[kWalkDepth];
+                walk_load<kWalkDepth>(gv, pl, m0, tb, t_end, g, d, jc, pos_shift);
+                walk_add<WEIGHT, kWalkDepth>(acc, w, gv, kl, m0, tb, t_end, prev, uo, out, d, jc, col_ok);
             }
             kl = kl_next;
             pl = pl_next;
@@ -1347,6 +1490,83 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
             reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
             reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
+    }
+}
+
+// The groups longer than kLongGroup items, listed in an unspecified order.
+__global__ void __launch_bounds__(256) long_groups_kernel(const int32_t* __restrict__ seg_start,
+                                                          const int64_t* __restrict__ n_unique, int64_t N,
+                                                          int32_t* __restrict__ longs, uint32_t* __restrict__ nlong) {
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (u >= N || u >= *n_unique) return;
+    if (seg_start[u + 1] - seg_start[u] > kLongGroup) longs[atomicAdd(nlong, 1u)] = static_cast<int32_t>(u);
+}
+
+// One long group per workgroup iteration: wavefront w of workgroup (x, y)
+// owns columns 512 y + 128 w + 2 lane (+1) and walks the group's items in
+// position order, so each column's sum runs in the same order as in
+// seg_walk_kernel.  Two banks of kLongBank dL/dout rows: while one bank is
+// summed, the other bank's loads (and the next 64 positions) are in flight.
+constexpr int kLongBank = 32;
+
+__device__ inline void long_load(uint32_t gv[kLongBank], int32_t pl, int first, int64_t tb, int64_t te,
+                                 const uint16_t* __restrict__ g, int32_t d, int64_t jc, int pos_shift) {
+#pragma unroll
+    for (int m = 0; m < kLongBank; ++m) {
+        const int src = tb + first + m < te ? first + m : 0;     // lane 0 (item tb) is always valid
+        const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readlane(pl, src) >> pos_shift);
+        gv[m] = *reinterpret_cast<const uint32_t*>(g + i * d + jc);
+    }
+}
+
+template <bool WEIGHT>
+__device__ inline void long_add(float& a0, float& a1, const uint32_t gv[kLongBank], int first, int64_t tb,
+                                int64_t te, float w0, float w1) {
+#pragma unroll
+    for (int m = 0; m < kLongBank; ++m) {
+        if (tb + first + m < te) {                                 // uniform predicate
+            const float x0 = bf16lo(gv[m]), x1 = bf16hi(gv[m]);
+            a0 = WEIGHT ? __builtin_fmaf(w0, x0, a0) : a0 + x0;
+            a1 = WEIGHT ? __builtin_fmaf(w1, x1, a1) : a1 + x1;
+        }
+    }
+}
+
+template <bool WEIGHT>
+__global__ void __launch_bounds__(256) long_walk_kernel(const int32_t* __restrict__ longs,
+                                                        const uint32_t* __restrict__ nlong,
+                                                        const int32_t* __restrict__ seg_start,
+                                                        const int32_t* __restrict__ sorted_pos, int pos_shift,
+                                                        const uint16_t* __restrict__ g, const float* __restrict__ W,
+                                                        int32_t d, float* __restrict__ out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t j0 = static_cast<int64_t>(blockIdx.y) * 512 + wave * 128 + lane * 2;
+    const bool col_ok = j0 < d;                  // d % 8 == 0: j0 + 1 < d as well
+    const int64_t jc = col_ok ? j0 : 0;
+    float w0 = 1.0f, w1 = 1.0f;
+    if (WEIGHT) {
+        const float2 wv = *reinterpret_cast<const float2*>(W + jc);
+        w0 = wv.x; w1 = wv.y;
+    }
+    const int64_t count = *nlong;
+    for (int64_t q = blockIdx.x; q < count; q += gridDim.x) {
+        const int64_t u = longs[q];
+        const int64_t tb0 = seg_start[u], te = seg_start[u + 1];
+        float a0 = 0.0f, a1 = 0.0f;
+        uint32_t ga[kLongBank], gb[kLongBank];
+        // lane m of pl holds the position of item tb + m
+        int32_t pl = tb0 + lane < te ? sorted_pos[tb0 + lane] : 0;
+        long_load(ga, pl, 0, tb0, te, g, d, jc, pos_shift);
+        for (int64_t tb = tb0; tb < te; tb += 2 * kLongBank) {
+            long_load(gb, pl, kLongBank, tb, te, g, d, jc, pos_shift);
+            const int64_t tn = tb + 2 * kLongBank;
+            const int32_t pn = tn + lane < te ? sorted_pos[tn + lane] : 0;
+            long_add<WEIGHT>(a0, a1, ga, 0, tb, te, w0, w1);
+            if (tn < te) long_load(ga, pn, 0, tn, te, g, d, jc, pos_shift);
+            long_add<WEIGHT>(a0, a1, gb, kLongBank, tb, te, w0, w1);
+            pl = pn;
+        }
+        if (col_ok) *reinterpret_cast<float2*>(out + u * d + j0) = make_float2(a0, a1);
     }
 }
 
@@ -1587,7 +1807,7 @@ int check_pool(const ngram_table* T, const ngram_row_pool* P) {
 // Workspace of the gradient calls, for N = 16 n sort items (the table) and
 // the gate's chunk partials.
 struct GradLayout {
-    int64_t N, nblocks, keysA, valsA, keysB, valsB, flags, segs, hist, tiles, parts, total;
+    int64_t N, nblocks, ntiles, keysA, valsA, keysB, valsB, segs, starts, hist, tiles, longs, parts, total;
 };
 
 GradLayout grad_layout(int64_t n, int32_t d) {
@@ -1595,35 +1815,26 @@ GradLayout grad_layout(int64_t n, int32_t d) {
     GradLayout L;
     L.N = kK * n;
     L.nblocks = (L.N + kSortTile - 1) / kSortTile;
+    L.ntiles = (L.N + kScanTile - 1) / kScanTile;
     int64_t o = 0;
     L.keysA = o; o = up(o + 4 * L.N);
     L.valsA = o; o = up(o + 4 * L.N);
     L.keysB = o; o = up(o + 4 * L.N);
     L.valsB = o; o = up(o + 4 * L.N);
-    L.flags = o; o = up(o + 4 * L.N);
-    L.segs = o; o = up(o + 4 * (L.N + 1));
-    L.hist = o; o = up(o + 4 * 256 * (L.nblocks > 0 ? L.nblocks : 1));
-    L.tiles = o; o = up(o + 4 * 2 * kScanTile);
+    L.segs = o; o = up(o + 4 * L.N);
+    L.starts = o; o = up(o + 4 * (L.N + 1));
+    L.hist = o; o = up(o + 4 * kRadixBins * (L.nblocks > 0 ? L.nblocks : 1));
+    L.tiles = o; o = up(o + 4 * (L.ntiles > 0 ? L.ntiles : 1));
+    L.longs = o; o = up(o + 16 + 4 * (L.N / kLongGroup + 1));
     L.parts = o; o = up(o + 8 * ((n + kGateChunk - 1) / kGateChunk) * static_cast<int64_t>(d > 0 ? d : 1));
     L.total = o;
     return L;
 }
 
-// Exclusive scan of M <= 4096^2 uint32 values, in place allowed.
-void scan_u32(const uint32_t* in, uint32_t* out, int64_t M, uint32_t* tiles, hipStream_t st) {
-    const int64_t ntiles = (M + kScanTile - 1) / kScanTile;
-    hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(1024), 0, st, in, out, M, tiles);
-    if (ntiles > 1) {
-        hipLaunchKernelGGL(scan_tiles_kernel, dim3(1), dim3(1024), 0, st, tiles, tiles + kScanTile, ntiles,
-                           static_cast<uint32_t*>(nullptr));
-        const int64_t rest = M - kScanTile;
-        hipLaunchKernelGGL(scan_add_kernel, dim3(static_cast<unsigned>((rest + 255) / 256)), dim3(256), 0, st, out, M,
-                           tiles + kScanTile);
-    }
-}
-
 // Stable sort of N (key, value) pairs by key (keys <= limit), ping-ponging
 // between the A and B buffers; returns the buffers that hold the result.
+// Each 9-bit pass: per-tile digit counts, their exclusive scan (one
+// workgroup), the stable scatter.
 void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStream_t st, uint32_t** keys_out,
                 int32_t** vals_out) {
     uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.keysA);
@@ -1631,18 +1842,22 @@ void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStr
     uint32_t* kB = reinterpret_cast<uint32_t*>(ws + L.keysB);
     int32_t* vB = reinterpret_cast<int32_t*>(ws + L.valsB);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
-    uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
     const int64_t nblocks = (N + kSortTile - 1) / kSortTile;
     int bits = 1;
     while (bits < 32 && (limit >> bits) != 0) ++bits;
-    const int passes = (bits + 7) / 8;
+    const int passes = (bits + kRadixBits - 1) / kRadixBits;
     for (int p = 0; p < passes; ++p) {
-        const int shift = 8 * p;
-        hipLaunchKernelGGL(radix_hist_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st, kA, N, shift,
-                           hist, nblocks);
-        scan_u32(hist, hist, 256 * nblocks, tiles, st);
-        hipLaunchKernelGGL(radix_scatter_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st, kA, vA, N,
-                           shift, hist, nblocks, kB, vB);
+        const int shift = kRadixBits * p;
+        hipLaunchKernelGGL(radix_hist_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0, st, kA, N,
+                           shift, hist, nblocks);
+        if (nblocks <= kScatterOwnOffsetsMax) {
+            hipLaunchKernelGGL(radix_scatter_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0,
+                               st, kA, vA, N, shift, hist, nblocks, kB, vB);
+        } else {
+            hipLaunchKernelGGL(scan_one_block_kernel, dim3(1), dim3(1024), 0, st, hist, kRadixBins * nblocks);
+            hipLaunchKernelGGL(radix_scatter_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0,
+                               st, kA, vA, N, shift, hist, nblocks, kB, vB);
+        }
         uint32_t* tk = kA; kA = kB; kB = tk;
         int32_t* tv = vA; vA = vB; vB = tv;
     }
@@ -1650,32 +1865,43 @@ void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStr
     *vals_out = vA;
 }
 
-// Sort, find the groups of equal ids and reduce each group in position order.
+// Sort, find the groups of equal ids and reduce each group in position order
+// (groups longer than kLongGroup items in a launch of their own).
 template <bool WEIGHT>
 int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* valid_rows, uint32_t limit, int pos_shift,
                    const uint16_t* g, const float* W, int32_t d, int32_t* ids_out, float* grad_out, int64_t* n_unique,
                    void* workspace, const GradLayout& L, hipStream_t st) {
     char* ws = static_cast<char*>(workspace);
-    hipLaunchKernelGGL(set_i64_kernel, dim3(1), dim3(64), 0, st, n_unique, int64_t{0});
-    if (N == 0) return hip_status("gradient launch");
+    if (N == 0) {
+        hipLaunchKernelGGL(set_i64_kernel, dim3(1), dim3(64), 0, st, n_unique, int64_t{0});
+        return hip_status("gradient launch");
+    }
     uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.keysA);
     int32_t* vA = reinterpret_cast<int32_t*>(ws + L.valsA);
     const unsigned gN = static_cast<unsigned>((N + 255) / 256);
-    hipLaunchKernelGGL(sort_init_kernel, dim3(gN), dim3(256), 0, st, ids, N, stride, valid_rows, limit, kA, vA);
+    hipLaunchKernelGGL(sort_init_kernel, dim3(gN), dim3(256), 0, st, ids, N, stride, valid_rows, limit, kA, vA,
+                       n_unique);
     uint32_t* keys = nullptr;
     int32_t* pos = nullptr;
     radix_sort(ws, L, N, limit, st, &keys, &pos);
-    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.flags);
-    int32_t* segs = reinterpret_cast<int32_t*>(ws + L.segs);
-    hipLaunchKernelGGL(seg_flags_kernel, dim3(gN), dim3(256), 0, st, keys, N, limit, flags);
-    scan_u32(flags, flags, N, reinterpret_cast<uint32_t*>(ws + L.tiles), st);
-    hipLaunchKernelGGL(seg_bounds_kernel, dim3(gN), dim3(256), 0, st, keys, flags, N, limit, segs, ids_out, n_unique);
+    uint32_t* segs = reinterpret_cast<uint32_t*>(ws + L.segs);
+    int32_t* starts = reinterpret_cast<int32_t*>(ws + L.starts);
+    uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
+    const unsigned ntiles = static_cast<unsigned>((N + kScanTile - 1) / kScanTile);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(ntiles), dim3(1024), 0, st, keys, N, limit, segs, tiles);
+    hipLaunchKernelGGL(seg_bounds_kernel, dim3(ntiles), dim3(1024), 0, st, keys, segs, tiles, N, limit, starts, ids_out,
+                       n_unique);
+    uint32_t* nlong = reinterpret_cast<uint32_t*>(ws + L.longs);
+    int32_t* longs = reinterpret_cast<int32_t*>(ws + L.longs + 16);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int32_t*>(nlong), 1, 0);
+    hipLaunchKernelGGL(long_groups_kernel, dim3(gN), dim3(256), 0, st, starts, n_unique, N, longs, nlong);
     const int nslices = (d + kSlice - 1) / kSlice;
     const int waves = nslices < 16 ? nslices : 16;
     const int64_t grid = (N + kWalkChunk - 1) / kWalkChunk;
-    // 16 rows ahead: the deepest prefetch that stays in registers (no scratch)
-    hipLaunchKernelGGL((seg_walk_kernel<WEIGHT, 16>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, keys,
-                       flags, segs, n_unique, pos, pos_shift, g, W, d, grad_out);
+    hipLaunchKernelGGL((seg_walk_kernel<WEIGHT>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, keys,
+                       segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out);
+    hipLaunchKernelGGL((long_walk_kernel<WEIGHT>), dim3(64, static_cast<unsigned>((d + 511) / 512)), dim3(256), 0, st,
+                       longs, nlong, starts, pos, pos_shift, g, W, d, grad_out);
     return hip_status("gradient launch");
 }
 

@@ -40,6 +40,8 @@ def _dev(a, dt):
     ((2000,), 4001, 2560, ()),              # two-level scans (32000 sort items)
     ((1,), 7, 8, ()),
     ((50,), 3, 136, ()),                    # groups of hundreds of items (several 64-item blocks)
+    ((200,), 3, 136, (7,)),                 # groups of about 1000 items: the long-group walk
+    ((700, 333), 11, 2568, ()),             # long groups, a ragged last column block
 ])
 def test_table_grad(lengths, R, d, bad):
     say(f"grad table {lengths} R={R} d={d}")
@@ -72,7 +74,9 @@ def test_table_grad_many_items_sampled():
 
 
 @pytest.mark.parametrize("lengths,V,d,bad", [((40, 0, 57), 13, 64, ()), ((300, 7), 1024, 520, (3, 17)),
-                                             ((5000,), 151936, 128, ())])
+                                             ((5000,), 151936, 128, ()),
+                                             ((3000,), 3, 520, (5,)),         # tokens of ~1000 items: long walk
+                                             ((20000,), 151936, 2560, ())])   # prefill-like Zipf head
 def test_e1_grad(lengths, V, d, bad):
     say(f"grad e1 {lengths} V={V}")
     toks, rows, g, W = _inputs(lengths, 4096, V, d, seed=7, bad=bad)
@@ -166,12 +170,16 @@ def test_full_prefill_backward_sampled():
     U = int(nu.item())
     assert U == uniq.size and np.array_equal(gr.cpu().numpy()[:U], uniq)
     rng = np.random.default_rng(2)
-    pick = np.unique(np.concatenate([np.argsort(-cnt)[:8], rng.integers(0, U, 8)]))
+    # every row with 64 or more items (the long chains) and 1000 random rows
+    pick = np.unique(np.concatenate([np.nonzero(cnt >= 64)[0], rng.integers(0, U, 1000)]))
+    say(f"grad prefill: checking {pick.size} of {U} table rows ({int((cnt >= 64).sum())} with >= 64 items, "
+        f"longest {cnt.max()})")
     _, want = oracle.grad_table(rows, W, g, query=uniq[pick])
     assert np.array_equal(gv[torch.from_numpy(pick).cuda()].cpu().numpy().view(np.uint32), want.view(np.uint32))
-    ut = np.unique(h.tokens)
+    ut, ct = np.unique(h.tokens, return_counts=True)
     assert int(nt.item()) == ut.size and np.array_equal(gt.cpu().numpy()[:ut.size], ut)
-    tp = np.unique(np.concatenate([[0, 1, 2], rng.integers(0, ut.size, 8)]))
+    tp = np.unique(np.concatenate([[0, 1, 2], np.nonzero(ct >= 64)[0], rng.integers(0, ut.size, 200)]))
+    say(f"grad prefill: checking {tp.size} of {ut.size} e1 rows (longest {ct.max()} items)")
     _, want_e = oracle.grad_e1(h.tokens, rows, g, query=ut[tp])
     assert np.array_equal(ge[torch.from_numpy(tp).cuda()].cpu().numpy().view(np.uint32), want_e.view(np.uint32))
     check_gate(gw.cpu().numpy(), rows, g, eN, "dW_g prefill")
