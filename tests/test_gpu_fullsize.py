@@ -1,7 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times: every row id of the batch bit-exact against the oracle's
-hash, and the bf16 outputs of sampled tokens (sequence starts and ends plus
-random positions) bit-exact against the oracle run on those tokens' rows.
+hash, and the bf16 outputs of 1024 sampled tokens (plus each sequence's first
+three and last tokens) bit-exact against the oracle run on those tokens'
+rows; on tables whose fp32 sums round, the test also shows that the checked
+sums depend on the k = 0..15 order.
 
 Memory: the 20M x 2560 bf16 table is 95.4 GiB of HBM; each test frees its
 tensors before the next one allocates.
@@ -15,6 +17,7 @@ torch = pytest.importorskip("torch")
 
 import hashed_gram_embedding_ngram_amd as ng  # noqa: E402
 import oracle  # noqa: E402
+import synth  # noqa: E402
 from synth.workloads import CONFIGS, DeviceInputs, HostInputs, Spec, fill_host_table  # noqa: E402
 from tests.oracle_ref import expected, sample_tokens  # noqa: E402
 from tests.test_gpu_parity import assert_bf16_equal, bits16, say  # noqa: E402
@@ -28,9 +31,29 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def _check_forward(name):
-    sp = CONFIGS[name]
-    say(f"full size {name}: n={sp.n} R={sp.R} d={sp.d} table={sp.table}")
+def _order_observable(h, idx, rows_all):
+    """Fraction of the sampled tokens' fp32 sums that change when their 16
+    rows are added in reversed order (the oracle on both orders): how much
+    of the check below depends on the k = 0..15 order."""
+    sp = h.spec
+    rows_s = rows_all[idx]
+    uniq, inv = np.unique(rows_s, return_inverse=True)
+    remap = inv.reshape(rows_s.shape).astype(np.int32)
+    rev = np.ascontiguousarray(remap[:, ::-1])
+    Tc = h.table_rows(uniq)
+    if sp.table == "int8":
+        sc = h.scale_rows(uniq)
+        a, b = oracle.embed_bag_int8(Tc, sc, remap), oracle.embed_bag_int8(Tc, sc, rev)
+    elif sp.table == "mxfp4":
+        a, b = oracle.embed_bag_mxfp4(Tc, sp.d, remap), oracle.embed_bag_mxfp4(Tc, sp.d, rev)
+    else:
+        a, b = oracle.embed_bag_bf16(Tc, remap), oracle.embed_bag_bf16(Tc, rev)
+    return float(np.mean(a.view(np.uint32) != b.view(np.uint32)))
+
+
+def _check_forward(name, table_kind=None, m=1024, min_order_share=None):
+    sp = CONFIGS[name] if table_kind is None else CONFIGS[name].replace(table_kind=table_kind)
+    say(f"full size {name}: n={sp.n} R={sp.R} d={sp.d} table={sp.table} kind={sp.table_kind}")
     h = HostInputs(sp)
     di = DeviceInputs(sp, h)
     out = di.residual if di.residual is not None else torch.empty(sp.n * sp.d, dtype=torch.int16, device="cuda:0")
@@ -41,10 +64,14 @@ def _check_forward(name):
     got_rows = rows.cpu().numpy()
     want_rows = oracle.hash_rows(h.tokens, h.offsets, sp.R, h.history)
     assert np.array_equal(got_rows, want_rows), "row ids differ"
-    idx = sample_tokens(sp, m=96) if sp.n > 64 else np.arange(sp.n)
+    idx = sample_tokens(sp, m=m) if sp.n > m else np.arange(sp.n)
     _, _, want = expected(h, idx, rows_all=want_rows)
     got = bits16(out.view(sp.n, sp.d)[torch.from_numpy(idx).to("cuda:0")])
     assert_bf16_equal(got, want, name)
+    if min_order_share is not None:
+        share = _order_observable(h, idx, want_rows)
+        say(f"full size {name}: {idx.size} tokens checked, {share:.0%} of their sums depend on the k order")
+        assert share >= min_order_share
     del di, out, rows
     _free()
 
@@ -53,17 +80,29 @@ def test_prefill_full_size():
     _check_forward("prefill")
 
 
+def test_prefill_full_size_wide_values():
+    """The same 20M x 2560 table filled with wide-exponent bf16 values, whose
+    fp32 sums round, so the check sees the k = 0..15 order."""
+    _check_forward("prefill", table_kind=synth.KIND_BF16_WIDE, min_order_share=0.4)
+
+
 @pytest.mark.parametrize("name", ["decode1", "decode2", "decode4"])
 def test_decode_full_size(name):
     _check_forward(name)
 
 
 def test_int8_full_size():
-    _check_forward("int8")
+    """Row scales in [2^-11, 2^-10) make every fused multiply-add round, so
+    the order is observable with the workload's own table."""
+    _check_forward("int8", min_order_share=0.4)
 
 
 def test_mxfp4_full_size():
     _check_forward("fp4")
+
+
+def test_mxfp4_full_size_wide_scales():
+    _check_forward("fp4", table_kind=synth.KIND_MXFP4_WIDE, min_order_share=0.2)
 
 
 def test_host_table_full_size():
