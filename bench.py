@@ -116,6 +116,9 @@ def parse():
                     help="backward: the three gradient calls in order on one stream")
     ap.add_argument("--cpu-rows", type=int, default=1_000_000,
                     help="table rows of the host copy the CPU oracle reads")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="run only a bare random-row gather (16 rows per token of the prefill batch, reads only) "
+                         "at several row sizes and load widths: what the memory system delivers for each")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy kernel (for scaling HBM counters)")
     return ap.parse_args()
@@ -236,6 +239,9 @@ def main():
     import synth
     from synth.workloads import CONFIGS, HostInputs
 
+    if args.gather_probe:
+        run_gather_probe(args)
+        return
     if args.workload == "host":
         run_host(args)
         return
@@ -468,6 +474,83 @@ def backward_bytes_per_token(d: int, rows_per_token_unique: float, tokens_unique
     e1 reduce's read of dL/dout (2d) and write of unique-token rows
     (x 4d), and the gate gradient's read of dL/dout and eN (2d + 4d)."""
     return 16 * 2 * d + rows_per_token_unique * 4 * d + 2 * d + tokens_unique * 4 * d + 6 * d
+
+
+def run_gather_probe(args):
+    """A bare gather of the prefill batch's 16 rows per token (the same
+    hashed row ids, R = 20M) from a table of R rows of S bytes, L bytes per
+    lane, reads only (synth/libprobe.so): the rate the memory system gives
+    random rows of each size, against which the fused kernels' rates are
+    read.  S: 1360 (an MXFP4 row at d = 2560), 2560 (int8), 5120 (bf16)."""
+    import ctypes
+
+    import torch
+
+    import hashed_gram_embedding_ngram_amd as ng
+    from synth.workloads import CONFIGS, HostInputs
+
+    dev = torch.device("cuda:0")
+    spec = CONFIGS["prefill"]
+    n, R = spec.n, spec.R
+    h = HostInputs(spec)
+    rows = ng.ngram_hash(torch.from_numpy(h.tokens).to(dev), torch.from_numpy(h.offsets).to(dev), R)
+    tab = torch.empty(R * 5120, dtype=torch.uint8, device=dev)       # contents do not matter
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+    probe = ctypes.CDLL(os.path.join(ROOT, "synth", "libprobe.so"))
+    stream = torch.cuda.current_stream()
+    res = []
+    for S, L in ((1360, 4), (1360, 8), (1360, 16), (2560, 4), (2560, 8), (2560, 16), (5120, 8), (5120, 16)):
+        def go():
+            rc = probe.probe_gather(ctypes.c_void_p(tab.data_ptr()), ctypes.c_int64(S), ctypes.c_void_p(rows.data_ptr()),
+                                    ctypes.c_int64(n), ctypes.c_int32(L), ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe_gather({S}, {L}) failed: {rc}")
+        for _ in range(args.warmup):
+            go()
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record(stream)
+        for _ in range(args.steps):
+            go()
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        t = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
+        gbps = n * 16 * S / t / 1e9
+        res.append({"row_bytes": S, "lane_bytes": L, "us_per_launch": t * 1e6, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS})
+    # the fused forward's byte mix without its arithmetic: the same gather
+    # plus an e1 row (by token id, V x 5120 B), a residual row read and an
+    # output row written per token (5120 B each, d = 2560 bf16)
+    side = 2 * spec.d
+    tokens = torch.from_numpy(h.tokens).to(dev)
+    e1 = torch.empty(spec.V * side, dtype=torch.uint8, device=dev)
+    resid = torch.empty(n * side, dtype=torch.uint8, device=dev)
+    outb = torch.empty(n * side, dtype=torch.uint8, device=dev)
+    mix = []
+    for S, L in ((1360, 4), (1360, 16), (2560, 8), (5120, 16)):
+        def go():
+            rc = probe.probe_gather_mix(ctypes.c_void_p(tab.data_ptr()), ctypes.c_int64(S),
+                                        ctypes.c_void_p(rows.data_ptr()), ctypes.c_int64(n), ctypes.c_int32(L),
+                                        ctypes.c_void_p(tokens.data_ptr()), ctypes.c_void_p(e1.data_ptr()),
+                                        ctypes.c_void_p(resid.data_ptr()), ctypes.c_int64(side),
+                                        ctypes.c_void_p(outb.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe_gather_mix({S}, {L}) failed: {rc}")
+        for _ in range(args.warmup):
+            go()
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record(stream)
+        for _ in range(args.steps):
+            go()
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        t = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
+        gbps = n * (16 * S + 3 * side) / t / 1e9
+        mix.append({"row_bytes": S, "lane_bytes": L, "side_bytes": side, "us_per_launch": t * 1e6, "GBps": gbps,
+                    "frac": gbps / HBM_PEAK_GBPS})
+    print(json.dumps({"gather_probe": res, "gather_mix_probe": mix, "tokens": n, "R": R, "rows_per_token": 16}),
+          flush=True)
 
 
 def cu_masked_streams(n_side: int):
