@@ -168,6 +168,13 @@ struct Fp4Slice {
 // scalar-base vector-offset global load, with no 64-bit address per lane.
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 
+__device__ inline gbytes uniform_ptr(const void* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return reinterpret_cast<gbytes>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __device__ inline gbytes uniform_row(const void* base, int32_t r, int64_t row_bytes) {
     const uint64_t u = reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(base) + static_cast<int64_t>(r) * row_bytes);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
@@ -220,15 +227,29 @@ __device__ inline void store_out(uint16_t* o, const uint4& v) {
     *reinterpret_cast<u32x4*>(o) = w;
 }
 
+// 8 bf16 values at byte offset `off` of a row with a wave-uniform start.
+__device__ inline uint4 load_row8(gbytes row, uint32_t off) {
+    const u32x4 t = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(row + off);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ inline void store_row8(gbytes row, uint32_t off, const uint4& v) {
+    u32x4 t;
+    t.x = v.x; t.y = v.y; t.z = v.z; t.w = v.w;
+    *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(
+        const_cast<__attribute__((address_space(1))) uint8_t*>(row + off)) = t;
+}
+
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 // acc += e2m1 * 2^(E-127) for the 8 elements; the hardware conversion takes
 // the scale's exponent (exact for the power-of-two E8M0 scale, including the
-// subnormal 2^-127).  E = 255 is reported through `nan`.
-__device__ inline void add_fp4(float acc[8], const Fp4Slice& f, bool& nan) {
+// subnormal 2^-127, which ldexp gives exactly).  The largest E seen is kept
+// in `emax`: E = 255 (NaN) is applied after the sum.
+__device__ inline void add_fp4(float acc[8], const Fp4Slice& f, uint32_t& emax) {
     const uint32_t E = f.scale;
-    nan = nan || E == 255u;
-    const float s = __uint_as_float(E == 0u ? 0x00400000u : (E << 23));
+    emax = E > emax ? E : emax;
+    const float s = __builtin_ldexpf(1.0f, static_cast<int>(E) - 127);
     const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.codes, s, 0);
     const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.codes, s, 1);
     const v2f c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.codes, s, 2);
@@ -294,10 +315,10 @@ __device__ inline void gather_reduce(float acc[8], const typename Row8<DT>::Raw 
 #pragma unroll
         for (int k = 0; k < kK; ++k) fma_row(acc, v[k], s[k]);
     } else {
-        bool nan = false;
+        uint32_t emax = 0;
 #pragma unroll
-        for (int k = 0; k < kK; ++k) add_fp4(acc, v[k], nan);
-        if (nan) {
+        for (int k = 0; k < kK; ++k) add_fp4(acc, v[k], emax);
+        if (emax == 255u) {
             // a NaN term makes the in-order sum NaN
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = __uint_as_float(kNaNf32);
@@ -440,7 +461,7 @@ __device__ inline void hash_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows
 // sums, gates and stores its slices of every token of the tile.
 template <int DT, bool E1, bool RES>
 __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const int nslices = (a.d + kSlice - 1) / kSlice;
@@ -453,37 +474,42 @@ __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows,
         if (j0 >= d) continue;
         float w[8];
         load_w8(w, a.wg, j0);
+        // e1, residual and output rows are addressed as the row's uniform
+        // start plus this 32-bit lane offset (no 64-bit address per lane held
+        // across the loop: fewer registers, more wavefronts per SIMD)
+        uint32_t off2 = static_cast<uint32_t>(j0) * 2u;
+        __asm__ volatile("" : "+v"(off2));
         for (int tl = 0; tl < tile_n; ++tl) {
             const int64_t i = tile0 + tl;
-            uint16_t* o = a.out + i * d + j0;
+            const gbytes orow = uniform_ptr(a.out + i * d);
             const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
             if (c0 < 0) {
-                const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
-                *reinterpret_cast<uint4*>(o) = make_uint4(nn, nn, nn, nn);
+                uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
+                __asm__ volatile("" : "+v"(nn));    // made here, not held in registers across the loop
+                store_row8(orow, off2, make_uint4(nn, nn, nn, nn));
                 continue;
             }
             int32_t r[kK];
 #pragma unroll
             for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
-            const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
-            const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            float acc[8];
+            uint4 e = z, rv = z;
             if constexpr (DT == NGRAM_TABLE_MXFP4 && (E1 || RES)) {
                 // the e1 and residual slices do not depend on the sum: issue
                 // their loads ahead of the rows, so a token costs one memory
                 // round trip (MXFP4 runs 4 tokens per wavefront in sequence;
                 // bf16 and int8 measured no gain, nor did bf16 decode steps)
-                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-                const uint4 e = E1 ? *reinterpret_cast<const uint4*>(e1row) : z;
-                const uint4 rv = RES ? *reinterpret_cast<const uint4*>(resrow) : z;
+                if constexpr (E1) e = load_row8(uniform_row(a.e1, c0, 2 * d), off2);
+                if constexpr (RES) rv = load_row8(uniform_ptr(a.res + i * d), off2);
                 __builtin_amdgcn_sched_barrier(0);
-                float acc[8];
                 gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
-                store_out(o, gate8v<E1, RES>(acc, w, e, rv));
             } else {
-                float acc[8];
                 gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
-                store_out(o, gate8<E1, RES>(acc, w, e1row, resrow));
+                if constexpr (E1) e = load_row8(uniform_row(a.e1, c0, 2 * d), off2);
+                if constexpr (RES) rv = load_row8(uniform_ptr(a.res + i * d), off2);
             }
+            store_row8(orow, off2, gate8v<E1, RES>(acc, w, e, rv));
         }
     }
 }

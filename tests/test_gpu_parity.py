@@ -403,7 +403,7 @@ def test_row_pool(table, C):
         hb.free()
 
 
-@pytest.mark.parametrize("d", [128, 384, 2560])
+@pytest.mark.parametrize("d", [128, 384, 640, 2560])
 def test_mxfp4_table(d):
     sp = Spec(f"mxfp4_d{d}", (1, 40, 0, 200, 3), 151936, 20_011, d, table="mxfp4",
               table_kind=synth.KIND_MXFP4_WIDE, residual=True, config_id=29)
@@ -438,6 +438,40 @@ def test_mxfp4_special_scales():
     nan = np.isnan(want)
     assert np.array_equal(np.isnan(got), nan) and nan[1, :32].all() and not nan[1, 32:].any()
     assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("d", [640, 1024])
+def test_mxfp4_forward_every_scale_byte(d):
+    """The fused forward (e1 and residual) on an MXFP4 table whose scale
+    bytes take every value 0..255: E = 0 (2^-127), large exponents (sums
+    that overflow to inf, and inf - inf), and E = 255 (NaN groups), over
+    whole 512-column slices and a partial one (d = 640)."""
+    R, V, lengths = 97, 500, (1, 3, 200, 57)
+    rb = synth.mxfp4_row_bytes(d)
+    rng = np.random.default_rng(d)
+    T = rng.integers(0, 256, size=(R, rb)).astype(np.uint8)
+    T[:, d // 2:] = rng.permutation(np.resize(np.arange(256), R * (d // 32))).reshape(R, d // 32)
+    n = sum(lengths)
+    tokens = rng.integers(0, V, size=n).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    W_g = rng.standard_normal(d).astype(np.float32)
+    e1 = (rng.standard_normal((V, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    res = (rng.standard_normal((n, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    want, want_rows, want_eN = oracle.forward(tokens, offsets, T, W_g, e1=e1, residual=res, mxfp4_d=d)
+    assert np.isnan(want_eN).any() and np.isinf(want_eN).any()
+    say(f"mxfp4 forward, every scale byte: d={d} n={n}")
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).cuda()
+    out = torch.empty(n * d, dtype=torch.int16, device="cuda:0")
+    rows = torch.empty((n, 16), dtype=torch.int32, device="cuda:0")
+    ng.ngram_forward(dev(tokens, np.int32), dev(offsets, np.int32), ng.Table(dev(T.reshape(-1), np.uint8), R, d,
+                     ng.TABLE_MXFP4), dev(W_g, np.float32), out, e1=dev(e1, np.int16),
+                     residual=dev(res, np.int16), rows_out=rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(rows.cpu().numpy(), want_rows)
+    got = bits16(out).reshape(n, d)
+    nan = (want & 0x7FFF) > 0x7F80
+    assert np.array_equal((got & 0x7FFF) > 0x7F80, nan)
+    assert np.array_equal(got[~nan], want[~nan])
 
 
 @pytest.mark.parametrize("d", [128, 2560])
