@@ -54,6 +54,7 @@ def lib():
         L.oracle_bf16_rne_f64.restype = ctypes.c_uint16
         L.oracle_bf16_rne_f64.argtypes = [ctypes.c_double]
         L.oracle_norm_gate_add.argtypes = [P, P, I64, I32, P, P, P, P, P, F, F, P, P, P, P]
+        L.oracle_project.argtypes = [P, I64, I32, P, I32, P, P]
         _lib = L
     return _lib
 
@@ -241,3 +242,19 @@ def norm_gate_add(eN, e1_rows, e1, W_g, gamma, u, v, b, eps, residual=None):
                                _p(_c(v, np.float32)), float(np.float32(b)), float(np.float32(eps)),
                                _p(_c(residual, np.uint16)), _p(out), _p(stats), _p(y))
     return out, stats, y
+
+
+def project(x, P):
+    """Projection of the sums x [n][d_in] (fp32) by the bf16 weights P
+    [d_out][d_in] (uint16 bits), x rounded to bf16 first; evaluated in
+    float64.  Returns (y float64 [n][d_out], sum of |terms| float64
+    [n][d_out])."""
+    x = _c(x, np.float32)
+    P = _c(P, np.uint16)
+    n, d_in = x.shape
+    d_out = P.shape[0]
+    assert P.shape[1] == d_in
+    y = np.zeros((n, d_out), dtype=np.float64)
+    a = np.zeros((n, d_out), dtype=np.float64)
+    lib().oracle_project(_p(x), n, d_in, _p(P), d_out, _p(y), _p(a))
+    return y, a

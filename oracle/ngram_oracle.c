@@ -408,3 +408,38 @@ void oracle_norm_gate_add(const float* eN, const int32_t* e1_rows, int64_t n, in
     }
     free(nv);
 }
+
+/*
+ * Projection.  "Qwen 3.8 Flash-Next Deep Dive…" draws a "Projection /
+ * Normalization" stage between the table lookup and the trunk and does not
+ * define it.  Form taken: a learned linear map of each token's n-gram sum x
+ * (d_in columns) to d_out columns, with the weights P [d_out][d_in] stored
+ * as bf16 (the model's storage type) and x rounded to bf16 first, ties to
+ * even (the pages fix no precision):
+ *   y[i][o] = sum over j of P[o][j] * bf16(x[i][j]).
+ * A product of two bf16 values has at most 16 significant bits, so each term
+ * is exact in float64; the sum is taken over ascending j in float64.
+ * abs_out (may be NULL) receives the sum of |terms| per output, the scale of
+ * the error of any other order of the same sum.
+ */
+void oracle_project(const float* x, int64_t n, int32_t d_in, const uint16_t* P, int32_t d_out,
+                    double* y_out, double* abs_out)
+{
+    double* xb = (double*)malloc(sizeof(double) * (size_t)(d_in > 0 ? d_in : 1));
+    for (int64_t i = 0; i < n; ++i) {
+        for (int32_t j = 0; j < d_in; ++j)
+            xb[j] = (double)oracle_bf16_to_f32(oracle_bf16_rne(x[i * d_in + j]));
+        for (int32_t o = 0; o < d_out; ++o) {
+            double acc = 0.0, a = 0.0;
+            for (int32_t j = 0; j < d_in; ++j) {
+                const double t = (double)oracle_bf16_to_f32(P[(int64_t)o * d_in + j]) * xb[j];
+                acc = acc + t;
+                a = a + fabs(t);
+            }
+            y_out[i * d_out + o] = acc;
+            if (abs_out)
+                abs_out[i * d_out + o] = a;
+        }
+    }
+    free(xb);
+}

@@ -88,17 +88,26 @@ MUTATIONS = {
     "bf16f64_ties_away": ("(a > mid || (a == mid && odd))", "(a >= mid)"),
     "bf16f64_truncates": ("const double r = (a > mid || (a == mid && odd)) ? hi : lo;", "const double r = lo;"),
     "bf16f64_spacing_off_by_one": ("int qe = e - 8;", "int qe = e - 9;"),
+    "project_no_bf16_round": ("xb[j] = (double)oracle_bf16_to_f32(oracle_bf16_rne(x[i * d_in + j]));",
+                              "xb[j] = (double)x[i * d_in + j];"),
+    "project_transposed": ("oracle_bf16_to_f32(P[(int64_t)o * d_in + j])", "oracle_bf16_to_f32(P[(int64_t)j * d_out + o])"),
+    "project_skips_last_term": ("for (int32_t j = 0; j < d_in; ++j) {\n                const double t",
+                                "for (int32_t j = 0; j + 1 < d_in; ++j) {\n                const double t"),
+    "project_float_accumulator": ("acc = acc + t;", "acc = (float)(acc + t);"),
+    "project_abs_signed": ("a = a + fabs(t);", "a = a + t;"),
+    "project_wrong_x_row": ("oracle_bf16_rne(x[i * d_in + j])", "oracle_bf16_rne(x[((i + 1) % n) * d_in + j])"),
 }
 
 
 ALL_PINS = ["tests/test_oracle_hash.py", "tests/test_oracle_sum_gate.py", "tests/test_oracle_grad.py",
-            "tests/test_oracle_mxfp4.py", "tests/test_oracle_norm_gate.py"]
+            "tests/test_oracle_mxfp4.py", "tests/test_oracle_norm_gate.py", "tests/test_oracle_project.py"]
 
 
 def pins_for(name):
     """The pin file of the function a mutation hits (so each run imports only
     what it needs); the whole set for anything else."""
     for prefix, f in (("grad_", "test_oracle_grad.py"), ("mxfp4_", "test_oracle_mxfp4.py"),
+                      ("project_", "test_oracle_project.py"),
                       ("e2m1_", "test_oracle_mxfp4.py"), ("norm_", "test_oracle_norm_gate.py"),
                       ("bf16f64_", "test_oracle_norm_gate.py"), ("gate_z_", "test_oracle_norm_gate.py"),
                       ("gate_sign", "test_oracle_norm_gate.py"), ("gate_uv", "test_oracle_norm_gate.py"),
