@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "int8", "fp4", "gated", "decode1", "decode2", "decode4", "host",
+                    choices=["prefill", "int8", "fp4", "gated", "projected", "decode1", "decode2", "decode4", "host",
                              "backward"])
     ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged", "async", "pool"],
                     help="host workload: sum straight from pinned memory; stage the distinct rows in HBM first, "
@@ -247,6 +247,9 @@ def main():
         return
     if args.workload == "backward":
         run_backward(args)
+        return
+    if args.workload == "projected":
+        run_projected(args)
         return
 
     dev = torch.device("cuda:0")
@@ -551,6 +554,164 @@ def run_gather_probe(args):
                     "frac": gbps / HBM_PEAK_GBPS})
     print(json.dumps({"gather_probe": res, "gather_mix_probe": mix, "tokens": n, "R": R, "rows_per_token": 16}),
           flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
+
+
+def run_projected(args):
+    """The projected path at the prefill shape: hash, gather-sum (the fp32
+    sums rounded to bf16), projection by a 2560 x 2560 bf16 weight (bf16
+    MFMA, fp32 accumulation),
+    then the normalised, input-gated epilogue with the residual in place.  A
+    step is the four launches on one stream; each launch is timed with HIP
+    events.  The roofline object is the projection's (matrix-core bound: 2
+    n d_in d_out flops per launch against the dense bf16 peak)."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import hashed_gram_embedding_ngram_amd as ng
+    import synth
+    from synth.workloads import CONFIGS, HostInputs, gate_params
+
+    dev = torch.device("cuda:0")
+    spec = CONFIGS["prefill"].replace(dist=args.dist)
+    n, d = spec.n, spec.d
+    t_setup = time.time()
+    h = HostInputs(spec)
+    s0 = spec.seed
+    table = synth.fill_gpu(spec.table_kind, s0, synth.TAG_TABLE, torch.empty(spec.R * d, dtype=torch.int16, device=dev))
+    T = ng.Table(table, spec.R, d)
+    e1 = synth.fill_gpu(synth.KIND_BF16_NORMAL12, s0, synth.TAG_E1, torch.empty(spec.V * d, dtype=torch.int16, device=dev))
+    W_g = torch.from_numpy(h.W_g).to(dev)
+    gp = gate_params(spec)
+    g_gamma, g_u, g_v = (torch.from_numpy(a).to(dev) for a in (gp.gamma, gp.u, gp.v))
+    w = (np.random.default_rng(s0).standard_normal((d, d)) / np.sqrt(d)).astype(np.float32)
+    P = torch.from_numpy((w.view(np.uint32) >> 16).astype(np.uint16).view(np.int16)).to(dev)
+    tok = torch.from_numpy(h.tokens).to(dev)
+    off = torch.from_numpy(h.offsets).to(dev)
+    res = synth.fill_gpu(synth.KIND_BF16_NORMAL6, s0, synth.TAG_RESIDUAL, torch.empty(n * d, dtype=torch.int16, device=dev))
+    rows = torch.empty((n, K_ROWS), dtype=torch.int32, device=dev)
+    xb = torch.empty((n, d), dtype=torch.int16, device=dev)
+    p = torch.empty((n, d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    stream = torch.cuda.current_stream()
+    names = ["hash", "embed_bag_bf16", "project", "norm_gate_add"]
+
+    def stages():
+        return [lambda: ng.ngram_hash(tok, off, spec.R, rows_out=rows, stream=stream),
+                lambda: ng.ngram_embed_bag_bf16(T, rows, out=xb, stream=stream),
+                lambda: ng.ngram_project(xb, P, y=p, stream=stream),
+                lambda: ng.ngram_norm_gate_add(p, tok, e1, W_g, g_gamma, g_u, g_v, gp.b, gp.eps, res, residual=res,
+                                               stream=stream)]
+
+    fns = stages()
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for k, f in enumerate(fns):
+            f()
+            ev[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {nm: statistics.mean(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)) * 1e3
+           for k, nm in enumerate(names)}
+    proj_s = per["project"] / 1e6
+    flops = 2.0 * n * d * d
+    achieved = flops / proj_s / 1e12
+    result = {
+        "metric": METRIC,
+        "value": n * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x bf16 -> f32 (projection), f32/f64 elsewhere",
+        "data": "synthetic",
+        "config": {"workload": "projected", "tokens": n, "sequences": len(spec.lengths), "R": spec.R, "d": d,
+                   "d_out": d, "K": K_ROWS, "table_dtype": spec.table, "vocab": spec.V,
+                   "token_dist": f"zipf({spec.zipf_s})" if args.dist == "zipf" else "uniform",
+                   "residual_in_place": True},
+        "stage_us": per,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "kernel": "project_kernel",
+            "algorithmic_flops_per_launch": flops,
+            "mean_launch_us": per["project"],
+        },
+        "setup_s": setup_s,
+        "cpu_baseline": None if args.no_cpu_baseline else projected_cpu_baseline(h, table, e1, res, P, gp, spec),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def projected_cpu_baseline(h, table, e1, res, P, gp, spec, m=256, repeats=5):
+    """The oracle's projected path (hash, sum, float64 projection, normalised
+    gated fusion) on the first m tokens of the batch, rows hashed into a host
+    copy of the first 1,000,000 table rows, one piece of m / 16 tokens per
+    thread; median of ``repeats`` passes, and of ``repeats`` passes on 1 core."""
+    import concurrent.futures as cf
+    import statistics
+
+    import numpy as np
+
+    import oracle
+
+    d = spec.d
+    R_cpu = 1_000_000
+    tp = time.time()
+    table_np = table[: R_cpu * d].cpu().numpy().view(np.uint16).reshape(R_cpu, d)
+    e1_np = e1.cpu().numpy().view(np.uint16).reshape(spec.V, d)
+    res_np = res[: m * d].cpu().numpy().view(np.uint16).reshape(m, d)
+    P_np = P.cpu().numpy().view(np.uint16)
+    prep = time.time() - tp
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    step = (m + threads - 1) // threads
+    toks = h.tokens[:m]
+    pieces = [(a, min(m, a + step)) for a in range(0, m, step)]
+
+    def one(piece):
+        a, b = piece
+        hist = None if a == 0 else np.array([[toks[a - 2] if a >= 2 else (1 << 21) - 1, toks[a - 1]]], np.int32)
+        rows = oracle.hash_rows(toks[a:b], np.array([0, b - a], np.int32), R_cpu, hist)
+        eN = oracle.embed_bag_bf16(table_np, rows)
+        y, _ = oracle.project(eN, P_np)
+        oracle.norm_gate_add(y.astype(np.float32), toks[a:b], e1_np, h.W_g, gp.gamma, gp.u, gp.v, gp.b, gp.eps,
+                             res_np[a:b])
+        return b - a
+
+    def timed(work, nthreads):
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            done = sum(ex.map(one, work))
+        return done / (time.perf_counter() - t0)
+
+    rate_all = [timed(pieces, threads) for _ in range(repeats)]
+    rate_one = [timed(pieces[:1], 1) for _ in range(repeats)]
+    return {"value": statistics.median(rate_all), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"the first {m} tokens of the batch in {len(pieces)} pieces (oracle hash, sum, float64 "
+                       f"projection by the {d} x {d} weight, normalised gated fusion), rows hashed mod {R_cpu} into "
+                       f"a host copy of the first {R_cpu} table rows; median of {repeats} passes; prep {prep:.1f} s"),
+            "single_core": {"value": statistics.median(rate_one), "unit": "tokens/s", "cores": 1,
+                            "sample": f"the first piece ({pieces[0][1]} tokens), median of {repeats} passes"},
+            "cpu_model": _cpu_model()}
 
 
 def cu_masked_streams(n_side: int):

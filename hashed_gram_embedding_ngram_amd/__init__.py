@@ -66,6 +66,10 @@ _SIGNATURES = {
     "ngram_forward_gated_ex": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, ctypes.POINTER(_Table), _P, _I64,
                                               _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P,
                                               ctypes.POINTER(_Launch), _P]),
+    "ngram_norm_gate_add": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, ctypes.c_float,
+                                           ctypes.c_float, _P, _P, _P, _P]),
+    "ngram_project": (ctypes.c_int, [_P, _I64, _I32, _P, _I32, _P, _P]),
+    "ngram_embed_bag_bf16": (ctypes.c_int, [ctypes.POINTER(_Table), _P, _I64, _P, _P]),
     "ngram_host_alloc": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
     "ngram_host_free": (ctypes.c_int, [_P]),
     "ngram_gather_host_workspace_bytes": (ctypes.c_int64, [_I64, _I32]),
@@ -355,6 +359,61 @@ def ngram_forward_gated(tokens, seq_offsets, table: Table, W_g, gamma, u, v, b, 
         rc = lib().ngram_forward_gated_ex(*args, _launch_arg(launch), _stream(stream))
     _check(rc, "ngram_forward_gated")
     return out
+
+
+def ngram_norm_gate_add(eN, tokens, e1, W_g, gamma, u, v, b, eps, out, residual=None, stats_out=None,
+                        stream=None):
+    """The normalised, input-gated epilogue on given fp32 sums eN [n][d]
+    (see ngram_norm_gate_add in ngram.h)."""
+    _dev(eN, _F32, "eN")
+    _dev(tokens, _I32T, "tokens")
+    for t, name in ((W_g, "W_g"), (gamma, "gamma"), (u, "u"), (v, "v")):
+        _dev(t, _F32, name)
+    _dev(out, _BF16, "out")
+    _dev(e1, _BF16, "e1")
+    _dev(residual, _BF16, "residual", allow_none=True)
+    _dev(stats_out, (torch.float64,), "stats_out", allow_none=True)
+    n, d = eN.shape
+    V = _vocab(e1, d)
+    _need(tokens, n, "tokens")
+    for t, name in ((W_g, "W_g"), (gamma, "gamma"), (u, "u"), (v, "v")):
+        _need(t, d, name)
+    _need(out, n * d, "out")
+    _need(residual, n * d, "residual")
+    _need(stats_out, 2 * n, "stats_out")
+    _check(lib().ngram_norm_gate_add(_ptr(eN), _ptr(tokens), n, d, _ptr(e1), V, _ptr(W_g), _ptr(gamma), _ptr(u),
+                                     _ptr(v), float(b), float(eps), _ptr(residual), _ptr(out), _ptr(stats_out),
+                                     _stream(stream)), "ngram_norm_gate_add")
+    return out
+
+
+def ngram_embed_bag_bf16(table: Table, rows, out=None, stream=None):
+    """The sums of ngram_embed_bag rounded to bf16: out [n][d] (bf16 bits)."""
+    _dev(rows, _I32T, "rows")
+    n = rows.shape[0]
+    if out is None:
+        out = torch.empty((n, table.d), dtype=torch.int16, device=rows.device)
+    _dev(out, _BF16, "out")
+    _need(out, n * table.d, "out")
+    _check(lib().ngram_embed_bag_bf16(table.c, _ptr(rows), n, _ptr(out), _stream(stream)), "ngram_embed_bag_bf16")
+    return out
+
+
+def ngram_project(x, P, y=None, stream=None):
+    """y [n][d_out] fp32 = P x for x [n][d_in] and P [d_out][d_in], both bf16
+    bits (int16 tensors); see ngram_project in ngram.h."""
+    _dev(x, _BF16, "x")
+    _dev(P, _BF16, "P")
+    n, d_in = x.shape
+    d_out = P.shape[0]
+    if P.dim() != 2 or P.shape[1] != d_in:
+        raise NgramError(f"P must be [d_out][{d_in}], got {tuple(P.shape)}")
+    if y is None:
+        y = torch.empty((n, d_out), dtype=torch.float32, device=x.device)
+    _dev(y, _F32, "y")
+    _need(y, n * d_out, "y")
+    _check(lib().ngram_project(_ptr(x), n, d_in, _ptr(P), d_out, _ptr(y), _stream(stream)), "ngram_project")
+    return y
 
 
 GATHER_ZERO_COPY = 0

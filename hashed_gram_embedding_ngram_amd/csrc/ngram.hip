@@ -531,6 +531,7 @@ __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows,
 // wavefronts' sums meet in LDS.
 struct GatedArgs {
     FwdArgs f;
+    const float* eN;    // MODE 3: the fp32 sums [n][d], read instead of gathered
     const float* gamma;
     const float* u;
     const float* v;
@@ -599,7 +600,7 @@ __device__ inline uint32_t bf16_rne_f64(double x) {
 // so every wavefront reaches the same barriers.  ONE: the tile is one token,
 // so there is no token loop (a loop lets the compiler keep loop-invariant
 // float64 constants of exp in registers through the gather).
-template <int DT, bool RES, bool FULL, bool ONE>
+template <int DT, bool RES, bool FULL, bool ONE, bool LOADED = false>
 __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lrows, int32_t* ltok, double* lred) {
     const FwdArgs& a = g.f;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -607,13 +608,20 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
     const int64_t d = a.d;
     const uint32_t jl = static_cast<uint32_t>(wave * kSlice + lane * kVec);   // the lane's first column
     const bool col = FULL || jl < static_cast<uint32_t>(d);  // FULL: d a multiple of 512, all lanes have columns
-    hash_tile(a, tile0, lrows, ltok, lrows + a.tpw * (kK + 1));
+    if constexpr (!LOADED) hash_tile(a, tile0, lrows, ltok, lrows + a.tpw * (kK + 1));
 
     const int64_t rem = a.n - tile0;
     const int tile_n = ONE ? 1 : (rem < a.tpw ? static_cast<int>(rem) : a.tpw);
     for (int tl = 0; tl < tile_n; ++tl) {
         const int64_t i = tile0 + tl;
-        const int32_t c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
+        int32_t c0;
+        if constexpr (LOADED) {
+            // the token's e1 row; an id outside [0, V) makes the token invalid
+            const uint32_t t = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(a.tok[i]));
+            c0 = t < a.c0_limit ? static_cast<int32_t>(t) : -1;
+        } else {
+            c0 = __builtin_amdgcn_readfirstlane(ltok[tl]);
+        }
         if (c0 < 0) {
             if (col) {
                 const uint32_t nn = kNaNbf16 | (kNaNbf16 << 16);
@@ -632,12 +640,19 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
         // too costs 13 registers and two wavefronts per SIMD, 4% slower)
         uint4 e1v = make_uint4(0u, 0u, 0u, 0u), rv = e1v;
         if (col) {
-            int32_t r[kK];
-#pragma unroll
-            for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
             e1v = load_row8(uniform_row(a.e1, c0, 2 * d), 2u * jl);
-            __builtin_amdgcn_sched_barrier(0);
-            gather_sum<DT>(acc, a.tab, a.scale, r, d, jl);
+            if constexpr (LOADED) {
+                const float4 x0 = *reinterpret_cast<const float4*>(g.eN + i * d + jl);
+                const float4 x1 = *reinterpret_cast<const float4*>(g.eN + i * d + jl + 4);
+                acc[0] = x0.x; acc[1] = x0.y; acc[2] = x0.z; acc[3] = x0.w;
+                acc[4] = x1.x; acc[5] = x1.y; acc[6] = x1.z; acc[7] = x1.w;
+            } else {
+                int32_t r[kK];
+#pragma unroll
+                for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
+                __builtin_amdgcn_sched_barrier(0);
+                gather_sum<DT>(acc, a.tab, a.scale, r, d, jl);
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
@@ -711,7 +726,8 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
 }
 
 // MODE 0: one token per workgroup; 1: one tile of tpw tokens per workgroup;
-// 2: a capped grid loops over the tiles (tables in host memory).
+// 2: a capped grid loops over the tiles (tables in host memory); 3: one
+// token per workgroup whose fp32 sum is read from g.eN (no hash, no gather).
 template <int DT, bool RES, bool FULL, int MODE>
 __global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
     extern __shared__ int32_t lds[];
@@ -723,6 +739,8 @@ __global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
     int32_t* ltok = lrows + g.f.tpw * kK;
     if constexpr (MODE == 0) {
         gated_tile<DT, RES, FULL, true>(g, static_cast<int64_t>(blockIdx.x), lrows, ltok, lred);
+    } else if constexpr (MODE == 3) {
+        gated_tile<DT, RES, FULL, true, true>(g, static_cast<int64_t>(blockIdx.x), lrows, ltok, lred);
     } else if constexpr (MODE == 1) {
         gated_tile<DT, RES, FULL, false>(g, static_cast<int64_t>(blockIdx.x) * g.f.tpw, lrows, ltok, lred);
     } else {
@@ -789,6 +807,7 @@ struct BagArgs {
     const float* scale;
     const int32_t* rows;
     float* eN;
+    uint16_t* eN16;     // bf16 output instead of eN (the sums rounded to nearest, ties to even)
     int64_t n;
     int64_t R;
     int32_t d;
@@ -817,7 +836,6 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
         const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
         if (j0 >= d) continue;
         for (int tl = 0; tl < tile_n; ++tl) {
-            float* o = a.eN + (tile0 + tl) * d + j0;
             int32_t r[kK];
             bool ok = true;
 #pragma unroll
@@ -832,8 +850,18 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
             }
-            reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+            if (a.eN16) {
+                uint4 w;
+                w.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
+                w.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+                w.z = bf16_rne(acc[4]) | (bf16_rne(acc[5]) << 16);
+                w.w = bf16_rne(acc[6]) | (bf16_rne(acc[7]) << 16);
+                *reinterpret_cast<uint4*>(a.eN16 + (tile0 + tl) * d + j0) = w;
+            } else {
+                float* o = a.eN + (tile0 + tl) * d + j0;
+                reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+            }
         }
     }
 }
@@ -887,6 +915,152 @@ __global__ void __launch_bounds__(256) ngram_gate_kernel(const GateArgs a) {
     const uint16_t* e1row = E1 ? a.e1 + static_cast<int64_t>(c0) * d + j0 : nullptr;
     const uint16_t* resrow = RES ? a.res + i * d + j0 : nullptr;
     *reinterpret_cast<uint4*>(o) = gate8<E1, RES>(acc, w, e1row, resrow);
+}
+
+// ---------------------------------------------------------------------------
+// Projection: y[i][o] = sum over j of P[o][j] * x[i][j] for bf16 x and P
+// ("Qwen 3.8 Flash-Next Deep Dive…", section 1: a "Projection /
+// Normalization" stage after the lookup; the form is taken, the page does
+// not define it).  A dense contraction, so it runs on the matrix cores:
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation of exact bf16 products).
+// A workgroup of 8 wavefronts owns a 256 x 256 tile of y (wavefront w: rows
+// 128 (w >> 2), columns 64 (w & 3), as 4 x 2 MFMA tiles of 32 x 32) and walks
+// K in steps of 64 through two LDS buffers.  Operands go from global memory
+// straight into LDS (global_load_lds_dwordx4: lane L's 16 bytes land at the
+// instruction's LDS base + 16 L), so they hold no registers on the way.  In
+// each step a wavefront first reads all its operand fragments of the step
+// from LDS, then issues the next step's loads into the other buffer, then
+// runs its 32 MFMAs; it waits for its own loads and the workgroup barrier
+// closes the step.
+// LDS rows are 64 bf16 (128 bytes, eight 16-byte chunks); chunk c of row r is
+// stored at position c ^ ((r >> 1) & 7), so the 16 rows a 16-lane group of an
+// operand read touches fall on 16 different 16-byte bank groups.  A load
+// instruction fills 8 rows (1 KiB): lane L writes row L >> 3, position L & 7,
+// so it fetches chunk (L & 7) ^ f(row) of that row.
+// Tiles are ordered row-tile major and handed out XCD by XCD: workgroup b
+// runs on XCD b mod 8, and the tiles of XCD x are a contiguous run of the
+// order, so the column tiles of one row tile share that XCD's L2 for x.
+constexpr int kPM = 256, kPN = 256, kPK = 64, kPThreads = 512;
+constexpr int kPTile = kPM * kPK * 2;                  // bytes of one operand tile of one step (x or P)
+constexpr int kPStage = 2 * kPTile;                    // one LDS buffer: x tile then P tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct ProjArgs {
+    const uint16_t* x;     // [n][K] bf16
+    const uint16_t* P;     // [N][K] bf16
+    float* y;              // [n][N] fp32
+    int64_t n;
+    int32_t K;
+    int32_t N;
+    int32_t ntiles_n;      // ceil(N / 256)
+    int32_t ntiles;        // all tiles
+};
+
+__device__ inline uint32_t proj_pos(int row, int c) {
+    return static_cast<uint32_t>(row) * (kPK * 2) + (static_cast<uint32_t>(c ^ ((row >> 1) & 7)) << 4);
+}
+
+// The step's 256-row x and P tiles into LDS buffer `buf`: 32 + 32
+// instructions of 8 rows each, 4 + 4 per wavefront.  `xrow`, `prow`: the
+// lane's source row pointers for its 4 row groups (rows past n or N are
+// clamped to the last row: their results are never stored).
+__device__ inline void proj_issue(uint8_t* buf, const uint16_t* const xrow[4], const uint16_t* const prow[4],
+                                  const uint32_t chunk[4], int wave, int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int g = 4 * wave + q;                       // row group: rows 8 g .. 8 g + 7
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(xrow[q] + k0 + 8 * chunk[q]),
+            (__attribute__((address_space(3))) void*)(buf + g * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(prow[q] + k0 + 8 * chunk[q]),
+            (__attribute__((address_space(3))) void*)(buf + kPTile + g * 1024), 16, 0, 0);
+    }
+}
+
+__global__ void __launch_bounds__(kPThreads, 1) project_kernel(const ProjArgs a) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t plds[];   // [2][x 256 rows | P 256 rows] x 128 B
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    // XCD-aware tile order: tiles of XCD b mod 8 form a contiguous run
+    const int b = blockIdx.x, per = (a.ntiles + 7) / 8, xcd = b & 7, slot = b >> 3;
+    const int full_xcds = a.ntiles - 8 * (per - 1);      // XCDs that get `per` tiles; the rest get per - 1
+    if (slot >= (xcd < full_xcds ? per : per - 1)) return;
+    const int tile = xcd < full_xcds ? xcd * per + slot : full_xcds * per + (xcd - full_xcds) * (per - 1) + slot;
+    const int mt = tile / a.ntiles_n, nt = tile - mt * a.ntiles_n;
+    const int64_t m0 = static_cast<int64_t>(mt) * kPM;
+    const int n0 = nt * kPN;
+    const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+    // the lane's load sources: row 8 (4 wave + q) + (lane >> 3), chunk (lane & 7) ^ f(row)
+    const uint16_t* xrow[4];
+    const uint16_t* prow[4];
+    uint32_t chunk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = 8 * (4 * wave + q) + (lane >> 3);
+        const int64_t xr = m0 + r < a.n ? m0 + r : a.n - 1;
+        const int pr = n0 + r < a.N ? n0 + r : a.N - 1;
+        xrow[q] = a.x + xr * a.K;
+        prow[q] = a.P + static_cast<int64_t>(pr) * a.K;
+        chunk[q] = static_cast<uint32_t>((lane & 7) ^ ((r >> 1) & 7));
+    }
+    const int KT = a.K / kPK;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[sm][sn][e] = 0.0f;
+
+    proj_issue(plds, xrow, prow, chunk, wave, 0);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const uint8_t* xs = plds + (kt & 1) * kPStage;
+        const uint8_t* ps = xs + kPTile;
+        // all operand fragments of the step: lane L holds k = 16 kk + 8 (L >> 5)
+        // .. +7 of row L & 31 of each 32-row operand tile
+        bf16x8 af[4][4], bf[4][2];
+#pragma unroll
+        for (int kk = 0; kk < kPK / 16; ++kk) {
+            const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                af[kk][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + proj_pos(wm + 32 * s + (lane & 31), c)));
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                bf[kk][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ps + proj_pos(wn + 32 * s + (lane & 31), c)));
+        }
+        if (kt + 1 < KT) proj_issue(plds + ((kt + 1) & 1) * kPStage, xrow, prow, chunk, wave, (kt + 1) * kPK);
+#pragma unroll
+        for (int kk = 0; kk < kPK / 16; ++kk)
+#pragma unroll
+            for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+                for (int sn = 0; sn < 2; ++sn)
+                    acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][sm], bf[kk][sn], acc[sm][sn], 0, 0, 0);
+        // the MFMAs stay ahead of the wait, so the loads land while they run
+        __builtin_amdgcn_sched_barrier(0);
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    // lane L holds rows 8 (e >> 2) + 4 (L >> 5) + (e & 3), column L & 31 of each 32 x 32 tile
+#pragma unroll
+    for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) {
+            const int col = n0 + wn + 32 * sn + (lane & 31);
+            if (col >= a.N) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = m0 + wm + 32 * sm + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (row < a.n) a.y[row * a.N + col] = acc[sm][sn][e];
+            }
+        }
 }
 
 // Zero-copy staging of host-table rows: one wavefront per (token, k) row,
@@ -2043,6 +2217,43 @@ int scratch_address(void** out) {
     return NGRAM_OK;
 }
 
+// ngram_embed_bag and ngram_embed_bag_bf16: the sums to fp32 or to bf16.
+int embed_bag_any(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out, uint16_t* eN16_out,
+                  const ngram_launch* launch, ngram_stream_t stream) {
+    int rc = check_table(T);
+    if (rc) return rc;
+    rc = check_launch(launch);
+    if (rc) return rc;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > INT32_MAX) return fail(NGRAM_ERANGE, "n=%lld above 2^31-1", (long long)n);
+    if (n > 0 && !rows) return fail(NGRAM_EINVAL, "rows is NULL");
+    if (n > 0 && !aligned(eN_out ? static_cast<const void*>(eN_out) : eN16_out, 16))
+        return fail(NGRAM_EALIGN, "output not 16-byte aligned");
+    if (n == 0) return NGRAM_OK;
+    const void* tab = nullptr;
+    rc = table_device_ptr(T, &tab);
+    if (rc) return rc;
+    BagArgs a;
+    a.tab = tab; a.scale = T->row_scale; a.rows = rows; a.eN = eN_out; a.eN16 = eN16_out;
+    a.n = n; a.R = T->R; a.d = T->d;
+    Shape sh = slice_shape(n, T->d, T->dtype, launch);
+    cap_for_host(sh, T, launch);
+    a.tpw = sh.tpw;
+    const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * sh.waves);
+    const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
+    if (T->dtype == NGRAM_TABLE_BF16) {
+        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, false>), grid, block, lds, stream, a);
+    } else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) {
+        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, false>), grid, block, lds, stream, a);
+    } else {
+        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, false>), grid, block, lds, stream, a);
+    }
+    return hip_status("ngram_embed_bag launch");
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -2096,38 +2307,17 @@ int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float*
 int ngram_embed_bag_ex(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
                        const ngram_launch* launch, ngram_stream_t stream) {
     g_err[0] = 0;
-    int rc = check_table(T);
-    if (rc) return rc;
-    rc = check_launch(launch);
-    if (rc) return rc;
-    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
-    if (n > INT32_MAX) return fail(NGRAM_ERANGE, "n=%lld above 2^31-1", (long long)n);
-    if (n > 0 && (!rows || !eN_out)) return fail(NGRAM_EINVAL, "rows or eN_out is NULL");
-    if (n > 0 && !aligned(eN_out, 16)) return fail(NGRAM_EALIGN, "eN_out not 16-byte aligned");
-    if (n == 0) return NGRAM_OK;
-    const void* tab = nullptr;
-    rc = table_device_ptr(T, &tab);
-    if (rc) return rc;
-    BagArgs a;
-    a.tab = tab; a.scale = T->row_scale; a.rows = rows; a.eN = eN_out;
-    a.n = n; a.R = T->R; a.d = T->d;
-    Shape sh = slice_shape(n, T->d, T->dtype, launch);
-    cap_for_host(sh, T, launch);
-    a.tpw = sh.tpw;
-    const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * sh.waves);
-    const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
-    if (T->dtype == NGRAM_TABLE_BF16) {
-        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, false>), grid, block, lds, stream, a);
-    } else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) {
-        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, false>), grid, block, lds, stream, a);
-    } else {
-        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, false>), grid, block, lds, stream, a);
-    }
-    return hip_status("ngram_embed_bag launch");
+    if (n > 0 && !eN_out) return fail(NGRAM_EINVAL, "eN_out is NULL");
+    return embed_bag_any(T, rows, n, eN_out, nullptr, launch, stream);
 }
+
+int ngram_embed_bag_bf16(const ngram_table* T, const int32_t* rows, int64_t n, uint16_t* out,
+                         ngram_stream_t stream) {
+    g_err[0] = 0;
+    if (n > 0 && !out) return fail(NGRAM_EINVAL, "out is NULL");
+    return embed_bag_any(T, rows, n, nullptr, out, nullptr, stream);
+}
+
 
 int ngram_gate_add(const float* eN, const int32_t* tokens, int64_t n, int32_t d,
                    const uint16_t* e1, int64_t V, const float* W_g, const uint16_t* residual,
@@ -2154,6 +2344,65 @@ int ngram_gate_add(const float* eN, const int32_t* tokens, int64_t n, int32_t d,
     else if (residual) hipLaunchKernelGGL((ngram_gate_kernel<false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((ngram_gate_kernel<false, false>), grid, block, 0, stream, a);
     return hip_status("ngram_gate_add launch");
+}
+
+int ngram_project(const uint16_t* x, int64_t n, int32_t d_in, const uint16_t* P, int32_t d_out, float* y,
+                  ngram_stream_t stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (d_in <= 0 || d_in % kPK != 0 || d_out <= 0 || d_out % kVec != 0)
+        return fail(NGRAM_EINVAL, "d_in=%d must be a positive multiple of %d and d_out=%d of %d", d_in, kPK, d_out, kVec);
+    if (d_in > NGRAM_MAX_D || d_out > NGRAM_MAX_D)
+        return fail(NGRAM_ERANGE, "d_in=%d or d_out=%d above %d", d_in, d_out, NGRAM_MAX_D);
+    if (!P) return fail(NGRAM_EINVAL, "P is NULL");
+    if (n > 0 && (!x || !y)) return fail(NGRAM_EINVAL, "x or y is NULL");
+    if (!aligned(P, 16) || (n > 0 && (!aligned(x, 16) || !aligned(y, 16))))
+        return fail(NGRAM_EALIGN, "x, P and y must be 16-byte aligned");
+    const int64_t mtiles = (n + kPM - 1) / kPM, ntiles = (d_out + kPN - 1) / kPN;
+    if (mtiles * ntiles > INT32_MAX / 2) return fail(NGRAM_ERANGE, "n=%lld too large for one launch", (long long)n);
+    if (n == 0) return NGRAM_OK;
+    ProjArgs a;
+    a.x = x; a.P = P; a.y = y; a.n = n; a.K = d_in; a.N = d_out; a.ntiles_n = static_cast<int32_t>(ntiles);
+    a.ntiles = static_cast<int32_t>(mtiles * ntiles);
+    // 8 * ceil(tiles / 8) workgroups: the XCD-aware order gives every XCD a
+    // run of tiles, and the workgroups beyond a short run exit at once
+    const int64_t grid = 8 * ((a.ntiles + 7) / 8);
+    hipLaunchKernelGGL(project_kernel, dim3(static_cast<unsigned>(grid)), dim3(kPThreads), 2 * kPStage, stream, a);
+    return hip_status("ngram_project launch");
+}
+
+int ngram_norm_gate_add(const float* eN, const int32_t* tokens, int64_t n, int32_t d, const uint16_t* e1,
+                        int64_t V, const float* W_g, const float* gamma, const float* u, const float* v, float b,
+                        float eps, const uint16_t* residual, uint16_t* out, double* stats_out,
+                        ngram_stream_t stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
+    if (n > INT32_MAX) return fail(NGRAM_ERANGE, "n=%lld above 2^31-1", (long long)n);
+    if (d <= 0 || d % kVec != 0) return fail(NGRAM_EINVAL, "d=%d must be a positive multiple of 8", d);
+    if (d > 16 * kSlice) return fail(NGRAM_ERANGE, "d=%d above %d for the gated path", d, 16 * kSlice);
+    if (!W_g || !gamma || !u || !v || !e1) return fail(NGRAM_EINVAL, "W_g, gamma, u, v or e1 is NULL");
+    if (V < 1) return fail(NGRAM_ERANGE, "V=%lld must be >= 1", (long long)V);
+    if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(b))
+        return fail(NGRAM_EINVAL, "eps must be finite and >= 0, b finite");
+    if (n > 0 && (!eN || !tokens || !out)) return fail(NGRAM_EINVAL, "eN, tokens or out is NULL");
+    if (!aligned(W_g, 16) || !aligned(gamma, 16) || !aligned(u, 16) || !aligned(v, 16) || !aligned(e1, 16) ||
+        (residual && !aligned(residual, 16)) || (n > 0 && (!aligned(out, 16) || !aligned(eN, 16))) ||
+        (stats_out && !aligned(stats_out, 8)))
+        return fail(NGRAM_EALIGN, "eN, e1, W_g, gamma, u, v, residual and out must be 16-byte aligned, stats_out 8");
+    if (n == 0) return NGRAM_OK;
+    GatedArgs g{};
+    FwdArgs& a = g.f;
+    a.tok = tokens; a.e1 = e1; a.wg = W_g; a.res = residual; a.out = out;
+    a.n = n; a.d = d; a.tpw = 1;
+    a.c0_limit = c0_limit_for(e1, V);
+    g.eN = eN; g.gamma = gamma; g.u = u; g.v = v; g.stats = stats_out; g.b = b; g.eps = eps;
+    const int nb = (d + kSlice - 1) / kSlice;
+    const dim3 grid(static_cast<unsigned>(n)), block(64 * nb);
+    const size_t lds = 2 * nb * sizeof(double) + (kK + 1) * sizeof(int32_t);
+    const bool full = d % kSlice == 0;
+    if (residual) launch_gated_mode<NGRAM_TABLE_BF16, true, 3>(g, grid, block, lds, full, stream);
+    else launch_gated_mode<NGRAM_TABLE_BF16, false, 3>(g, grid, block, lds, full, stream);
+    return hip_status("ngram_norm_gate_add launch");
 }
 
 int ngram_forward(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int32_t S,
@@ -2244,6 +2493,7 @@ int ngram_forward_gated_ex(const int32_t* tokens, int64_t n, const int32_t* seq_
     a.c0_limit = c0_limit_for(e1, V);
     a.stage = stage_for(n, S);
     a.sd = make_seeds(seeds);
+    g.eN = nullptr;
     g.gamma = gamma; g.u = u; g.v = v; g.stats = stats_out; g.b = b; g.eps = eps;
     // One token per workgroup for every table type (the kernel then has no
     // token loop, which keeps it at 69-78 VGPRs instead of 113-128).

@@ -126,6 +126,11 @@ int ngram_hash(const int32_t* tokens, int64_t n, const int32_t* seq_offsets, int
  * Errors: EINVAL, EALIGN, ERANGE (see ngram_table). */
 int ngram_embed_bag(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
                     ngram_stream_t stream);
+/* The same sums rounded to bf16 (nearest, ties to even; NaN to 0x7FC0) into
+ * out[n][d] (bf16 bits, device, 16-byte aligned): the input of
+ * ngram_project.  Other arguments and rules as ngram_embed_bag. */
+int ngram_embed_bag_bf16(const ngram_table* T, const int32_t* rows, int64_t n, uint16_t* out,
+                         ngram_stream_t stream);
 /* The same with launch-shape overrides (NULL: none); EINVAL for values out of
  * range. */
 int ngram_embed_bag_ex(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out,
@@ -185,6 +190,35 @@ int ngram_forward_gated_ex(const int32_t* tokens, int64_t n, const int32_t* seq_
                            const float* u, const float* v, float b, float eps,
                            const uint16_t* residual, uint16_t* out, int32_t* rows_out,
                            double* stats_out, const ngram_launch* launch, ngram_stream_t stream);
+
+/* The normalised, input-gated epilogue of ngram_forward_gated on given fp32
+ * sums: eN[n][d] (device, 16-byte aligned) takes the place of the gathered
+ * sums, tokens[n] (device int32) names each token's e1 row (an id outside
+ * [0, V) gives NaN outputs and NaN stats).  Same formula, precision, rounding
+ * and arguments as ngram_forward_gated; the sums over j run in the same order,
+ * so ngram_embed_bag followed by this call gives bit for bit what
+ * ngram_forward_gated gives.  With ngram_project in between it is the
+ * projected path: lookup, projection, normalisation and gate. */
+int ngram_norm_gate_add(const float* eN, const int32_t* tokens, int64_t n, int32_t d, const uint16_t* e1,
+                        int64_t V, const float* W_g, const float* gamma, const float* u, const float* v, float b,
+                        float eps, const uint16_t* residual, uint16_t* out, double* stats_out,
+                        ngram_stream_t stream);
+
+/* Projection: "Qwen 3.8 Flash-Next Deep Dive…", section 1, draws a
+ * "Projection / Normalization" stage between the lookup and the trunk and
+ * does not define it.  Form taken: a learned linear map of each token's sum
+ * x (d_in columns) to d_out columns, with x and the weights P [d_out][d_in]
+ * in bf16 (the model's storage type; ngram_embed_bag_bf16 gives x as the
+ * fp32 sums rounded to bf16):
+ *   y[i][o] = sum over j of P[o][j] * x[i][j].
+ * Each product is exact and the sum is accumulated in fp32 by the matrix
+ * cores in an order this library does not fix, so y can differ from another
+ * fp32 evaluation by up to about d_in 2^-24 sum |terms|.  x[n][d_in] and
+ * P (bf16 bits), y[n][d_out] fp32: device, row-major, 16-byte aligned; d_in a
+ * multiple of 64 and d_out of 8 (EINVAL otherwise), both <= NGRAM_MAX_D
+ * (ERANGE); n >= 0 (n = 0 launches nothing). */
+int ngram_project(const uint16_t* x, int64_t n, int32_t d_in, const uint16_t* P, int32_t d_out, float* y,
+                  ngram_stream_t stream);
 
 /* Pinned-host-table path, "N-grams, of all things" / "Which is why the
  * offload matters more than the parameter count": the table shard sits in

@@ -111,3 +111,28 @@ def gated_bounds(eN, e1v, resv, W, gamma, u, v, stats):
     b_y = wn * (b_alpha[:, None] + alpha[:, None] * rel_n) + \
         MARGIN * 8 * U * (np.abs(resv) + np.abs(e1v) + alpha[:, None] * wn)
     return r * rel_r, b_logit, b_y
+
+
+def project_bound(m, abs_sum):
+    """|difference| between the exact sum of m exact products and an fp32
+    evaluation of it in any order and association: each of the m - 1
+    additions and the final rounding errs by at most 2^-23 relative (a
+    rounding to nearest errs by half that; the allowance also covers a
+    rounding toward zero), so (m + 1) 2^-23 sum|terms|, plus m 2^-126 for
+    partial sums below fp32's normal range."""
+    m = np.asarray(m, np.float64)
+    return MARGIN * ((m + 1.0) * 2.0 ** -23 * np.asarray(abs_sum, np.float64) + m * 2.0 ** -126)
+
+
+def assert_project_close(got, y64, abs64, m, what):
+    """GPU fp32 projection against the oracle's float64 value (whose own
+    error, below (m - 1) 2^-53 sum|terms|, the bound absorbs).  Returns the
+    largest error as a fraction of the bound."""
+    got = np.asarray(got, np.float64)
+    bound = project_bound(m, abs64)
+    err = np.abs(got - y64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (f"{what}: error {err[worst]:.3g} above bound {bound[worst]:.3g} at {worst} "
+                                  f"(got {got[worst]!r}, want {y64[worst]!r})")
+    return float(np.max(err / np.maximum(bound, np.finfo(np.float64).tiny)))
