@@ -1290,10 +1290,10 @@ __global__ void __launch_bounds__(256) select_kernel(const int32_t* counts, int6
 // token ids) with their positions still ascending, then a segmented reduce
 // sums each group in that fixed order.  No floating-point atomics, so every
 // result is reproducible bit for bit.
-constexpr int kSortItems = 8;                      // items per thread
-constexpr int kSortThreads = 1024;
+constexpr int kSortItems = 4;                      // items per thread
+constexpr int kSortThreads = 512;
 constexpr int kSortWaves = kSortThreads / 64;
-constexpr int kSortTile = kSortThreads * kSortItems;   // 8192 items per tile
+constexpr int kSortTile = kSortThreads * kSortItems;   // 2048 items per tile (256 tiles at prefill)
 constexpr int kRadixBits = 9;
 constexpr int kRadixBins = 1 << kRadixBits;            // 512
 constexpr int kScanTile = 4096;                        // items per tile of the segment scan
@@ -1315,93 +1315,57 @@ __global__ void __launch_bounds__(kSortThreads) radix_hist_kernel(const uint32_t
         block_hist[static_cast<int64_t>(q) * nblocks + blockIdx.x] = h[q];
 }
 
-// Exclusive scan, in place, of M uint32 values by one workgroup: thread t
-// owns a contiguous run of ceil(M / 1024) values.
-__global__ void __launch_bounds__(1024) scan_one_block_kernel(uint32_t* __restrict__ v, int64_t M) {
-    __shared__ uint32_t wsum[16];
+// Per digit d (one workgroup each, 256 threads): the exclusive scan of its
+// tile counts block_hist[d][tile] over the tiles, in place, in chunks of 256
+// tiles, and the digit's total in dtot[d].
+__global__ void __launch_bounds__(256) digit_scan_kernel(uint32_t* __restrict__ block_hist, int64_t nblocks,
+                                                         uint32_t* __restrict__ dtot) {
+    __shared__ uint32_t wsum[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t per = (M + 1023) / 1024;
-    const int64_t b0 = static_cast<int64_t>(threadIdx.x) * per;
-    const int64_t b1 = b0 + per < M ? b0 + per : M;
-    uint32_t s = 0;
-    for (int64_t q0 = b0; q0 < b1; q0 += 8) {        // 8 independent loads in flight
-        uint32_t c[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) c[u] = q0 + u < b1 ? v[q0 + u] : 0u;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s += c[u];
-    }
-    uint32_t x = s;                                  // inclusive scan of the run sums over the wavefront
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-        uint32_t t = lane < 16 ? wsum[lane] : 0u;
-        for (int off = 1; off < 16; off <<= 1) {
-            const uint32_t y = __shfl_up(t, off);
-            if (lane >= off) t += y;
+    uint32_t* h = block_hist + static_cast<int64_t>(blockIdx.x) * nblocks;
+    uint32_t carry = 0;
+    for (int64_t c0 = 0; c0 < nblocks; c0 += 256) {
+        const int64_t t = c0 + threadIdx.x;
+        const uint32_t v = t < nblocks ? h[t] : 0u;
+        uint32_t x = v;                              // inclusive scan over the wavefront
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
         }
-        if (lane < 16) wsum[lane] = t;
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        uint32_t before = carry;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        const uint32_t chunk = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        if (t < nblocks) h[t] = before + x - v;
+        carry += chunk;
+        __syncthreads();                             // wsum is rewritten by the next chunk
     }
-    __syncthreads();
-    uint32_t run = (wave > 0 ? wsum[wave - 1] : 0u) + x - s;
-    for (int64_t q0 = b0; q0 < b1; q0 += 8) {
-        uint32_t c[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) c[u] = q0 + u < b1 ? v[q0 + u] : 0u;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (q0 + u < b1) v[q0 + u] = run;
-            run += c[u];
-        }
-    }
+    if (threadIdx.x == 0) dtot[blockIdx.x] = carry;
 }
-
-// Up to this many tiles the scatter computes its digit offsets itself from
-// the per-tile counts (no scan launch between the count and the scatter).
-constexpr int64_t kScatterOwnOffsetsMax = 128;
 
 // Stable scatter of one 9-bit digit.  Tile order is (wavefront, round, lane):
 // an item's rank among equal digits of its tile = equal digits in earlier
 // wavefronts + in earlier rounds of its wavefront + in lower lanes of its
-// round (lanes with an equal digit found by nine ballots).  The tile's base
-// for digit q is offs[q][tile] (the exclusive scan of the counts in digit-major
-// order) or, with OWN, computed here from the counts hist[q][tile].
-template <bool OWN>
+// round (lanes with an equal digit found by nine ballots).  An item of digit
+// q goes to (the count of smaller digits: the exclusive scan of dtot, formed
+// here) + (digit q in earlier tiles: offs[q][tile]) + its rank.
 __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint32_t* __restrict__ kin,
                                                                      const int32_t* __restrict__ vin, int64_t N,
                                                                      int shift, const uint32_t* __restrict__ offs,
-                                                                     int64_t nblocks, uint32_t* __restrict__ kout,
+                                                                     const uint32_t* __restrict__ dtot, int64_t nblocks,
+                                                                     uint32_t* __restrict__ kout,
                                                                      int32_t* __restrict__ vout) {
     __shared__ uint32_t cnt[kSortWaves][kRadixBins];
     __shared__ uint32_t base[kRadixBins];
     __shared__ uint32_t wtot[kSortWaves];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int q = threadIdx.x; q < kSortWaves * kRadixBins; q += kSortThreads) (&cnt[0][0])[q] = 0;
-    if constexpr (OWN) {
-        // digit q = thread / 2: half h of the tiles; the digit's count over all
-        // tiles and over the tiles before this one
-        const int q = threadIdx.x >> 1, h = threadIdx.x & 1;
-        const int64_t half = (nblocks + 1) / 2;
-        const int64_t c0 = h * half, c1 = c0 + half < nblocks ? c0 + half : nblocks;
-        uint32_t tot = 0, bef = 0;
-        for (int64_t c = c0; c < c1; c += 8) {
-            uint32_t v8[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v8[u] = c + u < c1 ? offs[static_cast<int64_t>(q) * nblocks + c + u] : 0u;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                tot += v8[u];
-                if (c + u < static_cast<int64_t>(blockIdx.x)) bef += v8[u];
-            }
-        }
-        tot += __shfl_xor(tot, 1);
-        bef += __shfl_xor(bef, 1);
-        // exclusive scan of the digit totals: lane pairs hold one digit each
-        uint32_t x = h == 0 ? tot : 0u;
+    {
+        // digit q = thread q (kSortThreads == kRadixBins): exclusive scan of the totals
+        static_assert(kSortThreads == kRadixBins, "one thread per digit");
+        const uint32_t tot = dtot[threadIdx.x];
+        uint32_t x = tot;
         for (int off = 1; off < 64; off <<= 1) {
             const uint32_t y = __shfl_up(x, off);
             if (lane >= off) x += y;
@@ -1410,7 +1374,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint3
         __syncthreads();
         uint32_t earlier = 0;
         for (int ww = 0; ww < w; ++ww) earlier += wtot[ww];
-        if (h == 0) base[q] = earlier + x - tot + bef;
+        base[threadIdx.x] = earlier + x - tot;
     }
     __syncthreads();
     const int64_t base0 = static_cast<int64_t>(blockIdx.x) * kSortTile + w * (64 * kSortItems);
@@ -1446,6 +1410,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint3
             cnt[ww][dg] = acc;
             acc += c;
         }
+        base[dg] += offs[static_cast<int64_t>(dg) * nblocks + blockIdx.x];
     }
     __syncthreads();
 #pragma unroll
@@ -1453,8 +1418,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint3
         const int64_t idx = base0 + r * 64 + lane;
         if (idx < N) {
             const uint32_t dg = (key[r] >> shift) & (kRadixBins - 1);
-            const uint32_t b0 = OWN ? base[dg] : offs[static_cast<int64_t>(dg) * nblocks + blockIdx.x];
-            const uint32_t pos = b0 + cnt[w][dg] + local[r];
+            const uint32_t pos = base[dg] + cnt[w][dg] + local[r];
             kout[pos] = key[r];
             vout[pos] = val[r];
         }
@@ -2009,7 +1973,7 @@ int check_pool(const ngram_table* T, const ngram_row_pool* P) {
 // Workspace of the gradient calls, for N = 16 n sort items (the table) and
 // the gate's chunk partials.
 struct GradLayout {
-    int64_t N, nblocks, ntiles, keysA, valsA, keysB, valsB, segs, starts, hist, tiles, longs, parts, total;
+    int64_t N, nblocks, ntiles, keysA, valsA, keysB, valsB, segs, starts, hist, dtot, tiles, longs, parts, total;
 };
 
 GradLayout grad_layout(int64_t n, int32_t d) {
@@ -2026,6 +1990,7 @@ GradLayout grad_layout(int64_t n, int32_t d) {
     L.segs = o; o = up(o + 4 * L.N);
     L.starts = o; o = up(o + 4 * (L.N + 1));
     L.hist = o; o = up(o + 4 * kRadixBins * (L.nblocks > 0 ? L.nblocks : 1));
+    L.dtot = o; o = up(o + 4 * kRadixBins);
     L.tiles = o; o = up(o + 4 * (L.ntiles > 0 ? L.ntiles : 1));
     L.longs = o; o = up(o + 16 + 4 * (L.N / kLongGroup + 1));
     L.parts = o; o = up(o + 8 * ((n + kGateChunk - 1) / kGateChunk) * static_cast<int64_t>(d > 0 ? d : 1));
@@ -2035,8 +2000,8 @@ GradLayout grad_layout(int64_t n, int32_t d) {
 
 // Stable sort of N (key, value) pairs by key (keys <= limit), ping-ponging
 // between the A and B buffers; returns the buffers that hold the result.
-// Each 9-bit pass: per-tile digit counts, their exclusive scan (one
-// workgroup), the stable scatter.
+// Each 9-bit pass: per-tile digit counts, each digit's scan over the tiles
+// (one workgroup per digit), the stable scatter.
 void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStream_t st, uint32_t** keys_out,
                 int32_t** vals_out) {
     uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.keysA);
@@ -2044,6 +2009,7 @@ void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStr
     uint32_t* kB = reinterpret_cast<uint32_t*>(ws + L.keysB);
     int32_t* vB = reinterpret_cast<int32_t*>(ws + L.valsB);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    uint32_t* dtot = reinterpret_cast<uint32_t*>(ws + L.dtot);
     const int64_t nblocks = (N + kSortTile - 1) / kSortTile;
     int bits = 1;
     while (bits < 32 && (limit >> bits) != 0) ++bits;
@@ -2052,14 +2018,9 @@ void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStr
         const int shift = kRadixBits * p;
         hipLaunchKernelGGL(radix_hist_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0, st, kA, N,
                            shift, hist, nblocks);
-        if (nblocks <= kScatterOwnOffsetsMax) {
-            hipLaunchKernelGGL(radix_scatter_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0,
-                               st, kA, vA, N, shift, hist, nblocks, kB, vB);
-        } else {
-            hipLaunchKernelGGL(scan_one_block_kernel, dim3(1), dim3(1024), 0, st, hist, kRadixBins * nblocks);
-            hipLaunchKernelGGL(radix_scatter_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0,
-                               st, kA, vA, N, shift, hist, nblocks, kB, vB);
-        }
+        hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadixBins), dim3(256), 0, st, hist, nblocks, dtot);
+        hipLaunchKernelGGL(radix_scatter_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0, st, kA,
+                           vA, N, shift, hist, dtot, nblocks, kB, vB);
         uint32_t* tk = kA; kA = kB; kB = tk;
         int32_t* tv = vA; vA = vB; vB = tv;
     }
