@@ -1298,17 +1298,42 @@ constexpr int kRadixBits = 9;
 constexpr int kRadixBins = 1 << kRadixBits;            // 512
 constexpr int kScanTile = 4096;                        // items per tile of the segment scan
 
+// Where the first pass takes its items: the ids themselves (key = the id,
+// or limit when it is out of range or its token is padding; value = the
+// item's index), so no separate pass writes the initial keys.  The first
+// pass's histogram kernel also clears the group and long-group counts.
+struct SortSource {
+    const int32_t* ids;            // NULL on later passes: read kin / vin
+    const int32_t* valid_rows;     // NULL, or item t is valid only if valid_rows[t * stride] >= 0
+    int stride;
+    uint32_t limit;
+    int64_t* n_unique;             // cleared by the first pass (NULL on later ones)
+    uint32_t* nlong;
+};
+
+__device__ inline uint32_t sort_key(const SortSource& s, const uint32_t* __restrict__ kin, int64_t t) {
+    if (!s.ids) return kin[t];
+    const int32_t id = s.ids[t];
+    bool ok = id >= 0 && static_cast<uint32_t>(id) < s.limit;
+    if (s.valid_rows) ok = ok && s.valid_rows[t * s.stride] >= 0;
+    return ok ? static_cast<uint32_t>(id) : s.limit;
+}
+
 // Per-tile digit counts: block_hist[digit][tile].
-__global__ void __launch_bounds__(kSortThreads) radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t N,
-                                                                  int shift, uint32_t* __restrict__ block_hist,
-                                                                  int64_t nblocks) {
+__global__ void __launch_bounds__(kSortThreads) radix_hist_kernel(SortSource src, const uint32_t* __restrict__ keys,
+                                                                  int64_t N, int shift,
+                                                                  uint32_t* __restrict__ block_hist, int64_t nblocks) {
     __shared__ uint32_t h[kRadixBins];
+    if (src.n_unique && blockIdx.x == 0 && threadIdx.x == 0) {
+        *src.n_unique = 0;
+        *src.nlong = 0u;
+    }
     for (int q = threadIdx.x; q < kRadixBins; q += kSortThreads) h[q] = 0;
     __syncthreads();
     const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kSortTile;
     for (int q = 0; q < kSortItems; ++q) {
         const int64_t idx = tile0 + q * kSortThreads + threadIdx.x;
-        if (idx < N) atomicAdd(&h[(keys[idx] >> shift) & (kRadixBins - 1)], 1u);
+        if (idx < N) atomicAdd(&h[(sort_key(src, keys, idx) >> shift) & (kRadixBins - 1)], 1u);
     }
     __syncthreads();
     for (int q = threadIdx.x; q < kRadixBins; q += kSortThreads)
@@ -1349,8 +1374,11 @@ __global__ void __launch_bounds__(256) digit_scan_kernel(uint32_t* __restrict__ 
 // wavefronts + in earlier rounds of its wavefront + in lower lanes of its
 // round (lanes with an equal digit found by nine ballots).  An item of digit
 // q goes to (the count of smaller digits: the exclusive scan of dtot, formed
-// here) + (digit q in earlier tiles: offs[q][tile]) + its rank.
-__global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint32_t* __restrict__ kin,
+// here) + (digit q in earlier tiles: offs[q][tile]) + its rank.  The tile is
+// first reordered in LDS, so each store instruction writes runs of
+// consecutive addresses rather than 64 scattered words.
+__global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(SortSource src,
+                                                                     const uint32_t* __restrict__ kin,
                                                                      const int32_t* __restrict__ vin, int64_t N,
                                                                      int shift, const uint32_t* __restrict__ offs,
                                                                      const uint32_t* __restrict__ dtot, int64_t nblocks,
@@ -1358,6 +1386,9 @@ __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint3
                                                                      int32_t* __restrict__ vout) {
     __shared__ uint32_t cnt[kSortWaves][kRadixBins];
     __shared__ uint32_t base[kRadixBins];
+    __shared__ uint32_t tstart[kRadixBins];
+    __shared__ uint32_t skey[kSortTile];
+    __shared__ int32_t sval[kSortTile];
     __shared__ uint32_t wtot[kSortWaves];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int q = threadIdx.x; q < kSortWaves * kRadixBins; q += kSortThreads) (&cnt[0][0])[q] = 0;
@@ -1385,8 +1416,8 @@ __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint3
     for (int r = 0; r < kSortItems; ++r) {
         const int64_t idx = base0 + r * 64 + lane;
         const bool active = idx < N;
-        key[r] = active ? kin[idx] : 0u;
-        val[r] = active ? vin[idx] : 0;
+        key[r] = active ? sort_key(src, kin, idx) : 0u;
+        val[r] = active ? (src.ids ? static_cast<int32_t>(idx) : vin[idx]) : 0;
         const uint32_t dg = (key[r] >> shift) & (kRadixBins - 1);
         uint64_t same = __ballot(active);
 #pragma unroll
@@ -1402,8 +1433,12 @@ __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint3
         local[r] = before + rank;
     }
     __syncthreads();
-    // cnt[w][dg] := equal digits in wavefronts before w (exclusive prefix)
-    for (int dg = threadIdx.x; dg < kRadixBins; dg += kSortThreads) {
+    {
+        // digit dg = thread dg: cnt[w][dg] := equal digits in wavefronts
+        // before w (exclusive prefix); tstart[dg] := the tile's items of
+        // smaller digits; base[dg] := where the tile's run of dg starts in
+        // the output
+        const int dg = threadIdx.x;
         uint32_t acc = 0;
         for (int ww = 0; ww < kSortWaves; ++ww) {
             const uint32_t c = cnt[ww][dg];
@@ -1411,34 +1446,45 @@ __global__ void __launch_bounds__(kSortThreads) radix_scatter_kernel(const uint3
             acc += c;
         }
         base[dg] += offs[static_cast<int64_t>(dg) * nblocks + blockIdx.x];
+        uint32_t x = acc;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wtot[w] = x;             // its first use ended two barriers ago
+        __syncthreads();
+        uint32_t earlier = 0;
+        for (int ww = 0; ww < w; ++ww) earlier += wtot[ww];
+        tstart[dg] = earlier + x - acc;
     }
     __syncthreads();
+    // the tile's items into LDS in output order (digit, then rank) ...
 #pragma unroll
     for (int r = 0; r < kSortItems; ++r) {
         const int64_t idx = base0 + r * 64 + lane;
         if (idx < N) {
             const uint32_t dg = (key[r] >> shift) & (kRadixBins - 1);
-            const uint32_t pos = base[dg] + cnt[w][dg] + local[r];
-            kout[pos] = key[r];
-            vout[pos] = val[r];
+            const uint32_t slot = tstart[dg] + cnt[w][dg] + local[r];
+            skey[slot] = key[r];
+            sval[slot] = val[r];
         }
     }
-}
-
-// Keys and positions to sort: keys[t] = the id (limit for an invalid one),
-// vals[t] = t.  Thread 0 also clears the group count.
-__global__ void __launch_bounds__(256) sort_init_kernel(const int32_t* __restrict__ ids, int64_t N, int stride,
-                                                        const int32_t* __restrict__ valid_rows, uint32_t limit,
-                                                        uint32_t* __restrict__ keys, int32_t* __restrict__ vals,
-                                                        int64_t* __restrict__ n_unique) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t == 0) *n_unique = 0;
-    if (t >= N) return;
-    const int32_t id = ids[t];
-    bool ok = id >= 0 && static_cast<uint32_t>(id) < limit;
-    if (valid_rows) ok = ok && valid_rows[t * stride] >= 0;
-    keys[t] = ok ? static_cast<uint32_t>(id) : limit;
-    vals[t] = static_cast<int32_t>(t);
+    __syncthreads();
+    // ... and out from there, consecutive threads taking consecutive slots, so
+    // that the stores of one digit's run go to consecutive addresses
+    const int64_t left = N - static_cast<int64_t>(blockIdx.x) * kSortTile;
+    const int count = left < kSortTile ? static_cast<int>(left) : kSortTile;
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int slot = r * kSortThreads + threadIdx.x;
+        if (slot < count) {
+            const uint32_t k = skey[slot];
+            const uint32_t dg = (k >> shift) & (kRadixBins - 1);
+            const uint32_t pos = base[dg] + static_cast<uint32_t>(slot) - tstart[dg];
+            kout[pos] = k;
+            vout[pos] = sval[slot];
+        }
+    }
 }
 
 // Group numbering of the sorted keys, first half: per tile of kScanTile
@@ -1485,13 +1531,22 @@ __global__ void __launch_bounds__(1024) seg_scan_kernel(const uint32_t* __restri
     if (threadIdx.x == 0) tile_sums[blockIdx.x] = wsum[15];
 }
 
+// Groups longer than this many items are walked by long_walk_kernel, with
+// four times the rows in flight per wavefront (a
+// Zipf-hot token's e1 gradient adds thousands of dL/dout rows, one after
+// another per column).
+constexpr int kLongGroup = 512;
+
 // Second half: seg[t] += the counts of the earlier tiles (each workgroup adds
 // them up itself), then each group's first index, its id, the end sentinel
-// and the group count.
+// and the group count; a group longer than kLongGroup items (its last item t
+// has the same key as item t - kLongGroup, the keys being sorted) is also
+// listed in longs[], in an unspecified order.
 __global__ void __launch_bounds__(1024) seg_bounds_kernel(const uint32_t* __restrict__ keys, uint32_t* __restrict__ seg,
                                                           const uint32_t* __restrict__ tile_sums, int64_t N,
                                                           uint32_t limit, int32_t* __restrict__ seg_start,
-                                                          int32_t* __restrict__ ids_out, int64_t* __restrict__ n_unique) {
+                                                          int32_t* __restrict__ ids_out, int64_t* __restrict__ n_unique,
+                                                          int32_t* __restrict__ longs, uint32_t* __restrict__ nlong) {
     __shared__ uint32_t red[16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t part = 0;
@@ -1520,17 +1575,15 @@ __global__ void __launch_bounds__(1024) seg_bounds_kernel(const uint32_t* __rest
             seg_start[U] = static_cast<int32_t>(t + 1);
             *n_unique = U;
         }
+        const bool last = t + 1 == N || keys[t + 1] != k;
+        if (last && t >= kLongGroup && keys[t - kLongGroup] == k)     // then not first: group sg - 1
+            longs[atomicAdd(nlong, 1u)] = static_cast<int32_t>(sg - 1u);
     }
 }
 
 __global__ void __launch_bounds__(64) set_i64_kernel(int64_t* p, int64_t v) {
     if (threadIdx.x == 0) *p = v;
 }
-
-// Groups longer than this many items are walked by long_walk_kernel, with
-// four times the rows in flight per wavefront (a Zipf-hot token's e1
-// gradient adds thousands of dL/dout rows, one after another per column).
-constexpr int kLongGroup = 512;
 
 // Workgroup c owns the groups that start among sorted items [64 c, 64 c + 64)
 // and walks their items in order (past the chunk's end for the last group),
@@ -1659,15 +1712,6 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
     }
 }
 
-// The groups longer than kLongGroup items, listed in an unspecified order.
-__global__ void __launch_bounds__(256) long_groups_kernel(const int32_t* __restrict__ seg_start,
-                                                          const int64_t* __restrict__ n_unique, int64_t N,
-                                                          int32_t* __restrict__ longs, uint32_t* __restrict__ nlong) {
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (u >= N || u >= *n_unique) return;
-    if (seg_start[u + 1] - seg_start[u] > kLongGroup) longs[atomicAdd(nlong, 1u)] = static_cast<int32_t>(u);
-}
-
 // One long group per workgroup iteration: wavefront w of workgroup (x, y)
 // owns columns 512 y + 128 w + 2 lane (+1) and walks the group's items in
 // position order, so each column's sum runs in the same order as in
@@ -1746,52 +1790,58 @@ constexpr int kGateChunk = 128;
 constexpr int kGateWaves = 4;
 constexpr int kGateCols = 4;       // columns per lane: 256 per wavefront
 constexpr int kGateUnroll = 8;     // tokens whose loads are issued together
+constexpr int kGateGrid = 1024;    // workgroups at most: 4 of 4 wavefronts per compute unit
 
 __global__ void __launch_bounds__(256) gate_grad_partial_kernel(const int32_t* __restrict__ rows,
                                                                 const uint16_t* __restrict__ g,
                                                                 const float* __restrict__ eN, int64_t n, int32_t d,
+                                                                int64_t nchunks, int colblocks,
                                                                 double* __restrict__ partials) {
     __shared__ double lp[kGateWaves][64 * kGateCols];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t c = blockIdx.x;
-    const int64_t j0 = (static_cast<int64_t>(blockIdx.y) * 64 + lane) * kGateCols;
-    const bool col = j0 < d;           // d % 8 == 0, so the lane's 4 columns are all in range
     constexpr int kPerWave = kGateChunk / kGateWaves;
-    const int64_t i0 = c * kGateChunk + wave * kPerWave;
-    const int64_t i1 = i0 + kPerWave < n ? i0 + kPerWave : n;
-    double part[kGateCols] = {0.0, 0.0, 0.0, 0.0};
-    if (col) {
-        for (int64_t ib = i0; ib < i1; ib += kGateUnroll) {
-            uint2 gv[kGateUnroll];
-            float4 ev[kGateUnroll];
-            bool ok[kGateUnroll];
+    // work item q = (chunk q / colblocks, 256-column block q % colblocks)
+    for (int64_t q = blockIdx.x; q < nchunks * colblocks; q += gridDim.x) {
+        const int64_t c = q / colblocks;
+        const int64_t j0 = ((q % colblocks) * 64 + lane) * kGateCols;
+        const bool col = j0 < d;       // d % 8 == 0, so the lane's 4 columns are all in range
+        const int64_t i0 = c * kGateChunk + wave * kPerWave;
+        const int64_t i1 = i0 + kPerWave < n ? i0 + kPerWave : n;
+        double part[kGateCols] = {0.0, 0.0, 0.0, 0.0};
+        if (col) {
+            for (int64_t ib = i0; ib < i1; ib += kGateUnroll) {
+                uint2 gv[kGateUnroll];
+                float4 ev[kGateUnroll];
+                bool ok[kGateUnroll];
 #pragma unroll
-            for (int q = 0; q < kGateUnroll; ++q) {
-                const int64_t i = ib + q < i1 ? ib + q : ib;
-                ok[q] = ib + q < i1 && rows[i * kK] >= 0;
-                gv[q] = *reinterpret_cast<const uint2*>(g + i * d + j0);
-                ev[q] = *reinterpret_cast<const float4*>(eN + i * d + j0);
-            }
+                for (int u = 0; u < kGateUnroll; ++u) {
+                    const int64_t i = ib + u < i1 ? ib + u : ib;
+                    ok[u] = ib + u < i1 && rows[i * kK] >= 0;
+                    gv[u] = *reinterpret_cast<const uint2*>(g + i * d + j0);
+                    ev[u] = *reinterpret_cast<const float4*>(eN + i * d + j0);
+                }
 #pragma unroll
-            for (int q = 0; q < kGateUnroll; ++q) {
-                if (!ok[q]) continue;
-                part[0] = part[0] + static_cast<double>(bf16lo(gv[q].x)) * static_cast<double>(ev[q].x);
-                part[1] = part[1] + static_cast<double>(bf16hi(gv[q].x)) * static_cast<double>(ev[q].y);
-                part[2] = part[2] + static_cast<double>(bf16lo(gv[q].y)) * static_cast<double>(ev[q].z);
-                part[3] = part[3] + static_cast<double>(bf16hi(gv[q].y)) * static_cast<double>(ev[q].w);
+                for (int u = 0; u < kGateUnroll; ++u) {
+                    if (!ok[u]) continue;
+                    part[0] = part[0] + static_cast<double>(bf16lo(gv[u].x)) * static_cast<double>(ev[u].x);
+                    part[1] = part[1] + static_cast<double>(bf16hi(gv[u].x)) * static_cast<double>(ev[u].y);
+                    part[2] = part[2] + static_cast<double>(bf16lo(gv[u].y)) * static_cast<double>(ev[u].z);
+                    part[3] = part[3] + static_cast<double>(bf16hi(gv[u].y)) * static_cast<double>(ev[u].w);
+                }
             }
         }
-    }
 #pragma unroll
-    for (int e = 0; e < kGateCols; ++e) lp[wave][lane * kGateCols + e] = part[e];
-    __syncthreads();
-    if (wave == 0 && col) {
+        for (int e = 0; e < kGateCols; ++e) lp[wave][lane * kGateCols + e] = part[e];
+        __syncthreads();
+        if (wave == 0 && col) {
 #pragma unroll
-        for (int e = 0; e < kGateCols; ++e) {
-            double t = lp[0][lane * kGateCols + e];
-            for (int w = 1; w < kGateWaves; ++w) t = t + lp[w][lane * kGateCols + e];
-            partials[c * d + j0 + e] = t;
+            for (int e = 0; e < kGateCols; ++e) {
+                double t = lp[0][lane * kGateCols + e];
+                for (int w = 1; w < kGateWaves; ++w) t = t + lp[w][lane * kGateCols + e];
+                partials[c * d + j0 + e] = t;
+            }
         }
+        __syncthreads();               // lp is rewritten by the next item
     }
 }
 
@@ -2002,8 +2052,8 @@ GradLayout grad_layout(int64_t n, int32_t d) {
 // between the A and B buffers; returns the buffers that hold the result.
 // Each 9-bit pass: per-tile digit counts, each digit's scan over the tiles
 // (one workgroup per digit), the stable scatter.
-void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStream_t st, uint32_t** keys_out,
-                int32_t** vals_out) {
+void radix_sort(char* ws, const GradLayout& L, int64_t N, const SortSource& first, hipStream_t st,
+                uint32_t** keys_out, int32_t** vals_out) {
     uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.keysA);
     int32_t* vA = reinterpret_cast<int32_t*>(ws + L.valsA);
     uint32_t* kB = reinterpret_cast<uint32_t*>(ws + L.keysB);
@@ -2012,15 +2062,16 @@ void radix_sort(char* ws, const GradLayout& L, int64_t N, uint32_t limit, hipStr
     uint32_t* dtot = reinterpret_cast<uint32_t*>(ws + L.dtot);
     const int64_t nblocks = (N + kSortTile - 1) / kSortTile;
     int bits = 1;
-    while (bits < 32 && (limit >> bits) != 0) ++bits;
+    while (bits < 32 && (first.limit >> bits) != 0) ++bits;
     const int passes = (bits + kRadixBits - 1) / kRadixBits;
     for (int p = 0; p < passes; ++p) {
         const int shift = kRadixBits * p;
-        hipLaunchKernelGGL(radix_hist_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0, st, kA, N,
-                           shift, hist, nblocks);
+        const SortSource src = p == 0 ? first : SortSource{nullptr, nullptr, 0, first.limit, nullptr, nullptr};
+        hipLaunchKernelGGL(radix_hist_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0, st, src,
+                           kA, N, shift, hist, nblocks);
         hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadixBins), dim3(256), 0, st, hist, nblocks, dtot);
-        hipLaunchKernelGGL(radix_scatter_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0, st, kA,
-                           vA, N, shift, hist, dtot, nblocks, kB, vB);
+        hipLaunchKernelGGL(radix_scatter_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kSortThreads), 0, st, src,
+                           kA, vA, N, shift, hist, dtot, nblocks, kB, vB);
         uint32_t* tk = kA; kA = kB; kB = tk;
         int32_t* tv = vA; vA = vB; vB = tv;
     }
@@ -2039,25 +2090,18 @@ int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* val
         hipLaunchKernelGGL(set_i64_kernel, dim3(1), dim3(64), 0, st, n_unique, int64_t{0});
         return hip_status("gradient launch");
     }
-    uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.keysA);
-    int32_t* vA = reinterpret_cast<int32_t*>(ws + L.valsA);
-    const unsigned gN = static_cast<unsigned>((N + 255) / 256);
-    hipLaunchKernelGGL(sort_init_kernel, dim3(gN), dim3(256), 0, st, ids, N, stride, valid_rows, limit, kA, vA,
-                       n_unique);
+    uint32_t* nlong = reinterpret_cast<uint32_t*>(ws + L.longs);
+    int32_t* longs = reinterpret_cast<int32_t*>(ws + L.longs + 16);
     uint32_t* keys = nullptr;
     int32_t* pos = nullptr;
-    radix_sort(ws, L, N, limit, st, &keys, &pos);
+    radix_sort(ws, L, N, SortSource{ids, valid_rows, stride, limit, n_unique, nlong}, st, &keys, &pos);
     uint32_t* segs = reinterpret_cast<uint32_t*>(ws + L.segs);
     int32_t* starts = reinterpret_cast<int32_t*>(ws + L.starts);
     uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
     const unsigned ntiles = static_cast<unsigned>((N + kScanTile - 1) / kScanTile);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(ntiles), dim3(1024), 0, st, keys, N, limit, segs, tiles);
     hipLaunchKernelGGL(seg_bounds_kernel, dim3(ntiles), dim3(1024), 0, st, keys, segs, tiles, N, limit, starts, ids_out,
-                       n_unique);
-    uint32_t* nlong = reinterpret_cast<uint32_t*>(ws + L.longs);
-    int32_t* longs = reinterpret_cast<int32_t*>(ws + L.longs + 16);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int32_t*>(nlong), 1, 0);
-    hipLaunchKernelGGL(long_groups_kernel, dim3(gN), dim3(256), 0, st, starts, n_unique, N, longs, nlong);
+                       n_unique, longs, nlong);
     const int nslices = (d + kSlice - 1) / kSlice;
     const int waves = nslices < 16 ? nslices : 16;
     const int64_t grid = (N + kWalkChunk - 1) / kWalkChunk;
@@ -2134,9 +2178,15 @@ void launch_gate_grad(const int32_t* rows, const uint16_t* dout, const float* eN
                       float* grad_Wg_out, double* parts, hipStream_t stream) {
     const int64_t nchunks = (n + kGateChunk - 1) / kGateChunk;
     if (nchunks > 0) {
-        const unsigned colblocks = static_cast<unsigned>((d / kGateCols + 63) / 64);
-        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(nchunks), colblocks),
-                           dim3(64 * kGateWaves), 0, stream, rows, dout, eN, n, d, parts);
+        // at most kGateGrid workgroups, each taking an equal share of the
+        // items, so the kernel leaves room on every compute unit for work
+        // on other streams (the sort of the table gradient)
+        const int colblocks = (d / kGateCols + 63) / 64;
+        const int64_t items = nchunks * colblocks;
+        const int64_t per = (items + kGateGrid - 1) / kGateGrid;
+        const int64_t grid = (items + per - 1) / per;
+        hipLaunchKernelGGL(gate_grad_partial_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * kGateWaves), 0,
+                           stream, rows, dout, eN, n, d, nchunks, colblocks, parts);
     }
     hipLaunchKernelGGL(gate_grad_total_kernel, dim3(static_cast<unsigned>((d + 63) / 64)), dim3(64 * kGateTotalWaves),
                        0, stream, parts, nchunks, d, grad_Wg_out);
