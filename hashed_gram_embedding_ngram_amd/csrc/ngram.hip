@@ -1712,71 +1712,97 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
     }
 }
 
-// One long group per workgroup iteration: wavefront w of workgroup (x, y)
-// owns columns 512 y + 128 w + 2 lane (+1) and walks the group's items in
+// One long group per workgroup iteration, one wavefront per workgroup: lane c
+// of workgroup (x, y) owns column 64 y + c and adds the group's items in
 // position order, so each column's sum runs in the same order as in
-// seg_walk_kernel.  Two banks of kLongBank dL/dout rows: while one bank is
-// summed, the other bank's loads (and the next 64 positions) are in flight.
-constexpr int kLongBank = 32;
+// seg_walk_kernel.  A group's items are taken in units of 64, kLongUnits units
+// in flight.  The dL/dout rows go straight into LDS (global_load_lds_dwordx4:
+// lanes 8 j .. 8 j + 7 of an instruction fetch 16 bytes each of item j's 64
+// columns, which land as one 128-byte row), so a wavefront keeps 256 rows in
+// flight without holding them in registers; a chain of thousands of items then
+// waits for memory once per 256 items rather than once per 64.  The items'
+// positions take the same route, issued before the rows of the unit kLongUnits
+// earlier: the load counter drains in issue order, so when a unit's rows have
+// landed, so have the positions of the unit whose rows are issued next.
+constexpr int kLongUnits = 4;      // units of 64 items in flight
+constexpr int kLongOps = 9;        // loads per unit: 1 of 64 positions + 8 of 8 rows
+static_assert((kLongUnits - 1) * kLongOps == 27, "the wait below counts the loads of kLongUnits - 1 units");
 
-__device__ inline void long_load(uint32_t gv[kLongBank], int32_t pl, int first, int64_t tb, int64_t te,
-                                 const uint16_t* __restrict__ g, int32_t d, int64_t jc, int pos_shift) {
+struct LongLds {
+    uint8_t rows[kLongUnits][64 * 128];        // item j of a unit: its 64 columns at 128 j
+    int32_t pos[2 * kLongUnits][64];
+};
+
+// Positions of unit x's items (past te: item tb0's, which is valid) into pos[slot].
+__device__ inline void long_issue_pos(LongLds& L, int slot, const int32_t* __restrict__ sorted_pos, int64_t tb0,
+                                      int64_t te, int64_t x, int lane) {
+    const int64_t t = tb0 + 64 * x + lane;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(sorted_pos + (t < te ? t : tb0)),
+                                     (__attribute__((address_space(3))) void*)(&L.pos[slot][0]), 4, 0, 0);
+}
+
+// Rows of the unit whose positions are in pos[pslot] into rows[slot]: load m
+// fetches items 8 m .. 8 m + 7, lane l item 8 m + (l >> 3), columns lc .. lc + 7.
+__device__ inline void long_issue_rows(LongLds& L, int slot, int pslot, const uint16_t* __restrict__ g, int32_t d,
+                                       int64_t lc, int pos_shift, int lane) {
 #pragma unroll
-    for (int m = 0; m < kLongBank; ++m) {
-        const int src = tb + first + m < te ? first + m : 0;     // lane 0 (item tb) is always valid
-        const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readlane(pl, src) >> pos_shift);
-        gv[m] = *reinterpret_cast<const uint32_t*>(g + i * d + jc);
+    for (int m = 0; m < 8; ++m) {
+        const int64_t i = static_cast<int64_t>(L.pos[pslot][8 * m + (lane >> 3)] >> pos_shift);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + i * d + lc),
+                                         (__attribute__((address_space(3))) void*)(&L.rows[slot][1024 * m]), 16, 0, 0);
     }
 }
 
 template <bool WEIGHT>
-__device__ inline void long_add(float& a0, float& a1, const uint32_t gv[kLongBank], int first, int64_t tb,
-                                int64_t te, float w0, float w1) {
-#pragma unroll
-    for (int m = 0; m < kLongBank; ++m) {
-        if (tb + first + m < te) {                                 // uniform predicate
-            const float x0 = bf16lo(gv[m]), x1 = bf16hi(gv[m]);
-            a0 = WEIGHT ? __builtin_fmaf(w0, x0, a0) : a0 + x0;
-            a1 = WEIGHT ? __builtin_fmaf(w1, x1, a1) : a1 + x1;
-        }
-    }
-}
-
-template <bool WEIGHT>
-__global__ void __launch_bounds__(256) long_walk_kernel(const int32_t* __restrict__ longs,
-                                                        const uint32_t* __restrict__ nlong,
-                                                        const int32_t* __restrict__ seg_start,
-                                                        const int32_t* __restrict__ sorted_pos, int pos_shift,
-                                                        const uint16_t* __restrict__ g, const float* __restrict__ W,
-                                                        int32_t d, float* __restrict__ out) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t j0 = static_cast<int64_t>(blockIdx.y) * 512 + wave * 128 + lane * 2;
-    const bool col_ok = j0 < d;                  // d % 8 == 0: j0 + 1 < d as well
-    const int64_t jc = col_ok ? j0 : 0;
-    float w0 = 1.0f, w1 = 1.0f;
-    if (WEIGHT) {
-        const float2 wv = *reinterpret_cast<const float2*>(W + jc);
-        w0 = wv.x; w1 = wv.y;
-    }
+__global__ void __launch_bounds__(64) long_walk_kernel(const int32_t* __restrict__ longs,
+                                                       const uint32_t* __restrict__ nlong,
+                                                       const int32_t* __restrict__ seg_start,
+                                                       const int32_t* __restrict__ sorted_pos, int pos_shift,
+                                                       const uint16_t* __restrict__ g, const float* __restrict__ W,
+                                                       int32_t d, float* __restrict__ out) {
+    __shared__ LongLds L;
+    const int lane = threadIdx.x;
+    const int64_t col = static_cast<int64_t>(blockIdx.y) * 64 + lane;
+    const bool col_ok = col < d;
+    // d % 8 == 0: the 8 columns a lane fetches are all inside the row or all
+    // past it (then it fetches columns 0 .. 7, which no lane adds)
+    const int64_t lcol = static_cast<int64_t>(blockIdx.y) * 64 + (lane & 7) * 8;
+    const int64_t lc = lcol < d ? lcol : 0;
+    const float w = WEIGHT ? W[col_ok ? col : 0] : 1.0f;
     const int64_t count = *nlong;
     for (int64_t q = blockIdx.x; q < count; q += gridDim.x) {
         const int64_t u = longs[q];
         const int64_t tb0 = seg_start[u], te = seg_start[u + 1];
-        float a0 = 0.0f, a1 = 0.0f;
-        uint32_t ga[kLongBank], gb[kLongBank];
-        // lane m of pl holds the position of item tb + m
-        int32_t pl = tb0 + lane < te ? sorted_pos[tb0 + lane] : 0;
-        long_load(ga, pl, 0, tb0, te, g, d, jc, pos_shift);
-        for (int64_t tb = tb0; tb < te; tb += 2 * kLongBank) {
-            long_load(gb, pl, kLongBank, tb, te, g, d, jc, pos_shift);
-            const int64_t tn = tb + 2 * kLongBank;
-            const int32_t pn = tn + lane < te ? sorted_pos[tn + lane] : 0;
-            long_add<WEIGHT>(a0, a1, ga, 0, tb, te, w0, w1);
-            if (tn < te) long_load(ga, pn, 0, tn, te, g, d, jc, pos_shift);
-            long_add<WEIGHT>(a0, a1, gb, kLongBank, tb, te, w0, w1);
-            pl = pn;
+        const int64_t nunits = (te - tb0 + 63) / 64;
+        for (int x = 0; x < kLongUnits; ++x) long_issue_pos(L, x, sorted_pos, tb0, te, x, lane);
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int x = 0; x < kLongUnits; ++x) {
+            long_issue_pos(L, x + kLongUnits, sorted_pos, tb0, te, x + kLongUnits, lane);
+            long_issue_rows(L, x, x, g, d, lc, pos_shift, lane);
         }
-        if (col_ok) *reinterpret_cast<float2*>(out + u * d + j0) = make_float2(a0, a1);
+        float acc = 0.0f;
+        for (int64_t k = 0; k < nunits; ++k) {
+            // unit k's rows have landed (the loads of the kLongUnits - 1 later
+            // units may still be in flight), and with them every earlier load
+            __asm__ volatile("s_waitcnt vmcnt(27)" ::: "memory");
+            const int rs = static_cast<int>(k % kLongUnits);
+            const int64_t left = te - tb0 - 64 * k;
+            const int nk = left < 64 ? static_cast<int>(left) : 64;
+            const uint16_t* r = reinterpret_cast<const uint16_t*>(&L.rows[rs][0]) + lane;
+#pragma unroll 16
+            for (int j = 0; j < nk; ++j) {
+                const float x = __uint_as_float(static_cast<uint32_t>(r[64 * j]) << 16);
+                acc = WEIGHT ? __builtin_fmaf(w, x, acc) : acc + x;
+            }
+            // slot rs is read out before it is refilled
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            long_issue_pos(L, static_cast<int>(k % (2 * kLongUnits)), sorted_pos, tb0, te, k + 2 * kLongUnits, lane);
+            long_issue_rows(L, rs, static_cast<int>((k + kLongUnits) % (2 * kLongUnits)), g, d, lc, pos_shift, lane);
+        }
+        // no load may land once the slots serve the next group or the
+        // workgroup has ended
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (col_ok) out[u * d + col] = acc;
     }
 }
 
@@ -2107,7 +2133,7 @@ int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* val
     const int64_t grid = (N + kWalkChunk - 1) / kWalkChunk;
     hipLaunchKernelGGL((seg_walk_kernel<WEIGHT>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, keys,
                        segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out);
-    hipLaunchKernelGGL((long_walk_kernel<WEIGHT>), dim3(64, static_cast<unsigned>((d + 511) / 512)), dim3(256), 0, st,
+    hipLaunchKernelGGL((long_walk_kernel<WEIGHT>), dim3(64, static_cast<unsigned>((d + 63) / 64)), dim3(64), 0, st,
                        longs, nlong, starts, pos, pos_shift, g, W, d, grad_out);
     return hip_status("gradient launch");
 }
