@@ -102,8 +102,8 @@ def parse():
                     help="host workload: also time the GEMM stand-in beside other PCIe readers (the same gather "
                          "kernel over consecutive rows, a DMA copy of the same bytes) to separate the causes of "
                          "its slowdown")
-    ap.add_argument("--cache-rows", type=int, default=1 << 20, help="pool mode: rows of the hot-row cache")
-    ap.add_argument("--cache-history", type=int, default=8, help="pool mode: earlier batches counted")
+    ap.add_argument("--cache-rows", type=int, default=1 << 22, help="pool mode: rows of the hot-row cache")
+    ap.add_argument("--cache-history", type=int, default=32, help="pool mode: earlier batches counted")
     ap.add_argument("--dist", default="zipf", choices=["zipf", "uniform"],
                     help="token distribution (uniform: the no-reuse control)")
     ap.add_argument("--batches", type=int, default=4, help="distinct batches rotated over")
