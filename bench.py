@@ -347,18 +347,19 @@ def main():
         latency_floor = graph_floor(batches, e1, d, nb, reps)
     else:
         latency_floor = None
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        # one event pair around the back-to-back launches on the launch
+        # stream: the mean interval per launch (kernel + dispatch gap), which
+        # per-launch pairs would inflate by each event's own processing
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        s_ev.record(stream)
         for i in range(args.steps):
-            starts[i].record(stream)
             step(args.warmup + i)
-            ends[i].record(stream)
+        e_ev.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-        mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+        mean_launch_s = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
 
     bpt = nominal_bytes_per_token(d, spec.table, spec.e1, spec.residual)
     bytes_per_launch = bpt * n + 4 * d * (4 if gated else 1)          # W_g (+ gamma, u, v) once per launch
