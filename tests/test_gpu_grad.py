@@ -55,6 +55,45 @@ def test_table_grad(lengths, R, d, bad):
     assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
 
 
+def test_table_grad_long_group_edges():
+    """The long-group walk at its edges: groups of exactly 512 (walked
+    with the short groups), 513 and 577 items (nine and ten 64-item units,
+    the last one ragged), spread over the batch's positions, beside random
+    short groups; d = 200 leaves a ragged 64-column slice."""
+    n, R, d = 120, 50, 200
+    rng = np.random.default_rng(11)
+    ids = np.concatenate([np.full(513, 5), np.full(512, 9), np.full(577, 2),
+                          rng.choice([r for r in range(R) if r not in (2, 5, 9)], n * 16 - 1602)])
+    rows = rng.permutation(ids).astype(np.int32).reshape(n, 16)
+    say("grad table long-group edges")
+    g = synth.tensor(synth.KIND_BF16_WIDE, 12, synth.TAG_RESIDUAL, n * d).reshape(n, d)
+    W = synth.as_f32(synth.tensor(synth.KIND_F32_UNIT, 12, synth.TAG_WG, d))
+    gr, gv, nu = ng.ngram_grad_table(_dev(rows, np.int32), _dev(W, np.float32), _dev(g.view(np.int16), np.int16), R)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    q, want = oracle.grad_table(rows, W, g)
+    assert U == q.size
+    assert np.array_equal(gr.cpu().numpy()[:U], q)
+    assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
+
+
+def test_table_grad_more_long_groups_than_walkers():
+    """About 100 groups longer than 512 items, more than the long-group
+    walk's 64 workgroup rows, so each row takes several groups in turn;
+    d = 72 (a 64-column slice and an 8-column one)."""
+    n, R, d = 5000, 100, 72
+    say("grad table 5000 tokens R=100")
+    toks, rows, g, W = _inputs((n,), R, 151936, d, seed=13)
+    assert (np.unique(rows, return_counts=True)[1] > 512).sum() > 64
+    gr, gv, nu = ng.ngram_grad_table(_dev(rows, np.int32), _dev(W, np.float32), _dev(g.view(np.int16), np.int16), R)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    q, want = oracle.grad_table(rows, W, g)
+    assert U == q.size
+    assert np.array_equal(gr.cpu().numpy()[:U], q)
+    assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
+
+
 def test_table_grad_many_items_sampled():
     """70000 tokens (1.12M sort items, multi-tile histogram scans): the
     distinct-row list in full, gradients of sampled rows (the most frequent
