@@ -927,11 +927,12 @@ __global__ void __launch_bounds__(256) ngram_gate_kernel(const GateArgs a) {
 // 128 (w >> 2), columns 64 (w & 3), as 4 x 2 MFMA tiles of 32 x 32) and walks
 // K in steps of 64 through two LDS buffers.  Operands go from global memory
 // straight into LDS (global_load_lds_dwordx4: lane L's 16 bytes land at the
-// instruction's LDS base + 16 L), so they hold no registers on the way.  In
-// each step a wavefront first reads all its operand fragments of the step
-// from LDS, then issues the next step's loads into the other buffer, then
-// runs its 32 MFMAs; it waits for its own loads and the workgroup barrier
-// closes the step.
+// instruction's LDS base + 16 L), so they hold no registers on the way.  A
+// step issues the next step's loads into the other buffer, then runs its four
+// k-quarters: the 8 MFMAs of a quarter with the 6 fragment reads of the next
+// quarter scheduled between them; a wavefront then waits for its own loads
+// and the workgroup barrier closes the step, after which the step's last
+// quarter of MFMAs runs beside the first reads of the next step.
 // LDS rows are 64 bf16 (128 bytes, eight 16-byte chunks); chunk c of row r is
 // stored at position c ^ ((r >> 1) & 7), so the 16 rows a 16-lane group of an
 // operand read touches fall on 16 different 16-byte bank groups.  A load
@@ -980,6 +981,40 @@ __device__ inline void proj_issue(uint8_t* buf, const uint16_t* const xrow[4], c
     }
 }
 
+// The wavefront's operand fragments of k-quarter kk from the LDS tiles xs and
+// ps: lane L holds k = 16 kk + 8 (L >> 5) .. +7 of row L & 31 of each of its
+// four 32-row x tiles and two 32-row P tiles.
+__device__ __forceinline__ void proj_frags(bf16x8 fa[4], bf16x8 fb[2], const uint8_t* xs, const uint8_t* ps, int wm,
+                                           int wn, int lane, int kk) {
+    const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        fa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + proj_pos(wm + 32 * s + (lane & 31), c)));
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        fb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ps + proj_pos(wn + 32 * s + (lane & 31), c)));
+}
+
+__device__ __forceinline__ void proj_mfma8(f32x16 acc[4][2], const bf16x8 fa[4], const bf16x8 fb[2]) {
+#pragma unroll
+    for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn)
+            acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sm], fb[sn], acc[sm][sn], 0, 0, 0);
+}
+
+// Scheduling of one quarter: MFMA, read, MFMA, read, ... (six reads between
+// the eight MFMAs), so the LDS reads run while the matrix core is busy.
+__device__ __forceinline__ void proj_interleave() {
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __global__ void __launch_bounds__(kPThreads, 1) project_kernel(const ProjArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t plds[];   // [2][x 256 rows | P 256 rows] x 128 B
     const int t = threadIdx.x, lane = t & 63;
@@ -1019,35 +1054,43 @@ __global__ void __launch_bounds__(kPThreads, 1) project_kernel(const ProjArgs a)
     proj_issue(plds, xrow, prow, chunk, wave, 0);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
+    // Software pipeline over k-quarters (kk = 0..3 of a 64-wide step): the
+    // 8 MFMAs of one quarter run while the 6 fragment reads of the next are
+    // issued between them, and the last quarter of a step runs after the
+    // step's barrier, beside the first reads of the next step.  ca/cb: the
+    // fragments the next MFMAs use; na/nb: the ones being read.
+    bf16x8 ca[4], cb[2], na[4], nb[2];
+    proj_frags(ca, cb, plds, plds + kPTile, wm, wn, lane, 0);
+    if (KT > 1) proj_issue(plds + kPStage, xrow, prow, chunk, wave, kPK);
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk) {
+        proj_frags(na, nb, plds, plds + kPTile, wm, wn, lane, kk);
+        proj_mfma8(acc, ca, cb);
+        proj_interleave();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ca[s] = na[s];
+        cb[0] = nb[0]; cb[1] = nb[1];
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kt = 1; kt < KT; ++kt) {
         const uint8_t* xs = plds + (kt & 1) * kPStage;
         const uint8_t* ps = xs + kPTile;
-        // all operand fragments of the step: lane L holds k = 16 kk + 8 (L >> 5)
-        // .. +7 of row L & 31 of each 32-row operand tile
-        bf16x8 af[4][4], bf[4][2];
-#pragma unroll
-        for (int kk = 0; kk < kPK / 16; ++kk) {
-            const int c = 2 * kk + (lane >> 5);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                af[kk][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + proj_pos(wm + 32 * s + (lane & 31), c)));
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                bf[kk][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ps + proj_pos(wn + 32 * s + (lane & 31), c)));
-        }
+        // the buffer of step kt - 1 was read out before the barrier
         if (kt + 1 < KT) proj_issue(plds + ((kt + 1) & 1) * kPStage, xrow, prow, chunk, wave, (kt + 1) * kPK);
 #pragma unroll
-        for (int kk = 0; kk < kPK / 16; ++kk)
+        for (int kk = 0; kk < 4; ++kk) {
+            proj_frags(na, nb, xs, ps, wm, wn, lane, kk);
+            proj_mfma8(acc, ca, cb);
+            proj_interleave();
 #pragma unroll
-            for (int sm = 0; sm < 4; ++sm)
-#pragma unroll
-                for (int sn = 0; sn < 2; ++sn)
-                    acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][sm], bf[kk][sn], acc[sm][sn], 0, 0, 0);
-        // the MFMAs stay ahead of the wait, so the loads land while they run
-        __builtin_amdgcn_sched_barrier(0);
+            for (int s = 0; s < 4; ++s) ca[s] = na[s];
+            cb[0] = nb[0]; cb[1] = nb[1];
+        }
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
+    proj_mfma8(acc, ca, cb);
     // lane L holds rows 8 (e >> 2) + 4 (L >> 5) + (e & 3), column L & 31 of each 32 x 32 tile
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm)
