@@ -2866,7 +2866,9 @@ int64_t ngram_grad_workspace_bytes(int64_t n, int32_t d) {
 
 static int check_grad_common(int64_t n, int32_t d, const uint16_t* dout, void* workspace, int64_t workspace_bytes) {
     if (n < 0) return fail(NGRAM_EINVAL, "n=%lld is negative", (long long)n);
-    // two-level scans of at most 4096^2 entries: 16 n <= 2^24
+    // 32-bit item indices and counts throughout the sort and the walks; each
+    // group-numbering workgroup adds the counts of all earlier tiles, so the
+    // tested range 16 n <= 2^24 is also the accepted one
     if (n > (1 << 20)) return fail(NGRAM_ERANGE, "n=%lld above 2^20", (long long)n);
     if (d <= 0 || d % kVec != 0) return fail(NGRAM_EINVAL, "d=%d must be a positive multiple of 8", d);
     if (d > NGRAM_MAX_D) return fail(NGRAM_ERANGE, "d=%d above %d", d, NGRAM_MAX_D);

@@ -37,7 +37,7 @@ def _dev(a, dt):
 @pytest.mark.parametrize("lengths,R,d,bad", [
     ((40, 0, 57), 61, 64, ()),              # long groups, ragged unroll tails
     ((300, 7), 100_003, 520, (3, 17)),      # invalid tokens, ragged slices
-    ((2000,), 4001, 2560, ()),              # two-level scans (32000 sort items)
+    ((2000,), 4001, 2560, ()),              # 16 sort tiles, 8 group-numbering tiles (32000 items)
     ((1,), 7, 8, ()),
     ((50,), 3, 136, ()),                    # groups of hundreds of items (several 64-item blocks)
     ((200,), 3, 136, (7,)),                 # groups of about 1000 items: the long-group walk
