@@ -55,6 +55,7 @@ def run_project(x_bits, P):
 
 
 @pytest.mark.parametrize("n,d_in,d_out", [(300, 256, 384), (129, 2560, 256), (1, 64, 128), (128, 128, 2560),
+                                          (4096, 128, 768),     # XCD runs of whole tile rows: column order
                                           (517, 640, 640), (65, 128, 72), (1000, 2560, 2560), (257, 64, 512),
                                           (40, 192, 8)])
 def test_project_matches_oracle_within_the_fp32_bound(n, d_in, d_out):
