@@ -129,6 +129,29 @@ def test_embed_bag_bf16_is_the_rounded_sum():
     assert np.array_equal(bits16(out).reshape(sp.n, sp.d), oracle.bf16_rne(want_eN).reshape(sp.n, sp.d))
 
 
+def test_forward_without_gate_terms_gives_the_rounded_sums():
+    """ngram_forward with W_g = 1 and neither e1 nor residual writes
+    bf16(fmaf(1, s, +0)) = bf16(s) for every fp32 sum s (a sum that starts
+    from +0 is never -0): the same bits as ngram_hash + ngram_embed_bag_bf16,
+    also around invalid tokens (their rows NaN both ways).  The projected
+    path's benchmark takes its sums this way, in one launch."""
+    sp = GSPEC.replace(d=640)
+    h = HostInputs(sp)
+    di = DeviceInputs(sp, h)
+    tok = di.tokens.clone()
+    tok[5] = -1
+    tok[17] = (1 << 21) - 1                          # the pad id is not a real token
+    say("forward W_g = 1 against embed_bag_bf16")
+    rows = ng.ngram_hash(tok, di.offsets, sp.R)
+    want = ng.ngram_embed_bag_bf16(di.table_obj(), rows)
+    got = torch.empty(sp.n * sp.d, dtype=torch.int16, device=DEV)
+    ng.ngram_forward(tok, di.offsets, di.table_obj(), torch.ones(sp.d, dtype=torch.float32, device=DEV), got)
+    torch.cuda.synchronize()
+    w, g = bits16(want).reshape(sp.n, sp.d), bits16(got).reshape(sp.n, sp.d)
+    assert np.all(w[5] == 0x7FC0) and np.all(w[17] == 0x7FC0)
+    assert np.array_equal(g, w)
+
+
 def test_project_full_size_sampled():
     """32,768 x 2560 x 2560 (the prefill batch's sums): every output of 96
     sampled rows, including the first and the last, against the oracle."""
