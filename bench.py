@@ -87,7 +87,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "int8", "fp4", "gated", "projected", "decode1", "decode2", "decode4", "host",
-                             "backward"])
+                             "backward", "unfused"])
     ap.add_argument("--host-mode", default="zero_copy", choices=["zero_copy", "staged", "async", "pool"],
                     help="host workload: sum straight from pinned memory; stage the distinct rows in HBM first, "
                          "read by GPU workgroups (staged) or copied by the DMA engines (async); or go through an "
@@ -250,6 +250,9 @@ def main():
         return
     if args.workload == "projected":
         run_projected(args)
+        return
+    if args.workload == "unfused":
+        run_unfused(args)
         return
 
     dev = torch.device("cuda:0")
@@ -663,6 +666,78 @@ def run_projected(args):
         "cpu_baseline": None if args.no_cpu_baseline else projected_cpu_baseline(h, table, e1, res, P, gp, spec),
     }
     print(json.dumps(result), flush=True)
+
+
+def run_unfused(args):
+    """The prefill batch through the three separate calls: ngram_hash (row ids
+    to HBM), ngram_embed_bag (the fp32 sums to HBM) and ngram_gate_add (gate
+    with e1 and W_g, residual added in place, bf16 out); the same outputs as
+    the fused forward, with the row ids and the sums written and read back.
+    A step is the three launches on one stream, each timed with HIP events;
+    the roofline object is the sum kernel's (16 rows and 64 B of row ids read
+    and 4 d bytes of sums written per token)."""
+    import statistics
+
+    import torch
+
+    import hashed_gram_embedding_ngram_amd as ng
+    import synth
+    from synth.workloads import CONFIGS, HostInputs
+
+    dev = torch.device("cuda:0")
+    spec = CONFIGS["prefill"].replace(dist=args.dist)
+    n, d = spec.n, spec.d
+    t_setup = time.time()
+    h = HostInputs(spec)
+    s0 = spec.seed
+    table = synth.fill_gpu(spec.table_kind, s0, synth.TAG_TABLE, torch.empty(spec.R * d, dtype=torch.int16, device=dev))
+    T = ng.Table(table, spec.R, d)
+    e1 = synth.fill_gpu(synth.KIND_BF16_NORMAL12, s0, synth.TAG_E1, torch.empty(spec.V * d, dtype=torch.int16, device=dev))
+    W_g = torch.from_numpy(h.W_g).to(dev)
+    tok = torch.from_numpy(h.tokens).to(dev)
+    off = torch.from_numpy(h.offsets).to(dev)
+    res = synth.fill_gpu(synth.KIND_BF16_NORMAL6, s0, synth.TAG_RESIDUAL, torch.empty(n * d, dtype=torch.int16, device=dev))
+    rows = torch.empty((n, K_ROWS), dtype=torch.int32, device=dev)
+    eN = torch.empty((n, d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    stream = torch.cuda.current_stream()
+    names = ["hash", "embed_bag", "gate_add"]
+    fns = [lambda: ng.ngram_hash(tok, off, spec.R, rows_out=rows, stream=stream),
+           lambda: ng.ngram_embed_bag(T, rows, eN_out=eN, stream=stream),
+           lambda: ng.ngram_gate_add(eN, tok, W_g, res, e1=e1, residual=res, stream=stream)]
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for k, f in enumerate(fns):
+            f()
+            ev[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {nm: statistics.mean(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)) * 1e3
+           for k, nm in enumerate(names)}
+    bag_bytes = n * (K_ROWS * 2 * d + K_ROWS * 4 + 4 * d)
+    achieved = bag_bytes / (per["embed_bag"] / 1e6) / 1e9
+    print(json.dumps({
+        "metric": METRIC, "value": n * args.steps / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "unfused", "tokens": n, "sequences": len(spec.lengths), "R": spec.R, "d": d,
+                   "K": K_ROWS, "table_dtype": spec.table, "vocab": spec.V,
+                   "token_dist": f"zipf({spec.zipf_s})" if args.dist == "zipf" else "uniform",
+                   "residual_in_place": True},
+        "stage_us": per,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "ngram_bag_kernel",
+                     "algorithmic_bytes_per_launch": bag_bytes, "mean_launch_us": per["embed_bag"],
+                     "gate_add_bytes_per_launch": n * 10 * d,
+                     "gate_add_frac": n * 10 * d / (per["gate_add"] / 1e6) / 1e9 / HBM_PEAK_GBPS},
+        "setup_s": setup_s, "cpu_baseline": None}), flush=True)
 
 
 def projected_cpu_baseline(h, table, e1, res, P, gp, spec, m=256, repeats=5):

@@ -814,9 +814,12 @@ struct BagArgs {
     int32_t tpw;
 };
 
-template <int DT>
+// OUT16: the sums rounded to bf16 (eN16), else fp32 (eN).  Output rows are
+// addressed as the row's uniform start plus a 32-bit lane offset, as in the
+// fused kernel (fewer registers, more wavefronts per SIMD).
+template <int DT, bool OUT16>
 __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int64_t d = a.d;
     const int nslices = (a.d + kSlice - 1) / kSlice;
@@ -835,7 +838,10 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
     for (int sl = wave; sl < nslices; sl += nwaves) {
         const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
         if (j0 >= d) continue;
+        uint32_t off = static_cast<uint32_t>(j0) * (OUT16 ? 2u : 4u);
+        __asm__ volatile("" : "+v"(off));
         for (int tl = 0; tl < tile_n; ++tl) {
+            const int64_t i = tile0 + tl;
             int32_t r[kK];
             bool ok = true;
 #pragma unroll
@@ -850,31 +856,33 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
             }
-            if (a.eN16) {
+            if constexpr (OUT16) {
                 uint4 w;
                 w.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
                 w.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
                 w.z = bf16_rne(acc[4]) | (bf16_rne(acc[5]) << 16);
                 w.w = bf16_rne(acc[6]) | (bf16_rne(acc[7]) << 16);
-                *reinterpret_cast<uint4*>(a.eN16 + (tile0 + tl) * d + j0) = w;
+                store_row8(uniform_ptr(a.eN16 + i * d), off, w);
             } else {
-                float* o = a.eN + (tile0 + tl) * d + j0;
-                reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+                const gbytes orow = uniform_ptr(a.eN + i * d);
+                store_row8(orow, off, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                                 __float_as_uint(acc[2]), __float_as_uint(acc[3])));
+                store_row8(orow, off + 16u, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                                                       __float_as_uint(acc[6]), __float_as_uint(acc[7])));
             }
         }
     }
 }
 
-template <int DT, bool PERSIST>
+template <int DT, bool PERSIST, bool OUT16>
 __global__ void __launch_bounds__(1024) ngram_bag_kernel(const BagArgs a) {
     extern __shared__ int32_t lds[];
     if constexpr (!PERSIST) {
-        bag_tile<DT>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lds);
+        bag_tile<DT, OUT16>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lds);
     } else {
         const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
         for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-            bag_tile<DT>(a, tile * a.tpw, lds);
+            bag_tile<DT, OUT16>(a, tile * a.tpw, lds);
             __syncthreads();
         }
     }
@@ -2313,6 +2321,20 @@ int scratch_address(void** out) {
 }
 
 // ngram_embed_bag and ngram_embed_bag_bf16: the sums to fp32 or to bf16.
+template <bool OUT16>
+void launch_bag(const BagArgs& a, int32_t dtype, bool persist, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+    if (dtype == NGRAM_TABLE_BF16) {
+        if (persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, true, OUT16>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, false, OUT16>), grid, block, lds, st, a);
+    } else if (dtype == NGRAM_TABLE_INT8_ROWSCALE) {
+        if (persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, true, OUT16>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, false, OUT16>), grid, block, lds, st, a);
+    } else {
+        if (persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, true, OUT16>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, false, OUT16>), grid, block, lds, st, a);
+    }
+}
+
 int embed_bag_any(const ngram_table* T, const int32_t* rows, int64_t n, float* eN_out, uint16_t* eN16_out,
                   const ngram_launch* launch, ngram_stream_t stream) {
     int rc = check_table(T);
@@ -2336,16 +2358,8 @@ int embed_bag_any(const ngram_table* T, const int32_t* rows, int64_t n, float* e
     a.tpw = sh.tpw;
     const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
-    if (T->dtype == NGRAM_TABLE_BF16) {
-        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, false>), grid, block, lds, stream, a);
-    } else if (T->dtype == NGRAM_TABLE_INT8_ROWSCALE) {
-        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, false>), grid, block, lds, stream, a);
-    } else {
-        if (sh.persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, false>), grid, block, lds, stream, a);
-    }
+    if (eN16_out) launch_bag<true>(a, T->dtype, sh.persist, grid, block, lds, stream);
+    else launch_bag<false>(a, T->dtype, sh.persist, grid, block, lds, stream);
     return hip_status("ngram_embed_bag launch");
 }
 
