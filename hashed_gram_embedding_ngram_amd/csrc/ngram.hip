@@ -602,6 +602,7 @@ __device__ inline uint32_t bf16_rne_f64(double x) {
 // float64 constants of exp in registers through the gather).
 template <int DT, bool RES, bool FULL, bool ONE, bool LOADED = false>
 __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lrows, int32_t* ltok, double* lred) {
+    constexpr bool EARLY = FULL && ONE;
     const FwdArgs& a = g.f;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
@@ -657,6 +658,24 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
         }
+        // Everything else the token needs (its residual slice, gamma, u, v
+        // and W_g) is fetched here, once the sum is formed: the row slices'
+        // registers are free by then, and the loads arrive during the two
+        // block sums instead of adding two memory round trips after them.
+        // (EARLY: with every lane holding columns and one token per
+        // workgroup; otherwise the registers this takes make the compiler
+        // spill, and the loads follow the sums that need them.)
+        float gm[8], uu[8], vv[8], w8[8];
+        if constexpr (EARLY) {
+            // the residual slice last: loads complete in issue order, and
+            // the first block sum waits only for gamma, u and v
+            __builtin_amdgcn_sched_barrier(0);
+            load_f8(gm, g.gamma, jl);
+            load_f8(uu, g.u, jl);
+            load_f8(vv, g.v, jl);
+            load_w8(w8, a.wg, jl);
+            if constexpr (RES) rv = load_row8(uniform_ptr(a.res + i * d), 2u * jl);
+        }
         double s = 0.0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = s + static_cast<double>(acc[e]) * static_cast<double>(acc[e]);
@@ -668,16 +687,17 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
         const double rn = 1.0 / sqrt(S / static_cast<double>(d) + static_cast<double>(g.eps));
 
         // n = eN r gamma is formed again after the second barrier (the same
-        // operations give the same bits), so only the fp32 sums, r and the
-        // packed e1 slice stay live across it.
+        // operations give the same bits), so the float64 n is not kept
+        // across it.
         double z = 0.0;
         if (col) {
+            if constexpr (!EARLY) {
+                load_f8(gm, g.gamma, jl);
+                load_f8(uu, g.u, jl);
+                load_f8(vv, g.v, jl);
+            }
             const float ev[8] = {bf16lo(e1v.x), bf16hi(e1v.x), bf16lo(e1v.y), bf16hi(e1v.y),
                                  bf16lo(e1v.z), bf16hi(e1v.z), bf16lo(e1v.w), bf16hi(e1v.w)};
-            float gm[8], uu[8], vv[8];
-            load_f8(gm, g.gamma, jl);
-            load_f8(uu, g.u, jl);
-            load_f8(vv, g.v, jl);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const double nv = static_cast<double>(acc[e]) * rn * static_cast<double>(gm[e]);
@@ -694,12 +714,13 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
         if (col) {
             const float ev[8] = {bf16lo(e1v.x), bf16hi(e1v.x), bf16lo(e1v.y), bf16hi(e1v.y),
                                  bf16lo(e1v.z), bf16hi(e1v.z), bf16lo(e1v.w), bf16hi(e1v.w)};
-            float gm[8], w8[8];
-            load_f8(gm, g.gamma, jl);
-            load_w8(w8, a.wg, jl);
+            if constexpr (!EARLY) {
+                load_f8(gm, g.gamma, jl);
+                load_w8(w8, a.wg, jl);
+                if constexpr (RES) rv = load_row8(uniform_ptr(a.res + i * d), 2u * jl);
+            }
             float rf[8];
             if constexpr (RES) {
-                rv = load_row8(uniform_ptr(a.res + i * d), 2u * jl);
                 rf[0] = bf16lo(rv.x); rf[1] = bf16hi(rv.x); rf[2] = bf16lo(rv.y); rf[3] = bf16hi(rv.y);
                 rf[4] = bf16lo(rv.z); rf[5] = bf16hi(rv.z); rf[6] = bf16lo(rv.w); rf[7] = bf16hi(rv.w);
             }
@@ -729,7 +750,7 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
 // 2: a capped grid loops over the tiles (tables in host memory); 3: one
 // token per workgroup whose fp32 sum is read from g.eN (no hash, no gather).
 template <int DT, bool RES, bool FULL, int MODE>
-__global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
+__device__ inline void gated_body(const GatedArgs& g) {
     extern __shared__ int32_t lds[];
     // [tpw][2][nwaves] float64 sums first (8-byte aligned), then the row
     // lists [tpw][16], w_t [tpw] and the staged sequence table
@@ -750,6 +771,24 @@ __global__ void __launch_bounds__(1024) ngram_gated_kernel(const GatedArgs g) {
             __syncthreads();              // the next tile rewrites the LDS lists
         }
     }
+}
+
+// One token per workgroup (MODE 0 and 3) on whole 512-column blocks, held
+// to at most 72 registers so that 7 wavefronts fit per SIMD: with the
+// token's residual, gamma, u, v and W_g fetched as soon as its sum is
+// formed, the compiler's own choice is 78 registers and 6 wavefronts.
+template <int DT, bool RES, int MODE>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7)))
+ngram_gated_kernel(const GatedArgs g) {
+    static_assert(MODE == 0 || MODE == 3, "one token per workgroup");
+    gated_body<DT, RES, true, MODE>(g);
+}
+
+// Every other case: a ragged last block, tiles of several tokens (MODE 1)
+// and the capped grid (MODE 2).
+template <int DT, bool RES, bool FULL, int MODE>
+__global__ void __launch_bounds__(1024) ngram_gated_any_kernel(const GatedArgs g) {
+    gated_body<DT, RES, FULL, MODE>(g);
 }
 
 // PERSIST = false: one tile per workgroup (tables in HBM).  PERSIST = true:
@@ -2240,8 +2279,13 @@ void launch_fwd_dt(const FwdArgs& a, const Shape& sh, hipStream_t st) {
 // The gated kernel: one wavefront per 512-column block (d <= 8192).
 template <int DT, bool RES, int MODE>
 void launch_gated_mode(const GatedArgs& g, dim3 grid, dim3 block, size_t lds, bool full, hipStream_t st) {
-    if (full) hipLaunchKernelGGL((ngram_gated_kernel<DT, RES, true, MODE>), grid, block, lds, st, g);
-    else hipLaunchKernelGGL((ngram_gated_kernel<DT, RES, false, MODE>), grid, block, lds, st, g);
+    if constexpr (MODE == 0 || MODE == 3) {
+        if (full) hipLaunchKernelGGL((ngram_gated_kernel<DT, RES, MODE>), grid, block, lds, st, g);
+        else hipLaunchKernelGGL((ngram_gated_any_kernel<DT, RES, false, MODE>), grid, block, lds, st, g);
+    } else {
+        if (full) hipLaunchKernelGGL((ngram_gated_any_kernel<DT, RES, true, MODE>), grid, block, lds, st, g);
+        else hipLaunchKernelGGL((ngram_gated_any_kernel<DT, RES, false, MODE>), grid, block, lds, st, g);
+    }
 }
 
 template <int DT>
