@@ -1696,7 +1696,7 @@ __global__ void __launch_bounds__(64) set_i64_kernel(int64_t* p, int64_t v) {
 // acc + g[i] (e1), i = position >> pos_shift; a group's sum is stored when
 // the id changes.  The dL/dout rows of the next DEPTH items are loaded ahead
 // (groups can be thousands of items long: a Zipf-hot token's e1 gradient).
-constexpr int kWalkChunk = 64;
+constexpr int kWalkChunk = 128;
 
 // 16 rows ahead: the deepest prefetch that stays in registers (no scratch).
 constexpr int kWalkDepth = 16;
@@ -1706,12 +1706,14 @@ constexpr int kWalkDepth = 16;
 // which is always valid, and is not added.
 template <int B>
 __device__ inline void walk_load(uint4 gv[B], int32_t pl, int first, int64_t tb, int64_t te,
-                                 const uint16_t* __restrict__ g, int32_t d, int64_t jc, int pos_shift) {
+                                 const uint16_t* __restrict__ g, int32_t d, int64_t ja, int64_t jb, int pos_shift) {
 #pragma unroll
     for (int m = 0; m < B; ++m) {
         const int src = tb + first + m < te ? first + m : 0;
         const int64_t i = static_cast<int64_t>(__builtin_amdgcn_readlane(pl, src) >> pos_shift);
-        gv[m] = *reinterpret_cast<const uint4*>(g + i * d + jc);
+        const uint2 a = *reinterpret_cast<const uint2*>(g + i * d + ja);
+        const uint2 b = *reinterpret_cast<const uint2*>(g + i * d + jb);
+        gv[m] = make_uint4(a.x, a.y, b.x, b.y);
     }
 }
 
@@ -1720,17 +1722,16 @@ __device__ inline void walk_load(uint4 gv[B], int32_t pl, int first, int64_t tb,
 template <bool WEIGHT, int B>
 __device__ inline void walk_add(float acc[8], const float w[8], const uint4 gv[B], uint32_t kl, int first,
                                 int64_t tb, int64_t te, uint32_t& prev, int64_t& uo, float* __restrict__ out,
-                                int32_t d, int64_t jc, bool col_ok) {
+                                int32_t d, int64_t ja, int64_t jb, bool ok_a, bool ok_b) {
+    // (ok_a, ok_b: the lane's two column groups exist)
 #pragma unroll
     for (int m = 0; m < B; ++m) {
         if (tb + first + m < te) {          // uniform predicate, so every index stays constant
             const uint32_t km = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kl), first + m));
             if (km != prev) {               // a new group: store the finished one
-                float* o = out + uo * d + jc;
-                if (col_ok) {
-                    reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                    reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-                }
+                float* o = out + uo * d;
+                if (ok_a) *reinterpret_cast<float4*>(o + ja) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                if (ok_b) *reinterpret_cast<float4*>(o + jb) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
                 ++uo;
@@ -1744,7 +1745,7 @@ __device__ inline void walk_add(float acc[8], const float w[8], const uint4 gv[B
     }
 }
 
-template <bool WEIGHT>
+template <bool WEIGHT, bool FULL>
 __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restrict__ keys,
                                                         const uint32_t* __restrict__ seg,
                                                         const int32_t* __restrict__ seg_start,
@@ -1783,11 +1784,22 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
     // the ids and positions that readlane then reads from any lane.  Lanes
     // past the row's end work on column 0 and do not store.
     for (int sl = wave; sl < nslices; sl += nwaves) {
-        const int64_t j0 = static_cast<int64_t>(sl) * kSlice + lane * kVec;
-        const bool col_ok = j0 < d;
-        const int64_t jc = col_ok ? j0 : 0;
+        // lane l owns columns 4l..4l+3 and 256+4l..256+4l+3 of the slice, so
+        // each of a group's two row stores writes 1 KiB of consecutive
+        // addresses (d is a multiple of 8, so a 4-column group is whole)
+        const int64_t j0a = static_cast<int64_t>(sl) * kSlice + lane * 4;
+        const int64_t j0b = j0a + kSlice / 2;
+        const bool ok_a = FULL || j0a < d, ok_b = FULL || j0b < d;
+        // (FULL: d is a multiple of 512, every lane has both column groups,
+        // and the second is the first plus 512 bytes in every row)
+        const int64_t ja = FULL || ok_a ? j0a : 0, jb = FULL || ok_b ? j0b : 0;
         float w[8];
-        if (WEIGHT) load_w8(w, W, jc);
+        if (WEIGHT) {
+            const float4 wa = *reinterpret_cast<const float4*>(W + ja);
+            const float4 wb = *reinterpret_cast<const float4*>(W + jb);
+            w[0] = wa.x; w[1] = wa.y; w[2] = wa.z; w[3] = wa.w;
+            w[4] = wb.x; w[5] = wb.y; w[6] = wb.z; w[7] = wb.w;
+        }
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
@@ -1803,17 +1815,15 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
             const int32_t pl_next = tn < t_end ? sorted_pos[tn] : 0;
             for (int m0 = 0; m0 < 64 && tb + m0 < t_end; m0 += kWalkDepth) {
                 uint4 gv[kWalkDepth];
-                walk_load<kWalkDepth>(gv, pl, m0, tb, t_end, g, d, jc, pos_shift);
-                walk_add<WEIGHT, kWalkDepth>(acc, w, gv, kl, m0, tb, t_end, prev, uo, out, d, jc, col_ok);
+                walk_load<kWalkDepth>(gv, pl, m0, tb, t_end, g, d, ja, FULL ? ja + kSlice / 2 : jb, pos_shift);
+                walk_add<WEIGHT, kWalkDepth>(acc, w, gv, kl, m0, tb, t_end, prev, uo, out, d, ja, jb, ok_a, ok_b);
             }
             kl = kl_next;
             pl = pl_next;
         }
-        if (col_ok) {
-            float* o = out + uo * d + j0;
-            reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        }
+        float* o = out + uo * d;
+        if (ok_a) *reinterpret_cast<float4*>(o + ja) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (ok_b) *reinterpret_cast<float4*>(o + jb) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
 }
 
@@ -2236,8 +2246,12 @@ int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* val
     const int nslices = (d + kSlice - 1) / kSlice;
     const int waves = nslices < 16 ? nslices : 16;
     const int64_t grid = (N + kWalkChunk - 1) / kWalkChunk;
-    hipLaunchKernelGGL((seg_walk_kernel<WEIGHT>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, keys,
-                       segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out);
+    if (d % kSlice == 0)
+        hipLaunchKernelGGL((seg_walk_kernel<WEIGHT, true>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st,
+                           keys, segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out);
+    else
+        hipLaunchKernelGGL((seg_walk_kernel<WEIGHT, false>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st,
+                           keys, segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out);
     hipLaunchKernelGGL((long_walk_kernel<WEIGHT>), dim3(64, static_cast<unsigned>((d + 63) / 64)), dim3(64), 0, st,
                        longs, nlong, starts, pos, pos_shift, g, W, d, grad_out);
     return hip_status("gradient launch");
