@@ -879,6 +879,10 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
         if (j0 >= d) continue;
         uint32_t off = static_cast<uint32_t>(j0) * (OUT16 ? 2u : 4u);
         __asm__ volatile("" : "+v"(off));
+        // fp32 output of a whole 512-column slice (uniform over the wavefront)
+        const bool full = !OUT16 && (static_cast<int64_t>(sl) + 1) * kSlice <= d;
+        float* stage = reinterpret_cast<float*>(lds + a.tpw * kK) + wave * kSlice;
+        const uint32_t offa = (static_cast<uint32_t>(sl) * kSlice + lane * 4u) * 4u;
         for (int tl = 0; tl < tile_n; ++tl) {
             const int64_t i = tile0 + tl;
             int32_t r[kK];
@@ -904,10 +908,27 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
                 store_row8(uniform_ptr(a.eN16 + i * d), off, w);
             } else {
                 const gbytes orow = uniform_ptr(a.eN + i * d);
-                store_row8(orow, off, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                                                 __float_as_uint(acc[2]), __float_as_uint(acc[3])));
-                store_row8(orow, off + 16u, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                                                       __float_as_uint(acc[6]), __float_as_uint(acc[7])));
+                if (full) {
+                    // through the wavefront's 2 KiB of LDS, so that each of
+                    // the two stores writes 1 KiB of consecutive addresses
+                    // (lane l: columns 4l..4l+3, then 256+4l..256+4l+3)
+                    // rather than 16 bytes per lane at a 32-byte stride
+                    *reinterpret_cast<float4*>(stage + lane * 8) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    *reinterpret_cast<float4*>(stage + lane * 8 + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+                    __builtin_amdgcn_wave_barrier();
+                    const float4 p = *reinterpret_cast<const float4*>(stage + lane * 4);
+                    const float4 q = *reinterpret_cast<const float4*>(stage + kSlice / 2 + lane * 4);
+                    __builtin_amdgcn_wave_barrier();
+                    store_row8(orow, offa, make_uint4(__float_as_uint(p.x), __float_as_uint(p.y),
+                                                      __float_as_uint(p.z), __float_as_uint(p.w)));
+                    store_row8(orow, offa + 2u * kSlice, make_uint4(__float_as_uint(q.x), __float_as_uint(q.y),
+                                                                    __float_as_uint(q.z), __float_as_uint(q.w)));
+                } else {
+                    store_row8(orow, off, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                                     __float_as_uint(acc[2]), __float_as_uint(acc[3])));
+                    store_row8(orow, off + 16u, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                                                           __float_as_uint(acc[6]), __float_as_uint(acc[7])));
+                }
             }
         }
     }
@@ -2415,7 +2436,9 @@ int embed_bag_any(const ngram_table* T, const int32_t* rows, int64_t n, float* e
     cap_for_host(sh, T, launch);
     a.tpw = sh.tpw;
     const dim3 grid(static_cast<unsigned>(sh.grid)), block(64 * sh.waves);
-    const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t);
+    // the row lists [tpw][16], then (fp32 output) 2 KiB per wavefront
+    const size_t lds = static_cast<size_t>(sh.tpw) * kK * sizeof(int32_t) +
+                       (eN16_out ? 0 : static_cast<size_t>(sh.waves) * kSlice * sizeof(float));
     if (eN16_out) launch_bag<true>(a, T->dtype, sh.persist, grid, block, lds, stream);
     else launch_bag<false>(a, T->dtype, sh.persist, grid, block, lds, stream);
     return hip_status("ngram_embed_bag launch");
