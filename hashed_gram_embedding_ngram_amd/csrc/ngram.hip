@@ -1660,19 +1660,26 @@ __global__ void __launch_bounds__(1024) seg_scan_kernel(const uint32_t* __restri
 // Groups longer than this many items are walked by long_walk_kernel, with
 // four times the rows in flight per wavefront (a
 // Zipf-hot token's e1 gradient adds thousands of dL/dout rows, one after
-// another per column).
+// another per column): 512 items for the table's row groups, 64 for the e1
+// gradient's token groups, whose Zipf head holds dozens of tokens with
+// hundreds of items each (walked 16 rows at a time by seg_walk_kernel,
+// they set its length).  The list of long groups has room for
+// 16 n / kLongGroup + 1 entries, which covers both.
 constexpr int kLongGroup = 512;
+constexpr int kLongGroupE1 = 64;
+static_assert(kLongGroupE1 * kK >= kLongGroup, "the e1 call's long groups must fit the list");
 
 // Second half: seg[t] += the counts of the earlier tiles (each workgroup adds
 // them up itself), then each group's first index, its id, the end sentinel
-// and the group count; a group longer than kLongGroup items (its last item t
-// has the same key as item t - kLongGroup, the keys being sorted) is also
+// and the group count; a group longer than long_min items (its last item t
+// has the same key as item t - long_min, the keys being sorted) is also
 // listed in longs[], in an unspecified order.
 __global__ void __launch_bounds__(1024) seg_bounds_kernel(const uint32_t* __restrict__ keys, uint32_t* __restrict__ seg,
                                                           const uint32_t* __restrict__ tile_sums, int64_t N,
                                                           uint32_t limit, int32_t* __restrict__ seg_start,
                                                           int32_t* __restrict__ ids_out, int64_t* __restrict__ n_unique,
-                                                          int32_t* __restrict__ longs, uint32_t* __restrict__ nlong) {
+                                                          int32_t* __restrict__ longs, uint32_t* __restrict__ nlong,
+                                                          int long_min) {
     __shared__ uint32_t red[16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t part = 0;
@@ -1702,7 +1709,7 @@ __global__ void __launch_bounds__(1024) seg_bounds_kernel(const uint32_t* __rest
             *n_unique = U;
         }
         const bool last = t + 1 == N || keys[t + 1] != k;
-        if (last && t >= kLongGroup && keys[t - kLongGroup] == k)     // then not first: group sg - 1
+        if (last && t >= long_min && keys[t - long_min] == k)     // then not first: group sg - 1
             longs[atomicAdd(nlong, 1u)] = static_cast<int32_t>(sg - 1u);
     }
 }
@@ -1773,7 +1780,7 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
                                                         const int64_t* __restrict__ n_unique,
                                                         const int32_t* __restrict__ sorted_pos, int pos_shift,
                                                         const uint16_t* __restrict__ g, const float* __restrict__ W,
-                                                        int32_t d, float* __restrict__ out) {
+                                                        int32_t d, float* __restrict__ out, int long_min) {
     const int64_t U = *n_unique;
     if (U == 0) return;
     const int64_t nvalid = seg_start[U];
@@ -1791,9 +1798,9 @@ __global__ void __launch_bounds__(1024) seg_walk_kernel(const uint32_t* __restri
     const int64_t u_last = static_cast<int64_t>(seg[tl]) - (tl_starts ? 0 : 1);
     const int64_t t_begin = seg_start[u];
     int64_t t_end = seg_start[u_last + 1];
-    // a group longer than kLongGroup items (only the last one can be) is
+    // a group longer than long_min items (only the last one can be) is
     // walked by long_walk_kernel instead
-    if (t_end - seg_start[u_last] > kLongGroup) {
+    if (t_end - seg_start[u_last] > long_min) {
         if (u_last == u) return;
         t_end = seg_start[u_last];
     }
@@ -2242,11 +2249,11 @@ void radix_sort(char* ws, const GradLayout& L, int64_t N, const SortSource& firs
 }
 
 // Sort, find the groups of equal ids and reduce each group in position order
-// (groups longer than kLongGroup items in a launch of their own).
+// (groups longer than long_min items in a launch of their own).
 template <bool WEIGHT>
 int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* valid_rows, uint32_t limit, int pos_shift,
                    const uint16_t* g, const float* W, int32_t d, int32_t* ids_out, float* grad_out, int64_t* n_unique,
-                   void* workspace, const GradLayout& L, hipStream_t st) {
+                   void* workspace, const GradLayout& L, int long_min, hipStream_t st) {
     char* ws = static_cast<char*>(workspace);
     if (N == 0) {
         hipLaunchKernelGGL(set_i64_kernel, dim3(1), dim3(64), 0, st, n_unique, int64_t{0});
@@ -2263,16 +2270,16 @@ int grad_by_groups(const int32_t* ids, int64_t N, int stride, const int32_t* val
     const unsigned ntiles = static_cast<unsigned>((N + kScanTile - 1) / kScanTile);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(ntiles), dim3(1024), 0, st, keys, N, limit, segs, tiles);
     hipLaunchKernelGGL(seg_bounds_kernel, dim3(ntiles), dim3(1024), 0, st, keys, segs, tiles, N, limit, starts, ids_out,
-                       n_unique, longs, nlong);
+                       n_unique, longs, nlong, long_min);
     const int nslices = (d + kSlice - 1) / kSlice;
     const int waves = nslices < 16 ? nslices : 16;
     const int64_t grid = (N + kWalkChunk - 1) / kWalkChunk;
     if (d % kSlice == 0)
         hipLaunchKernelGGL((seg_walk_kernel<WEIGHT, true>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st,
-                           keys, segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out);
+                           keys, segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out, long_min);
     else
         hipLaunchKernelGGL((seg_walk_kernel<WEIGHT, false>), dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st,
-                           keys, segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out);
+                           keys, segs, starts, n_unique, pos, pos_shift, g, W, d, grad_out, long_min);
     hipLaunchKernelGGL((long_walk_kernel<WEIGHT>), dim3(64, static_cast<unsigned>((d + 63) / 64)), dim3(64), 0, st,
                        longs, nlong, starts, pos, pos_shift, g, W, d, grad_out);
     return hip_status("gradient launch");
@@ -3001,7 +3008,7 @@ int ngram_grad_table(const int32_t* rows, int64_t n, int32_t d, int64_t R, const
         return fail(NGRAM_EINVAL, "rows, grad_rows_out or grad_out is NULL/misaligned");
     const GradLayout L = grad_layout(n, d);
     return grad_by_groups<true>(rows, kK * n, 0, nullptr, static_cast<uint32_t>(R), 4, dout, W_g, d, grad_rows_out,
-                                grad_out, n_unique_out, workspace, L, stream);
+                                grad_out, n_unique_out, workspace, L, kLongGroup, stream);
 }
 
 int ngram_grad_e1(const int32_t* tokens, const int32_t* rows, int64_t n, int32_t d, int64_t V, const uint16_t* dout,
@@ -3016,7 +3023,7 @@ int ngram_grad_e1(const int32_t* tokens, const int32_t* rows, int64_t n, int32_t
         return fail(NGRAM_EINVAL, "tokens, rows, grad_tokens_out or grad_out is NULL/misaligned");
     const GradLayout L = grad_layout(n, d);
     return grad_by_groups<false>(tokens, n, kK, rows, static_cast<uint32_t>(V), 0, dout, nullptr, d, grad_tokens_out,
-                                 grad_out, n_unique_out, workspace, L, stream);
+                                 grad_out, n_unique_out, workspace, L, kLongGroupE1, stream);
 }
 
 int ngram_grad_gate(const int32_t* rows, const uint16_t* dout, const float* eN, int64_t n, int32_t d,

@@ -128,6 +128,28 @@ def test_e1_grad(lengths, V, d, bad):
     assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
 
 
+def test_e1_grad_long_group_edges():
+    """The e1 gradient's long-token walk at its edges: tokens of exactly 64
+    items (walked with the short groups), 65 and 129 items (the long-group
+    walk, a ragged last unit), spread over the batch, beside random short
+    groups; d = 200 leaves a ragged 64-column slice."""
+    n, V, d = 1200, 1024, 200
+    rng = np.random.default_rng(21)
+    toks = np.concatenate([np.full(65, 5), np.full(64, 9), np.full(129, 2),
+                           rng.choice([v for v in range(V) if v not in (2, 5, 9)], n - 258)])
+    toks = rng.permutation(toks).astype(np.int32)
+    offs = synth.ragged_offsets((n,))
+    rows = oracle.hash_rows(toks, offs, 4096)
+    say("grad e1 long-group edges")
+    g = synth.tensor(synth.KIND_BF16_WIDE, 22, synth.TAG_RESIDUAL, n * d).reshape(n, d)
+    gt, gv, nu = ng.ngram_grad_e1(_dev(toks, np.int32), _dev(rows, np.int32), _dev(g.view(np.int16), np.int16), V)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    q, want = oracle.grad_e1(toks, rows, g)
+    assert U == q.size
+    assert np.array_equal(gt.cpu().numpy()[:U], q)
+    assert np.array_equal(gv.cpu().numpy()[:U].view(np.uint32), want.view(np.uint32))
+
 @pytest.mark.parametrize("n,d", [(1, 8), (255, 64), (257, 64), (263, 520), (1000, 2560), (515, 1032)])
 def test_gate_grad(n, d):
     say(f"grad gate n={n} d={d}")
