@@ -1174,18 +1174,31 @@ __global__ void __launch_bounds__(kPThreads, 1) project_kernel(const ProjArgs a)
         __syncthreads();
     }
     proj_mfma8(acc, ca, cb);
-    // lane L holds rows 8 (e >> 2) + 4 (L >> 5) + (e & 3), column L & 31 of each 32 x 32 tile
+    // Lane L holds rows 8 (e >> 2) + 4 (L >> 5) + (e & 3), column L & 31 of
+    // each 32 x 32 tile.  The operand buffers are free (every read of them
+    // finished before the last barrier), so each 32 x 32 tile goes through
+    // this wavefront's 4 KiB of LDS and out as 16 bytes per lane: one store
+    // instruction writes 8 rows of 128 consecutive bytes, where one 4-byte
+    // value per lane took 4 times the instructions.  d_out % 8 == 0, so a
+    // lane's 4 columns are all inside the row or all past it.
+    float* st = reinterpret_cast<float*>(plds + wave * 4096);
+    const int rq = lane >> 3, cq = 4 * (lane & 7);
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm)
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
-            const int col = n0 + wn + 32 * sn + (lane & 31);
-            if (col >= a.N) continue;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm + 32 * sm + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (row < a.n) a.y[row * a.N + col] = acc[sm][sn][e];
+            for (int e = 0; e < 16; ++e)
+                st[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * 32 + (lane & 31)] = acc[sm][sn][e];
+            __builtin_amdgcn_wave_barrier();
+            const int col = n0 + wn + 32 * sn + cq;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(st + (8 * q + rq) * 32 + cq);
+                const int64_t row = m0 + wm + 32 * sm + 8 * q + rq;
+                if (row < a.n && col < a.N) *reinterpret_cast<float4*>(a.y + row * a.N + col) = v;
             }
+            __builtin_amdgcn_wave_barrier();
         }
 }
 
