@@ -327,11 +327,37 @@ __device__ inline void gather_reduce(float acc[8], const typename Row8<DT>::Raw 
 }
 
 // The fp32 sum over k = 0..15 of the lane's 8 columns of rows r[0..15].
-template <int DT>
+template <int DT, bool WS = false>
 __device__ inline void gather_sum(float acc[8], const void* __restrict__ tab,
                                   const float* __restrict__ scale, const int32_t r[kK],
                                   int64_t d, int64_t j0) {
     typename Row8<DT>::Raw v[kK];
+    if constexpr (DT == NGRAM_TABLE_INT8_ROWSCALE && WS) {
+        // WS: every lane of the wavefront is active (whole 512-column
+        // slices).  The 16 row scales by one load ahead of the rows: lane
+        // k < 16 takes row k's scale (the other lanes row 0's, unused), and
+        // readlane hands each one to the whole wavefront once the load is
+        // back (the rows' loads, issued after it, can still be in flight:
+        // loads complete in issue order).  Sixteen per-row loads of one
+        // broadcast word each otherwise share the load queue with the rows
+        // (measured: int8 prefill shape 566-576 -> 554-559 us).
+        int32_t rk = 0;
+#pragma unroll
+        for (int k = 0; k < kK; ++k) __asm__("v_writelane_b32 %0, %1, %2" : "+v"(rk) : "s"(r[k]), "n"(k));
+        const float sv = scale[rk];
+        __builtin_amdgcn_sched_barrier(0);
+        gather_load<DT>(v, tab, r, d, j0);
+        // all 16 row loads in flight before the first add (2 registers each)
+        __builtin_amdgcn_sched_barrier(0);
+        float sk[kK];
+#pragma unroll
+        for (int k = 0; k < kK; ++k) sk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), k));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kK; ++k) fma_row(acc, v[k], sk[k]);
+        return;
+    }
     gather_load<DT>(v, tab, r, d, j0);
     // MXFP4 rows take 2 registers per row slice, so all 32 loads fit in
     // flight before the first add (measured 3% faster; for int8 the same
@@ -459,7 +485,7 @@ __device__ inline void hash_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows
 
 // One tile: hash its tokens' rows into LDS, then each wavefront gathers,
 // sums, gates and stores its slices of every token of the tile.
-template <int DT, bool E1, bool RES>
+template <int DT, bool E1, bool RES, bool WS>
 __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows, int32_t* ltok) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
@@ -505,7 +531,7 @@ __device__ inline void fwd_tile(const FwdArgs& a, int64_t tile0, int32_t* lrows,
                 __builtin_amdgcn_sched_barrier(0);
                 gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
             } else {
-                gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+                gather_sum<DT, WS>(acc, a.tab, a.scale, r, d, j0);
                 if constexpr (E1) e = load_row8(uniform_row(a.e1, c0, 2 * d), off2);
                 if constexpr (RES) rv = load_row8(uniform_ptr(a.res + i * d), off2);
             }
@@ -652,7 +678,7 @@ __device__ inline void gated_tile(const GatedArgs& g, int64_t tile0, int32_t* lr
 #pragma unroll
                 for (int k = 0; k < kK; ++k) r[k] = __builtin_amdgcn_readfirstlane(lrows[tl * kK + k]);
                 __builtin_amdgcn_sched_barrier(0);
-                gather_sum<DT>(acc, a.tab, a.scale, r, d, jl);
+                gather_sum<DT, FULL>(acc, a.tab, a.scale, r, d, jl);
             }
         } else {
 #pragma unroll
@@ -793,17 +819,18 @@ __global__ void __launch_bounds__(1024) ngram_gated_any_kernel(const GatedArgs g
 
 // PERSIST = false: one tile per workgroup (tables in HBM).  PERSIST = true:
 // a capped grid loops over the tiles (tables in host memory, read over PCIe).
-template <int DT, bool E1, bool RES, bool PERSIST>
+// WS: d is a multiple of 512 (every slice whole; int8 only).
+template <int DT, bool E1, bool RES, bool PERSIST, bool WS>
 __global__ void __launch_bounds__(1024) ngram_fwd_kernel(const FwdArgs a) {
     extern __shared__ int32_t lds[];
     int32_t* lrows = lds;                 // [tpw][16] row ids (-1: invalid token)
     int32_t* ltok = lds + a.tpw * kK;     // [tpw] w_t (-1: invalid token)
     if constexpr (!PERSIST) {
-        fwd_tile<DT, E1, RES>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lrows, ltok);
+        fwd_tile<DT, E1, RES, WS>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lrows, ltok);
     } else {
         const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
         for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-            fwd_tile<DT, E1, RES>(a, tile * a.tpw, lrows, ltok);
+            fwd_tile<DT, E1, RES, WS>(a, tile * a.tpw, lrows, ltok);
             __syncthreads();              // the next tile rewrites the LDS lists
         }
     }
@@ -856,7 +883,7 @@ struct BagArgs {
 // OUT16: the sums rounded to bf16 (eN16), else fp32 (eN).  Output rows are
 // addressed as the row's uniform start plus a 32-bit lane offset, as in the
 // fused kernel (fewer registers, more wavefronts per SIMD).
-template <int DT, bool OUT16>
+template <int DT, bool OUT16, bool WS>
 __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
@@ -894,7 +921,7 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
             }
             float acc[8];
             if (ok) {
-                gather_sum<DT>(acc, a.tab, a.scale, r, d, j0);
+                gather_sum<DT, WS>(acc, a.tab, a.scale, r, d, j0);
             } else {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = __uint_as_float(kNaNf32);
@@ -934,15 +961,16 @@ __device__ inline void bag_tile(const BagArgs& a, int64_t tile0, int32_t* lds) {
     }
 }
 
-template <int DT, bool PERSIST, bool OUT16>
+// WS: d is a multiple of 512 (every slice whole; int8 only).
+template <int DT, bool PERSIST, bool OUT16, bool WS = false>
 __global__ void __launch_bounds__(1024) ngram_bag_kernel(const BagArgs a) {
     extern __shared__ int32_t lds[];
     if constexpr (!PERSIST) {
-        bag_tile<DT, OUT16>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lds);
+        bag_tile<DT, OUT16, WS>(a, static_cast<int64_t>(blockIdx.x) * a.tpw, lds);
     } else {
         const int64_t ntiles = (a.n + a.tpw - 1) / a.tpw;
         for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-            bag_tile<DT, OUT16>(a, tile * a.tpw, lds);
+            bag_tile<DT, OUT16, WS>(a, tile * a.tpw, lds);
             __syncthreads();
         }
     }
@@ -2318,8 +2346,15 @@ void launch_fwd(const FwdArgs& a, const Shape& sh, hipStream_t st) {
     const dim3 block(64 * sh.waves);
     const size_t lds = static_cast<size_t>(sh.tpw) * (kK + 1) * sizeof(int32_t) +
                        (a.stage ? kSeqLds * sizeof(int32_t) : 0);
-    if (sh.persist) hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, true>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, false>), grid, block, lds, st, a);
+    if constexpr (DT == NGRAM_TABLE_INT8_ROWSCALE) {
+        if (a.d % kSlice == 0) {
+            if (sh.persist) hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, true, true>), grid, block, lds, st, a);
+            else hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, false, true>), grid, block, lds, st, a);
+            return;
+        }
+    }
+    if (sh.persist) hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, true, false>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((ngram_fwd_kernel<DT, E1, RES, false, false>), grid, block, lds, st, a);
 }
 
 template <int DT>
@@ -2426,8 +2461,14 @@ void launch_bag(const BagArgs& a, int32_t dtype, bool persist, dim3 grid, dim3 b
         if (persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, true, OUT16>), grid, block, lds, st, a);
         else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_BF16, false, OUT16>), grid, block, lds, st, a);
     } else if (dtype == NGRAM_TABLE_INT8_ROWSCALE) {
-        if (persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, true, OUT16>), grid, block, lds, st, a);
-        else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_INT8_ROWSCALE, false, OUT16>), grid, block, lds, st, a);
+        constexpr int I8 = NGRAM_TABLE_INT8_ROWSCALE;
+        if (a.d % kSlice == 0) {
+            if (persist) hipLaunchKernelGGL((ngram_bag_kernel<I8, true, OUT16, true>), grid, block, lds, st, a);
+            else hipLaunchKernelGGL((ngram_bag_kernel<I8, false, OUT16, true>), grid, block, lds, st, a);
+        } else {
+            if (persist) hipLaunchKernelGGL((ngram_bag_kernel<I8, true, OUT16>), grid, block, lds, st, a);
+            else hipLaunchKernelGGL((ngram_bag_kernel<I8, false, OUT16>), grid, block, lds, st, a);
+        }
     } else {
         if (persist) hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, true, OUT16>), grid, block, lds, st, a);
         else hipLaunchKernelGGL((ngram_bag_kernel<NGRAM_TABLE_MXFP4, false, OUT16>), grid, block, lds, st, a);
