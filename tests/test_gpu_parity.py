@@ -207,6 +207,24 @@ def test_unfused_int8_sum_bits():
     assert np.array_equal(eN.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
 
 
+@pytest.mark.parametrize("table,d", [("bf16", 1536), ("bf16", 9216), ("int8", 1024), ("int8", 9216),
+                                     ("int8", 1032)])
+def test_unfused_and_fused_whole_and_looped_slices(table, d):
+    """Widths made of whole 512-column slices (the int8 scales by one load
+    per token, the bag kernel's fp32 sums through LDS), up to 18 slices, so
+    each of 16 wavefronts takes two in turn; 1032 leaves an 8-column last
+    slice beside whole ones.  fp32 sums and bf16 outputs bit-exact."""
+    kw = dict(table="int8", table_kind=synth.KIND_I8_NORMAL) if table == "int8" else \
+        dict(table_kind=synth.KIND_BF16_WIDE)
+    sp = Spec(f"slices_{table}_{d}", (3, 0, 40, 1), 151936, 20_011, d, residual=True, config_id=61, **kw)
+    h, di = check_spec(sp)
+    rows = ng.ngram_hash(di.tokens, di.offsets, sp.R)
+    eN = ng.ngram_embed_bag(di.table_obj(), rows)
+    torch.cuda.synchronize()
+    _, want_eN, _ = expected(h)
+    assert np.array_equal(eN.cpu().numpy().view(np.uint32), want_eN.view(np.uint32))
+
+
 def test_hash_extreme_R():
     sp = Spec("hashR", (1, 2, 300), 151936, 4096, 64, config_id=21)
     h = HostInputs(sp)
