@@ -42,6 +42,7 @@ def _dev(a, dt):
     ((50,), 3, 136, ()),                    # groups of hundreds of items (several 64-item blocks)
     ((200,), 3, 136, (7,)),                 # groups of about 1000 items: the long-group walk
     ((700, 333), 11, 2568, ()),             # long groups, a ragged last column block
+    ((90, 3), 500, 9216, (2,)),             # 18 whole slices: each of 16 wavefronts walks two in turn
 ])
 def test_table_grad(lengths, R, d, bad):
     say(f"grad table {lengths} R={R} d={d}")
@@ -115,7 +116,8 @@ def test_table_grad_many_items_sampled():
 @pytest.mark.parametrize("lengths,V,d,bad", [((40, 0, 57), 13, 64, ()), ((300, 7), 1024, 520, (3, 17)),
                                              ((5000,), 151936, 128, ()),
                                              ((3000,), 3, 520, (5,)),         # tokens of ~1000 items: long walk
-                                             ((20000,), 151936, 2560, ())])   # prefill-like Zipf head
+                                             ((20000,), 151936, 2560, ()),    # prefill-like Zipf head
+                                             ((400, 5), 64, 9216, (3,))])     # 18 whole slices, looped
 def test_e1_grad(lengths, V, d, bad):
     say(f"grad e1 {lengths} V={V}")
     toks, rows, g, W = _inputs(lengths, 4096, V, d, seed=7, bad=bad)
